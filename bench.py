@@ -1,0 +1,219 @@
+"""CSA2 decode benchmark on one MI355X.
+
+One step = one decode token for every sequence of the batch through every layer of
+the workload (default: batch 32, 65,536 FP4 entries per sequence, one sharing group in
+modes Full, Reindex, Reuse, Reuse, top-k 2048, 16 bf16 heads of dim 128, window 128).
+Inputs are seeded synthetic N(0,1) data already resident in HBM when timing starts.
+
+Prints one JSON line with tokens/s, the roofline of the dominant kernel (the exact
+index-score stream) measured with HIP events, and the CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def _dev(a, device):
+    import torch
+
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(device)
+
+
+def algorithmic_bytes(wl):
+    """Bytes the method must move per step (measurement section)."""
+    B, N, D, K, k, W, Hq, Qs = wl.B, wl.N, wl.D, wl.H_I * wl.d_I, wl.k, wl.W, wl.Hq, wl.Qs
+    eb = 2 if wl.idx_dtype == "bf16" else 1
+    per_layer_attend = B * Qs * (k * (D // 2 + D // 32 * 4) + 2 * (Qs + W - 1) * D * 2 // Qs
+                                 + Hq * D * 2 + Hq * D * 4 + Hq * 4)
+    scan = B * (N * K * eb + Qs * K * eb + Qs * N * 4)  # keys + index query + score write
+    select = B * Qs * k * 4                            # selection written
+    full_write = B * Qs * (D * 4 + D // 2 + D // 32 * 4 + K * eb * 2)
+    total = 0
+    for mode in wl.pattern * wl.groups:
+        total += per_layer_attend + B * Qs * k * 4  # every mode reads its selection
+        if mode in ("F", "Ri"):
+            total += scan + select
+        if mode == "F":
+            total += full_write
+    return total, scan
+
+
+def run_gpu(wl, steps, warmup, device):
+    import torch
+
+    import compressed_kv_cache_03_amd as csa2
+    from synth.inputs import make_inputs
+
+    t0 = time.time()
+    inp = make_inputs(wl)
+    B, N, D = wl.B, wl.N, wl.D
+    groups = []
+    for g in range(wl.groups):
+        gc, gs = csa2.fp4_pack(_dev(inp.cache_x[g], device))
+        groups.append(csa2.Group(gc, gs, _dev(inp.ikeys[g], device), _dev(inp.n_valid, device),
+                                 wl.idx_dtype, wl.k, sel_rows=B * wl.Qs))
+    layers = []
+    for L in inp.layers:
+        d = {k: (_dev(v, device) if isinstance(v, np.ndarray) else v) for k, v in L.items()}
+        d["out"] = torch.empty(B, wl.Qs, wl.Hq, D, dtype=torch.float32, device=device)
+        d["lse"] = torch.empty(B, wl.Qs, wl.Hq, dtype=torch.float32, device=device)
+        layers.append(d)
+    for grp in groups:
+        grp.workspace(wl.Qs, wl.Hq, wl.W)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def step():
+        for d in layers:
+            grp = groups[d["group"]]
+            kw = dict(q=d["q"], wk=d["wk"], wv=d["wv"], W=wl.W, sm_scale=wl.sm_scale,
+                      out=d["out"], lse=d["lse"])
+            if d["iq"] is not None:
+                kw["iq"] = d["iq"]
+            if d["new_entry"] is not None:
+                kw["new_entry"] = d["new_entry"]
+                kw["new_ikey"] = d["new_ikey"]
+            grp.layer_step(d["mode"], **kw)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+
+    # dominant kernel: the exact index-score stream over one group's keys (same kernel the
+    # Full/Reindex layers launch), timed over its own loop on the same stream
+    first = next(d for d in layers if d["mode"] == "F")
+    grp = groups[first["group"]]
+    scores = torch.empty(B, wl.Qs, N, dtype=torch.float32, device=device)
+    reps = max(steps, 5)
+    for _ in range(2):
+        csa2.index_score(first["iq"], grp.ikeys, wl.idx_dtype, out=scores)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        csa2.index_score(first["iq"], grp.ikeys, wl.idx_dtype, out=scores)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_scan = e0.elapsed_time(e1) / reps
+    return ms_step, ms_scan, inp
+
+
+def cpu_baseline(wl, inp, target_seconds=12.0, max_reps=50):
+    """The oracle, as it stands, on a bounded sample of the same workload: whole decode steps
+    over (up to) 32 sequences, repeated until about target_seconds of host time have run."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = max(1, min(threads, os.cpu_count() or 1))
+    bs = min(wl.B, 32)
+    B, N, D = wl.B, wl.N, wl.D
+    t0 = time.time()
+    groups = []
+    for g in range(wl.groups):
+        x = inp.cache_x[g][:bs]
+        oc, os_ = oracle.fp4_pack(x.reshape(bs * N, D))
+        groups.append(oracle.Group(oc.reshape(bs, N, D // 2), os_.reshape(bs, N, D // 32),
+                                   inp.ikeys[g][:bs].copy(), inp.n_valid[:bs].astype(np.int64),
+                                   wl.idx_dtype, wl.k, max_rows=bs * wl.Qs))
+    t_setup = time.time() - t0
+    reps = 0
+    t0 = time.time()
+    while True:
+        for L in inp.layers:
+            kw = dict(q=L["q"][:bs], wk=L["wk"][:bs], wv=L["wv"][:bs], W=wl.W,
+                      sm_scale=np.float32(wl.sm_scale))
+            if L["iq"] is not None:
+                kw["iq"] = L["iq"][:bs]
+            if L["new_entry"] is not None:
+                kw["new_entry"] = L["new_entry"][:bs]
+                kw["new_ikey"] = L["new_ikey"][:bs]
+            rc, _, _ = groups[L["group"]].layer_step(L["mode"], **kw)
+            assert rc == 0
+        reps += 1
+        if time.time() - t0 >= target_seconds or reps >= max_reps:
+            break
+    t_step = time.time() - t0
+    return {"value": round(reps * bs * wl.Qs / t_step, 4), "unit": "tokens/s",
+            "cores": min(threads, bs), "kind": "oracle",
+            "sample": f"{reps} decode step(s) of {bs} of {B} sequences through all "
+                      f"{len(inp.layers)} layers, {t_step:.1f}s on {min(threads, bs)} host threads "
+                      f"(OpenMP over sequences; cache packing untimed, {t_setup:.1f}s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this implementation runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard by sequence with no exchange, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from synth.workloads import ALL
+
+    wl = ALL[args.workload]
+    device = "cuda:0"
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ms_step, ms_scan, inp = run_gpu(wl, args.steps, args.warmup, device)
+    total_bytes, scan_bytes = algorithmic_bytes(wl)
+    achieved = scan_bytes / (ms_scan * 1e-3) / 1e9
+    tokens = wl.B * wl.Qs
+    res = {
+        "metric": "CSA2 decode tokens/s + achieved HBM GB/s (frac. of peak) at 1 MI355X",
+        "value": round(tokens / (ms_step * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "dtype_detail": "exact index scores accumulated in f64 from bf16/e4m3 keys; attention in "
+                        "f32 over FP4 e2m1 entries and bf16 window rows",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "entries": wl.N, "layers": list(wl.pattern) * wl.groups,
+                   "index": f"{wl.H_I}x{wl.d_I} {wl.idx_dtype}", "k": wl.k, "heads": wl.Hq,
+                   "head_dim": wl.D, "window": wl.W},
+        "step_hbm": {"algorithmic_bytes": total_bytes,
+                     "GBps": round(total_bytes / (ms_step * 1e-3) / 1e9, 1),
+                     "frac": round(total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "roofline": {"kernel": "score_exact_kernel (exact index-score stream)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": scan_bytes, "avg_launch_us": round(ms_scan * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,84 @@
+// Device helpers shared by the CSA2 HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define CSA2_DEV static __device__ __forceinline__
+#define CSA2_DEV_HOST_INLINE static __host__ __device__ __forceinline__
+
+namespace csa2 {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kHistBits = 12;             // first radix digit: top 12 bits of the sort key
+static_assert(kHistBits == 12, "host workspace sizing assumes 4096 bins");
+constexpr int kHistBins = 1 << kHistBits;  // 4096
+
+// bf16 bit pattern -> fp32 (exact).
+CSA2_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+CSA2_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+CSA2_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// OCP fp8 e4m3fn byte -> fp64, exact, by field arithmetic (bias 7; exponent
+// field 0 holds the subnormals m * 2^-9).  NaN (S.1111.111) is not produced
+// for finite inputs and is not handled.
+CSA2_DEV double e4m3_to_f64(uint32_t b) {
+    uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    double mag = e ? __longlong_as_double((long long)(((uint64_t)(e + 1016u) << 52) | ((uint64_t)m << 49)))
+                   : (double)m * 0x1p-9;
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// Order-preserving map fp32 -> uint32: a > b (as reals) <=> key(a) > key(b).
+// -0 is mapped like +0 so the two compare equal.
+CSA2_DEV uint32_t sort_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Butterfly exchange inside groups of 32 lanes (ds_swizzle, bitmask mode).
+template <int XOR>
+CSA2_DEV float swz_xor(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (XOR << 10) | 0x1f));
+}
+template <int XOR>
+CSA2_DEV double swz_xor(double v) {
+    int2 p = *reinterpret_cast<int2*>(&v);
+    p.x = __builtin_amdgcn_ds_swizzle(p.x, (XOR << 10) | 0x1f);
+    p.y = __builtin_amdgcn_ds_swizzle(p.y, (XOR << 10) | 0x1f);
+    return *reinterpret_cast<double*>(&p);
+}
+
+// Block-wide exclusive prefix sum of one uint32 per thread (blockDim.x <= 1024,
+// a multiple of 64).  `lds` must hold blockDim.x/64 + 1 words.  Returns the
+// exclusive prefix; *total receives the block sum.  Contains barriers.
+CSA2_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) lds[wid] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t run = 0;
+        for (int w = 0; w < nw; ++w) {
+            uint32_t t = lds[w];
+            lds[w] = run;
+            run += t;
+        }
+        lds[nw] = run;
+    }
+    __syncthreads();
+    uint32_t excl = lds[wid] + x - v;
+    *total = lds[nw];
+    __syncthreads();
+    return excl;
+}
+
+}  // namespace csa2

@@ -1,0 +1,362 @@
+// C-ABI entry points of libcsa2 (declared in include/csa2.h).
+//
+// Host side only: argument validation (before anything is launched), the
+// workspace layout, the Full / Reindex / Reuse plumbing of a sharing group, and
+// the kernel launches.  No entry point allocates, synchronises or keeps global
+// state.
+#include "../../include/csa2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+
+namespace {
+
+using namespace csa2;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int idx_elem_bytes(csa2_idx_dtype dt) { return dt == CSA2_IDX_BF16 ? 2 : 1; }
+
+// Workspace carve-up shared by all entry points.  Offsets are 256-byte aligned.
+struct Layout {
+    size_t hist = 0, hist_bytes = 0;     // [R][4096] u32 (zeroed per selection)
+    size_t scores = 0;                   // [R][N] f32
+    size_t cand_idx = 0, cand_key = 0;   // [R][N]
+    size_t slice_cnt = 0;                // [R][slices]
+    size_t part = 0;                     // attention partials
+    size_t total = 0;
+};
+
+struct TopkShape {
+    int64_t R, N, slices;
+};
+
+void add_topk(Layout& L, size_t& off, const TopkShape& t) {
+    L.hist = off;
+    L.hist_bytes = (size_t)t.R * kHistBinsHost * 4;
+    off = align_up(off + L.hist_bytes);
+    L.cand_idx = off;
+    off = align_up(off + (size_t)t.R * t.N * 4);
+    L.cand_key = off;
+    off = align_up(off + (size_t)t.R * t.N * 4);
+    L.slice_cnt = off;
+    off = align_up(off + (size_t)t.R * t.slices * 4);
+}
+
+size_t attend_part_bytes(int64_t R, int Hq, int D, int k, int W) {
+    int sg, sw;
+    attend_splits(Hq, D, k, W, &sg, &sw);
+    return (size_t)R * (sg + sw) * Hq * (D + 2) * 4;
+}
+
+Layout layer_layout(const csa2_group* g, int Qs, int Hq, int W) {
+    Layout L;
+    const int64_t R = (int64_t)g->B * Qs, N = g->N_cap;
+    size_t off = 0;
+    L.scores = off;
+    off = align_up(off + (size_t)R * N * 4);
+    add_topk(L, off, TopkShape{R, N, (N + topk_slice_len(N) - 1) / topk_slice_len(N)});
+    L.part = off;
+    off = align_up(off + attend_part_bytes(R, Hq, g->D, g->k, W));
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+bool valid_dim(int32_t D) { return D >= 32 && D <= 256 && D % 32 == 0; }
+
+bool valid_index_width(csa2_idx_dtype dt, int32_t H, int32_t d) {
+    if (H < 1 || d < 1) return false;
+    const int64_t K = (int64_t)H * d;
+    return K <= 4096 && K % 16 == 0 && (dt == CSA2_IDX_BF16 || dt == CSA2_IDX_FP8_E4M3);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_str(csa2_status s) {
+    switch (s) {
+        case CSA2_OK: return "CSA2_OK";
+        case CSA2_ERR_INVALID_ARG: return "CSA2_ERR_INVALID_ARG";
+        case CSA2_ERR_UNSUPPORTED: return "CSA2_ERR_UNSUPPORTED";
+        case CSA2_ERR_WORKSPACE: return "CSA2_ERR_WORKSPACE";
+        case CSA2_ERR_STATE: return "CSA2_ERR_STATE";
+        case CSA2_ERR_HIP: return "CSA2_ERR_HIP";
+    }
+    return "CSA2_ERR_UNKNOWN";
+}
+
+const char* csa2_version(void) { return "csa2-gfx950 0.1"; }
+
+int64_t csa2_cache_bytes(int64_t entries, int64_t numbers, int64_t copies, int64_t bits) {
+    if (entries < 0 || numbers < 0 || copies < 0 || bits < 0) return -1;
+    __int128 v = (__int128)entries * numbers;
+    v *= copies;
+    v *= bits;
+    v /= 8;
+    if (v > INT64_MAX) return -1;
+    return (int64_t)v;
+}
+
+csa2_status csa2_fp4_pack(const float* x, int64_t rows, int32_t dim, uint8_t* codes, float* scales,
+                          void* stream) {
+    if (rows < 0 || dim <= 0 || dim % 32 != 0) return CSA2_ERR_INVALID_ARG;
+    if (rows == 0) return CSA2_OK;
+    if (!x || !codes || !scales) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(scales, 4)) return CSA2_ERR_INVALID_ARG;
+    return hip_status(launch_fp4_pack(x, rows, dim, codes, scales, nullptr, 1, rows,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+csa2_status csa2_index_score(const void* iq, const void* ik, csa2_idx_dtype dtype, int32_t B,
+                             int32_t Qs, int64_t N, int32_t H, int32_t d, float* scores,
+                             void* stream) {
+    if (B < 0 || Qs < 1 || N < 0) return CSA2_ERR_INVALID_ARG;
+    if (!valid_index_width(dtype, H, d)) return CSA2_ERR_INVALID_ARG;
+    if (N >= (int64_t)1 << 31) return CSA2_ERR_UNSUPPORTED;
+    if (B == 0 || N == 0) return CSA2_OK;
+    if (!iq || !ik || !scores) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(iq, 16) || !aligned(ik, 16) || !aligned(scores, 4)) return CSA2_ERR_INVALID_ARG;
+    if ((int64_t)B * Qs > 65535) return CSA2_ERR_UNSUPPORTED;  // grid.y
+    ScoreArgs a{};
+    a.iq = iq;
+    a.ik = ik;
+    a.dtype = dtype == CSA2_IDX_BF16 ? 0 : 1;
+    a.K = H * d;
+    a.B = B;
+    a.Qs = Qs;
+    a.N = N;
+    a.N_cap = N;
+    a.nvb = nullptr;
+    a.scores = scores;
+    a.ld = N;
+    a.hist = nullptr;
+    return hip_status(launch_score_exact(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_topk_workspace_bytes(int64_t R, int64_t N, int32_t k) {
+    (void)k;
+    if (R <= 0 || N <= 0) return 0;
+    Layout L;
+    size_t off = 0;
+    add_topk(L, off, TopkShape{R, N, (N + topk_slice_len(N) - 1) / topk_slice_len(N)});
+    return off;
+}
+
+csa2_status csa2_topk(const float* scores, int64_t R, int64_t N, int64_t ld, const int32_t* n_valid,
+                      int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    if (R < 0 || N < 0 || k < 1 || ld < N) return CSA2_ERR_INVALID_ARG;
+    if (N >= (int64_t)1 << 31 || R > 65535) return CSA2_ERR_UNSUPPORTED;
+    if (R == 0) return CSA2_OK;
+    if (!idx || (N > 0 && !scores)) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(idx, 4) || (scores && !aligned(scores, 4))) return CSA2_ERR_INVALID_ARG;
+    const size_t need = csa2_topk_workspace_bytes(R, N > 0 ? N : 1, k);
+    if (!ws || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Layout L;
+    size_t off = 0;
+    const int64_t Nn = N > 0 ? N : 1;
+    const int64_t slices = (Nn + topk_slice_len(Nn) - 1) / topk_slice_len(Nn);
+    add_topk(L, off, TopkShape{R, Nn, slices});
+    TopkArgs t{};
+    t.scores = scores;
+    t.R = R;
+    t.N = N;
+    t.ld = ld;
+    t.nvb = n_valid;
+    t.Qs = 1;
+    t.k = k;
+    t.idx = idx;
+    t.hist = at<uint32_t>(ws, L.hist);
+    t.cand_idx = at<int32_t>(ws, L.cand_idx);
+    t.cand_key = at<uint32_t>(ws, L.cand_key);
+    t.slice_cnt = at<uint32_t>(ws, L.slice_cnt);
+    t.slices = (int)slices;
+    t.slice_len = topk_slice_len(Nn);
+    hipError_t e = launch_zero(t.hist, (int64_t)R * kHistBinsHost, s);
+    if (e == hipSuccess) e = launch_topk_hist(t, s);
+    if (e == hipSuccess) e = launch_topk_select(t, s);
+    return hip_status(e);
+}
+
+size_t csa2_attend_workspace_bytes(int32_t B, int32_t Qs, int32_t Hq, int32_t D, int32_t k,
+                                   int32_t W) {
+    if (B <= 0 || Qs <= 0 || Hq <= 0 || !valid_dim(D) || k < 0 || W < 0) return 0;
+    return align_up(attend_part_bytes((int64_t)B * Qs, Hq, D, k, W));
+}
+
+csa2_status csa2_sparse_attend(const void* q, int32_t B, int32_t Qs, int32_t Hq, int32_t D,
+                               const uint8_t* codes, const float* scales, int64_t N,
+                               const int32_t* idx, int32_t k, const void* wk, const void* wv,
+                               int32_t W, const int32_t* wlen, float sm_scale, float* out,
+                               float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (B < 0 || Qs < 1 || Hq < 1 || Hq > 32 || !valid_dim(D) || N < 0 || k < 0 || W < 0 ||
+        W > 1024 || !std::isfinite(sm_scale))
+        return CSA2_ERR_INVALID_ARG;
+    if (k == 0 && W == 0) return CSA2_ERR_INVALID_ARG;
+    if ((int64_t)B * Qs > 65535 || N >= (int64_t)1 << 31) return CSA2_ERR_UNSUPPORTED;
+    if (B == 0) return CSA2_OK;
+    if (!q || !out) return CSA2_ERR_INVALID_ARG;
+    if (k > 0 && (!idx || !codes || !scales)) return CSA2_ERR_INVALID_ARG;
+    if (W > 0 && (!wk || !wv)) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(q, 4) || !aligned(out, 4) || (codes && !aligned(codes, 4)))
+        return CSA2_ERR_INVALID_ARG;
+    const size_t need = csa2_attend_workspace_bytes(B, Qs, Hq, D, k, W);
+    if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
+    AttendArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.B = B;
+    a.Qs = Qs;
+    a.Hq = Hq;
+    a.D = D;
+    a.codes = codes;
+    a.scales = scales;
+    a.N = N;
+    a.idx = idx;
+    a.k = k;
+    a.wk = static_cast<const uint16_t*>(wk);
+    a.wv = static_cast<const uint16_t*>(wv);
+    a.W = W;
+    a.wlen = wlen;
+    a.sm_scale = sm_scale;
+    a.out = out;
+    a.lse = lse;
+    a.part = static_cast<float*>(ws);
+    return hip_status(launch_attend(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_layer_workspace_bytes(const csa2_group* g, int32_t Qs, int32_t Hq, int32_t W) {
+    if (!g || g->B <= 0 || g->N_cap <= 0 || Qs <= 0 || Hq <= 0 || W < 0 || !valid_dim(g->D))
+        return 0;
+    return layer_layout(g, Qs, Hq, W).total;
+}
+
+csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group* g, void* ws,
+                            size_t ws_bytes, void* stream) {
+    if (!a || !g) return CSA2_ERR_INVALID_ARG;
+    if (mode != CSA2_MODE_FULL && mode != CSA2_MODE_REINDEX && mode != CSA2_MODE_REUSE)
+        return CSA2_ERR_INVALID_ARG;
+    // group geometry
+    if (g->B < 1 || g->N_cap < 1 || !valid_dim(g->D) || g->k < 1 || g->k > g->N_cap ||
+        !valid_index_width(g->idx_dtype, g->H_I, g->d_I))
+        return CSA2_ERR_INVALID_ARG;
+    if (g->N_cap >= (int64_t)1 << 31) return CSA2_ERR_UNSUPPORTED;
+    if (!g->codes || !g->scales || !g->ikeys || !g->n_valid || !g->sel) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(g->codes, 16) || !aligned(g->scales, 16) || !aligned(g->ikeys, 16) ||
+        !aligned(g->sel, 4) || !aligned(g->n_valid, 4))
+        return CSA2_ERR_INVALID_ARG;
+    // layer arguments
+    const int Qs = a->Qs;
+    if (Qs < 1 || a->Hq < 1 || a->Hq > 32 || a->W < 0 || a->W > 1024 || !std::isfinite(a->sm_scale))
+        return CSA2_ERR_INVALID_ARG;
+    if (g->n_valid_max < Qs || g->n_valid_max > g->N_cap) return CSA2_ERR_INVALID_ARG;
+    if ((int64_t)g->B * Qs > 65535) return CSA2_ERR_UNSUPPORTED;
+    if (g->sel_rows < (int64_t)g->B * Qs) return CSA2_ERR_INVALID_ARG;
+    if (!a->q || !a->out || (a->W > 0 && (!a->wk || !a->wv))) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(a->q, 4) || !aligned(a->out, 4)) return CSA2_ERR_INVALID_ARG;
+    const bool selects = mode != CSA2_MODE_REUSE;
+    if (selects && (!a->iq || !aligned(a->iq, 16))) return CSA2_ERR_INVALID_ARG;
+    if (mode == CSA2_MODE_FULL &&
+        (!a->new_entry || !a->new_ikey || !aligned(a->new_entry, 16) || !aligned(a->new_ikey, 4)))
+        return CSA2_ERR_INVALID_ARG;
+    // group state
+    if (mode == CSA2_MODE_REINDEX && !g->has_entries) return CSA2_ERR_STATE;
+    if (mode == CSA2_MODE_REUSE && (!g->has_selection || g->sel_qs != Qs)) return CSA2_ERR_STATE;
+    // workspace
+    const Layout L = layer_layout(g, Qs, a->Hq, a->W);
+    if (!ws || ws_bytes < L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t R = (int64_t)g->B * Qs;
+    const int K = g->H_I * g->d_I;
+    hipError_t e = hipSuccess;
+
+    if (mode == CSA2_MODE_FULL) {
+        // S1: the step's new rows go to slots n_valid-Qs .. n_valid-1
+        e = launch_fp4_pack(a->new_entry, R, g->D, g->codes, g->scales, g->n_valid, Qs, g->N_cap, s);
+        if (e == hipSuccess)
+            e = launch_store_rows(a->new_ikey, R, K * idx_elem_bytes(g->idx_dtype), g->ikeys,
+                                  g->n_valid, Qs, g->N_cap, s);
+    }
+    if (e == hipSuccess && selects) {
+        // S2 + S3: exact scores of the valid entries, digit histogram, selection
+        TopkArgs t{};
+        t.scores = at<float>(ws, L.scores);
+        t.R = R;
+        t.N = g->n_valid_max;
+        t.ld = g->N_cap;
+        t.nvb = g->n_valid;
+        t.Qs = Qs;
+        t.k = g->k;
+        t.idx = g->sel;
+        t.hist = at<uint32_t>(ws, L.hist);
+        t.cand_idx = at<int32_t>(ws, L.cand_idx);
+        t.cand_key = at<uint32_t>(ws, L.cand_key);
+        t.slice_cnt = at<uint32_t>(ws, L.slice_cnt);
+        t.slice_len = topk_slice_len(g->N_cap);
+        t.slices = (int)((g->n_valid_max + t.slice_len - 1) / t.slice_len);
+        ScoreArgs sa{};
+        sa.iq = a->iq;
+        sa.ik = g->ikeys;
+        sa.dtype = g->idx_dtype == CSA2_IDX_BF16 ? 0 : 1;
+        sa.K = K;
+        sa.B = g->B;
+        sa.Qs = Qs;
+        sa.N = g->n_valid_max;
+        sa.N_cap = g->N_cap;
+        sa.nvb = g->n_valid;
+        sa.scores = at<float>(ws, L.scores);
+        sa.ld = g->N_cap;
+        sa.hist = t.hist;
+        e = launch_zero(t.hist, R * kHistBinsHost, s);
+        if (e == hipSuccess) e = launch_score_exact(sa, s);
+        if (e == hipSuccess) e = launch_topk_select(t, s);
+    }
+    if (e == hipSuccess) {
+        // S5 + S6: gather, dequantise, attend over the selection and the window
+        AttendArgs at_{};
+        at_.q = static_cast<const uint16_t*>(a->q);
+        at_.B = g->B;
+        at_.Qs = Qs;
+        at_.Hq = a->Hq;
+        at_.D = g->D;
+        at_.codes = g->codes;
+        at_.scales = g->scales;
+        at_.N = g->N_cap;
+        at_.idx = g->sel;
+        at_.k = g->k;
+        at_.wk = static_cast<const uint16_t*>(a->wk);
+        at_.wv = static_cast<const uint16_t*>(a->wv);
+        at_.W = a->W;
+        at_.wlen = a->wlen;
+        at_.sm_scale = a->sm_scale;
+        at_.out = a->out;
+        at_.lse = a->lse;
+        at_.part = at<float>(ws, L.part);
+        e = launch_attend(at_, s);
+    }
+    if (e != hipSuccess) return CSA2_ERR_HIP;
+    if (mode == CSA2_MODE_FULL) g->has_entries = 1;
+    if (selects) {
+        g->has_selection = 1;
+        g->sel_qs = Qs;
+    }
+    return CSA2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+// Every function enqueues work on `stream` and returns hipGetLastError().
+// Shapes are validated by the caller (csa2_api.cpp) before these are reached.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kHistBitsHost = 12;
+constexpr int64_t kHistBinsHost = 1 << kHistBitsHost;  // first radix digit bins per row
+
+// Zero `words` uint32 words (a plain fill kernel, safe inside graph capture).
+hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t stream);
+
+// S1: see pack.hip for the row -> slot mapping when nvb != nullptr.
+hipError_t launch_fp4_pack(const float* x, int64_t rows, int dim, uint8_t* codes, float* scales,
+                           const int32_t* nvb, int Qs, int64_t N_cap, hipStream_t stream);
+// Copy rows of row_bytes (multiple of 4) to the same slots as launch_fp4_pack.
+hipError_t launch_store_rows(const void* src, int64_t rows, int row_bytes, void* dst,
+                             const int32_t* nvb, int Qs, int64_t N_cap, hipStream_t stream);
+
+// S2: exact index scores.  Row r = b*Qs + i scores entries j < nv(r) of
+// sequence b (ik row stride N_cap entries), where nv(r) = N when nvb is null and
+// nvb[b] - Qs + i + 1 otherwise (clamped to [0, N]).  Writes scores[r*ld + j].
+// When hist != nullptr, also accumulates the first radix digit histogram of
+// every written score into hist[r*4096 + digit].
+struct ScoreArgs {
+    const void* iq;       // [R][K]
+    const void* ik;       // [B][N_cap][K]
+    int dtype;            // 0 bf16, 1 e4m3
+    int K;                // H*d
+    int B, Qs;
+    int64_t N;            // entries to consider per sequence (<= N_cap)
+    int64_t N_cap;        // entry row stride of ik
+    const int32_t* nvb;   // [B] or null
+    float* scores;        // [R][ld]
+    int64_t ld;
+    uint32_t* hist;       // [R][4096] or null
+};
+hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t stream);
+
+// S3: top-k over scores [R][ld] with per-row valid counts nv(r) as above (Qs,
+// nvb) and k.  hist must already hold the digit histogram of each row's valid
+// scores (launch_topk_hist builds it when the scores come from elsewhere).
+struct TopkArgs {
+    const float* scores;
+    int64_t R, N, ld;
+    const int32_t* nvb;
+    int Qs;
+    int k;
+    int32_t* idx;         // [R][k]
+    uint32_t* hist;       // [R][4096]
+    int32_t* cand_idx;    // [R][N]
+    uint32_t* cand_key;   // [R][N]
+    uint32_t* slice_cnt;  // [R][slices]
+    int slices;           // slices per row
+    int64_t slice_len;
+};
+int64_t topk_slice_len(int64_t N);
+hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t stream);
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t stream);
+
+// S5+S6: sparse attention with split-k partials and a combine pass.
+struct AttendArgs {
+    const uint16_t* q;    // [R][Hq][D] bf16
+    int B, Qs, Hq, D;
+    const uint8_t* codes; // [B][N][D/2]
+    const float* scales;  // [B][N][D/32]
+    int64_t N;
+    const int32_t* idx;   // [R][k]
+    int k;
+    const uint16_t* wk;   // [B][Qs+W-1][D]
+    const uint16_t* wv;
+    int W;
+    const int32_t* wlen;  // [B] or null
+    float sm_scale;
+    float* out;           // [R][Hq][D]
+    float* lse;           // [R][Hq] or null
+    float* part;          // [R][splits][Hq][D+2]
+    int splits_g, splits_w;
+};
+void attend_splits(int Hq, int D, int k, int W, int* splits_g, int* splits_w);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
+
+}  // namespace csa2

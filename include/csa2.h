@@ -1,0 +1,191 @@
+/*
+ * csa2.h - C ABI of the CSA2 layer-step library for AMD Instinct MI355X (gfx950).
+ *
+ * CSA2 (Compressed Sparse Attention 2, as described for DeepSeek-V4.1-Flash):
+ * a lightweight indexer scores a compressed global KV cache, the top-k entries
+ * are kept, and attention runs over those entries together with a local
+ * sliding window ("Why Is DeepSeek V4.1 Flash So Fast?", sections 3 and 4).
+ * Layers run in one of three modes that decide which of these steps they
+ * repeat ("DeepSeek-V4.1-Flash", section "Sharing the cache across layers";
+ * "Inference-Efficient LLMs: How Sparse Compute and Compressed Memory Work",
+ * section 4).  The main cache is stored in FP4 with per-group scales (same
+ * pages, "Fast memory, persistent storage and recomputation" and section 6).
+ *
+ * Parameters the pages leave open are fixed here:
+ *   - FP4 element: OCP MX e2m1; one fp32 scale per 32 consecutive elements,
+ *     scale = fl32(amax / 6); each element is rounded to the nearest multiple
+ *     of the scale on the e2m1 grid, ties to the even code, magnitudes beyond
+ *     6*scale saturate; element 2i sits in the low nibble of byte i.
+ *   - Index score of entry j for query row r: the exact real value of
+ *     sum_h sum_e iq[r,h,e] * ik[j,h,e], rounded once to fp32 (nearest, ties
+ *     to even; an exact zero is +0).  Index elements are bf16 or fp8 e4m3fn.
+ *   - Top-k: the k valid entries first in the order (score descending, index
+ *     ascending), written in ascending index order, padded with -1.
+ *   - Attention: one softmax over the selected entries and the query's window
+ *     rows.  An entry (dequantised FP4 row of dim D) is both key and value and
+ *     is shared by all Hq query heads; window keys and values are bf16 rows.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are device pointers owned by the caller, row-major
+ *     and contiguous, 16-byte aligned.  bf16 and fp8 tensors are passed as raw
+ *     bytes (const void*).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; no entry point synchronises, allocates device memory or
+ *     keeps global mutable state, so calls on different streams with disjoint
+ *     buffers may run concurrently.
+ *   - Arguments are validated on the host before anything is launched; on an
+ *     error nothing is enqueued and the status says why.  A launch failure
+ *     returns CSA2_ERR_HIP.  No C++ exception crosses this interface.
+ *   - Scratch memory is a caller-provided workspace of at least the size the
+ *     matching *_workspace_bytes function returns; its contents on entry do
+ *     not matter and are undefined on return.
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified results.
+ */
+#ifndef CSA2_H_
+#define CSA2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer   */
+    CSA2_ERR_UNSUPPORTED = 2, /* valid request outside the supported shapes   */
+    CSA2_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required   */
+    CSA2_ERR_STATE = 4,       /* mode not allowed in the group's current state */
+    CSA2_ERR_HIP = 5          /* the HIP runtime reported an error             */
+} csa2_status;
+
+typedef enum {
+    CSA2_MODE_FULL = 0,    /* writes its own entries, makes its own selection  */
+    CSA2_MODE_REINDEX = 1, /* shares the group's entries, selects afresh        */
+    CSA2_MODE_REUSE = 2    /* shares the group's entries and latest selection   */
+} csa2_mode;
+
+typedef enum { CSA2_IDX_BF16 = 0, CSA2_IDX_FP8_E4M3 = 1 } csa2_idx_dtype;
+
+/* State of one sharing group ("DeepSeek-V4.1-Flash", "Sharing the cache
+ * across layers": one stored copy of the entries per group, plus the
+ * selection that Reuse layers share).  The struct lives in host memory and is
+ * owned by the caller; the buffers it points to are device memory. */
+typedef struct csa2_group {
+    int32_t B;                /* sequences                                          */
+    int64_t N_cap;            /* entry slots per sequence (row stride of the cache) */
+    int32_t D;                /* entry dimension, multiple of 32, <= 256            */
+    int32_t H_I, d_I;         /* index heads and index head dimension              */
+    csa2_idx_dtype idx_dtype; /* dtype of index keys and index queries             */
+    int32_t k;                /* entries kept per query row, 1 <= k <= N_cap        */
+    uint8_t* codes;           /* [B][N_cap][D/2]   FP4 e2m1 codes                   */
+    float* scales;            /* [B][N_cap][D/32]  fp32 block scales                */
+    void* ikeys;              /* [B][N_cap][H_I][d_I] index keys                    */
+    const int32_t* n_valid;   /* [B] valid entries per sequence, counting the step's
+                                 own new rows; Qs <= n_valid[b] <= N_cap            */
+    int64_t n_valid_max;      /* host copy of max_b n_valid[b], sizes the launches  */
+    int32_t* sel;             /* [sel_rows][k] the group's current selection        */
+    int32_t sel_rows;         /* rows sel can hold; must be >= B * Qs               */
+    int32_t has_entries;      /* caller sets it after filling the cache; Full sets it */
+    int32_t has_selection;    /* set by Full and Reindex, required by Reuse        */
+    int32_t sel_qs;           /* Qs of the stored selection                         */
+} csa2_group;
+
+/* Per-layer inputs.  Every mode uses its own queries and window ("every layer
+ * keeps its own queries and its own local-window state"). */
+typedef struct csa2_layer_args {
+    int32_t Qs;            /* query rows per sequence: 1 for decode, >1 for a prefill
+                              chunk (row i of the chunk sits at entry n_valid-Qs+i and
+                              sees entries j <= n_valid-Qs+i)                       */
+    int32_t Hq;            /* query heads, 1..32                                      */
+    const void* q;         /* bf16 [B][Qs][Hq][D]                                     */
+    const void* iq;        /* [B][Qs][H_I][d_I] in idx_dtype; Full and Reindex only   */
+    const void* wk;        /* bf16 [B][Qs+W-1][D] window keys; row i..i+W-1 for row i */
+    const void* wv;        /* bf16 [B][Qs+W-1][D] window values                       */
+    int32_t W;             /* window rows per query (0..1024)                         */
+    const int32_t* wlen;   /* [B] valid window rows, counted from the end of the
+                              window buffer; NULL = all valid                         */
+    const float* new_entry;/* fp32 [B][Qs][D]: Full writes these at slots
+                              n_valid-Qs .. n_valid-1                                 */
+    const void* new_ikey;  /* [B][Qs][H_I][d_I] index keys stored with them (Full)    */
+    float sm_scale;        /* softmax scale, e.g. 1/sqrt(D)                           */
+    float* out;            /* fp32 [B][Qs][Hq][D]                                     */
+    float* lse;            /* fp32 [B][Qs][Hq] natural-log sum-exp, or NULL           */
+} csa2_layer_args;
+
+/* Human-readable name of a status code (static storage). */
+const char* csa2_status_str(csa2_status s);
+
+/* Library version string (static storage). */
+const char* csa2_version(void);
+
+/* S1 - FP4 cache write ("Fast memory, persistent storage and recomputation";
+ * "Inference-Efficient LLMs", section 6: FP4 main KV with per-group scaling).
+ * x: fp32 [rows][dim]; codes: [rows][dim/2]; scales: [rows][dim/32].
+ * dim must be a positive multiple of 32.  rows == 0 is a no-op. */
+csa2_status csa2_fp4_pack(const float* x, int64_t rows, int32_t dim, uint8_t* codes,
+                          float* scales, void* stream);
+
+/* S2 - Index scores ("Why Is DeepSeek V4.1 Flash So Fast?", section 4: a
+ * cheaper search scores positions before attention; "Inference-Efficient
+ * LLMs", section 5).  iq: [B][Qs][H][d], ik: [B][N][H][d] in `dtype`;
+ * scores: fp32 [B][Qs][N], each the exact sum rounded once to fp32 (see the
+ * top of this file).  H*d must be a multiple of 64 (bf16) or 128 (fp8) for
+ * the streaming kernel and at most 4096.  N == 0 is a no-op. */
+csa2_status csa2_index_score(const void* iq, const void* ik, csa2_idx_dtype dtype, int32_t B,
+                             int32_t Qs, int64_t N, int32_t H, int32_t d, float* scores,
+                             void* stream);
+
+/* S3 - Top-k selection ("Why Is DeepSeek V4.1 Flash So Fast?", sections 3 and
+ * 4: select the useful compressed positions).  scores: fp32 [R][ld], row r
+ * considers entries j < n_valid[r] (n_valid: device int32 [R], or NULL = N).
+ * idx: int32 [R][k] ascending, -1 padded.  Ties go to the lower index; -0 and
+ * +0 are equal.  Scores must not be NaN. */
+size_t csa2_topk_workspace_bytes(int64_t R, int64_t N, int32_t k);
+csa2_status csa2_topk(const float* scores, int64_t R, int64_t N, int64_t ld,
+                      const int32_t* n_valid, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* S5+S6 - Gather, dequantise and attend ("Why Is DeepSeek V4.1 Flash So
+ * Fast?", sections 3 and 4: expensive attention only over the selected
+ * positions plus the 128-token window).  q: bf16 [B][Qs][Hq][D]; codes/scales:
+ * [B][N] records as in csa2_fp4_pack; idx: int32 [B*Qs][k] (-1 = empty slot,
+ * other values must be < N); wk, wv: bf16 [B][Qs+W-1][D], query row i uses
+ * window rows i..i+W-1 of which only the last wlen[b] rows of the buffer are
+ * valid (wlen NULL = all); out fp32 [B][Qs][Hq][D]; lse fp32 [B][Qs][Hq] or
+ * NULL.  A row with nothing to attend gets out = 0 and lse = -inf. */
+size_t csa2_attend_workspace_bytes(int32_t B, int32_t Qs, int32_t Hq, int32_t D, int32_t k,
+                                   int32_t W);
+csa2_status csa2_sparse_attend(const void* q, int32_t B, int32_t Qs, int32_t Hq, int32_t D,
+                               const uint8_t* codes, const float* scales, int64_t N,
+                               const int32_t* idx, int32_t k, const void* wk, const void* wv,
+                               int32_t W, const int32_t* wlen, float sm_scale, float* out,
+                               float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* S4 - One CSA2 layer in the given mode ("DeepSeek-V4.1-Flash", "Sharing the
+ * cache across layers"; "Why Is DeepSeek V4.1 Flash So Fast?", section 5):
+ *   FULL    packs new_entry/new_ikey into slots n_valid-Qs .. n_valid-1,
+ *           scores the group's keys with iq, selects into g->sel, attends;
+ *   REINDEX scores the shared keys with its own iq, overwrites g->sel, attends;
+ *           writes no entries (CSA2_ERR_STATE if g->has_entries == 0);
+ *   REUSE   attends with g->sel as left by the latest Full/Reindex of the
+ *           group; writes neither entries nor the selection (CSA2_ERR_STATE if
+ *           g->has_selection == 0 or g->sel_qs != Qs).
+ * The library updates g->has_entries, g->has_selection and g->sel_qs on the
+ * host when the work has been enqueued. */
+size_t csa2_layer_workspace_bytes(const csa2_group* g, int32_t Qs, int32_t Hq, int32_t W);
+csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group* g, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* S7 - Cache accounting ("DeepSeek-V4.1-Flash", "Several mechanisms in one
+ * release": entries x numbers per entry x stored layer copies x bits per
+ * number).  Returns bytes, or -1 if an argument is negative or the product
+ * overflows int64. */
+int64_t csa2_cache_bytes(int64_t entries, int64_t numbers, int64_t copies, int64_t bits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H_ */

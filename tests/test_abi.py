@@ -1,0 +1,134 @@
+"""C-ABI library: it loads, exports every declared entry point, and validates its
+arguments on the host before anything reaches the GPU (no device is touched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_kv_cache_03_amd as csa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launch
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(csa2.LIB_PATH)
+    names = _declared()
+    assert {"csa2_fp4_pack", "csa2_index_score", "csa2_topk", "csa2_sparse_attend",
+            "csa2_layer_step"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    for code, name in enumerate(["CSA2_OK", "CSA2_ERR_INVALID_ARG", "CSA2_ERR_UNSUPPORTED",
+                                 "CSA2_ERR_WORKSPACE", "CSA2_ERR_STATE", "CSA2_ERR_HIP"]):
+        assert csa2.status_str(code) == name
+    assert csa2.version().startswith("csa2-gfx950")
+
+
+def test_cache_bytes_worked_figure_and_overflow():
+    assert csa2.cache_bytes(4096, 128, 16, 8) == 8388608
+    assert csa2.cache_bytes(4096, 128, 4, 8) == 2097152
+    assert csa2.cache_bytes(-1, 1, 1, 8) == -1
+    assert csa2.cache_bytes(1 << 40, 1 << 20, 1 << 10, 8) == -1
+
+
+def test_fp4_pack_validation():
+    L = csa2.lib()
+    assert L.csa2_fp4_pack(FAKE, 4, 48, FAKE, FAKE, None) == csa2.ERR_INVALID_ARG  # dim % 32
+    assert L.csa2_fp4_pack(FAKE, -1, 128, FAKE, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_fp4_pack(None, 4, 128, FAKE, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_fp4_pack(FAKE + 4, 4, 128, FAKE, FAKE, None) == csa2.ERR_INVALID_ARG  # misaligned
+    assert L.csa2_fp4_pack(None, 0, 128, None, None, None) == csa2.OK  # empty: no-op
+
+
+def test_index_score_validation():
+    L = csa2.lib()
+    assert L.csa2_index_score(FAKE, FAKE, 0, 1, 1, 10, 64, 65, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, 7, 1, 1, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, 0, 1, 0, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(None, FAKE, 0, 1, 1, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, 0, 1, 1, 1 << 31, 4, 64, FAKE, None) == csa2.ERR_UNSUPPORTED
+    assert L.csa2_index_score(FAKE, FAKE, 0, 1, 1, 0, 4, 64, FAKE, None) == csa2.OK
+
+
+def test_topk_validation():
+    L = csa2.lib()
+    need = L.csa2_topk_workspace_bytes(4, 1000, 16)
+    assert need > 4 * 4096 * 4
+    assert L.csa2_topk(FAKE, 4, 1000, 1000, None, 0, FAKE, FAKE, need, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_topk(FAKE, 4, 1000, 999, None, 8, FAKE, FAKE, need, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_topk(FAKE, 4, 1000, 1000, None, 8, FAKE, FAKE, need - 1, None) == csa2.ERR_WORKSPACE
+    assert L.csa2_topk(FAKE, 4, 1000, 1000, None, 8, FAKE, None, need, None) == csa2.ERR_WORKSPACE
+
+
+def test_attend_validation():
+    L = csa2.lib()
+    need = L.csa2_attend_workspace_bytes(2, 1, 16, 128, 64, 128)
+    args = [FAKE, 2, 1, 16, 128, FAKE, FAKE, 100, FAKE, 64, FAKE, FAKE, 128, None, 0.0884, FAKE,
+            FAKE, FAKE, need, None]
+    bad_d = list(args)
+    bad_d[4] = 100
+    assert L.csa2_sparse_attend(*bad_d) == csa2.ERR_INVALID_ARG
+    bad_h = list(args)
+    bad_h[3] = 33
+    assert L.csa2_sparse_attend(*bad_h) == csa2.ERR_INVALID_ARG
+    nan = list(args)
+    nan[14] = float("nan")
+    assert L.csa2_sparse_attend(*nan) == csa2.ERR_INVALID_ARG
+    small = list(args)
+    small[18] = need - 1
+    assert L.csa2_sparse_attend(*small) == csa2.ERR_WORKSPACE
+
+
+def _group(**over):
+    g = csa2.CGroup(2, 1000, 128, 4, 64, 0, 64, FAKE, FAKE, FAKE, FAKE, 1000, FAKE, 2, 1, 0, 0)
+    for k, v in over.items():
+        setattr(g, k, v)
+    return g
+
+
+def _args(**over):
+    a = csa2.CLayerArgs(1, 16, FAKE, FAKE, FAKE, FAKE, 128, None, FAKE, FAKE, 0.0884, FAKE, FAKE)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def _step(mode, g, a, ws_bytes=None):
+    L = csa2.lib()
+    need = L.csa2_layer_workspace_bytes(ctypes.byref(g), a.Qs, a.Hq, a.W)
+    return L.csa2_layer_step(mode, ctypes.byref(a), ctypes.byref(g), FAKE,
+                             need if ws_bytes is None else ws_bytes, None)
+
+
+def test_layer_step_state_machine_errors():
+    # Reuse before any selection, Reindex with no entries: state errors, nothing launched
+    assert _step(2, _group(), _args()) == csa2.ERR_STATE
+    assert _step(1, _group(has_entries=0), _args()) == csa2.ERR_STATE
+    # Reuse of a selection made for another Qs
+    assert _step(2, _group(has_selection=1, sel_qs=4), _args()) == csa2.ERR_STATE
+
+
+def test_layer_step_argument_errors():
+    assert _step(3, _group(), _args()) == csa2.ERR_INVALID_ARG               # unknown mode
+    assert _step(0, _group(D=100), _args()) == csa2.ERR_INVALID_ARG          # D % 32
+    assert _step(0, _group(k=0), _args()) == csa2.ERR_INVALID_ARG            # k < 1
+    assert _step(0, _group(k=1001), _args()) == csa2.ERR_INVALID_ARG         # k > N_cap
+    assert _step(0, _group(n_valid_max=1001), _args()) == csa2.ERR_INVALID_ARG
+    assert _step(0, _group(), _args(new_entry=None)) == csa2.ERR_INVALID_ARG  # Full needs new rows
+    assert _step(1, _group(), _args(iq=None)) == csa2.ERR_INVALID_ARG        # Reindex needs iq
+    assert _step(0, _group(sel_rows=1), _args()) == csa2.ERR_INVALID_ARG     # sel too small
+    assert _step(0, _group(), _args(Hq=0)) == csa2.ERR_INVALID_ARG
+    assert _step(0, _group(), _args(), ws_bytes=100) == csa2.ERR_WORKSPACE
+    assert _step(0, _group(B=70000), _args()) == csa2.ERR_UNSUPPORTED
