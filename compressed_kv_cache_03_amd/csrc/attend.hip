@@ -5,217 +5,346 @@
 // retrieved compressed positions plus the recent 128-token window);
 // "DeepSeek-V4.1-Flash", "Sharing the cache across layers" (each layer uses its
 // own queries and window).  An entry is one D-vector used as key and value and
-// shared by all Hq heads; window keys and values are bf16 rows.
+// shared by all query heads; window keys and values are bf16 rows.
 //
-// Split-k with an online softmax: a workgroup takes up to 128 keys of one query
-// row (a slice of the selection, or of the window), streams them through LDS in
-// sub-chunks, keeps (m, l) per head and the unnormalised output in registers,
-// and writes one partial (o, m, l).  attend_combine_kernel merges the partials
-// of a row in split order (m = max m_s, o = sum e^(m_s-m) o_s / sum e^(m_s-m) l_s),
-// so the result does not depend on scheduling.
+// One wave works on one (query row, split of the key list, group of 16 heads)
+// and walks its keys 32 at a time.  Both contractions run on bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16) in transposed form so that heads are the MFMA
+// columns and every per-head quantity stays in one lane:
+//   logits  S^T[key][h] = sum_d K[key][d] q[h][d]: one MFMA per 32-element scale
+//           block (A = the block's e2m1 codes converted exactly to bf16, B = q),
+//           then z = sum_blk S_blk^T * scale[key][blk] in fp32;
+//   output  O^T[d][h] += sum_key V^T[d][key] (p[key][h] scale[key][blk(d)]):
+//           A = exact codes of 16 d-rows of one block, B = p*scale split into a
+//           bf16 high part and a bf16 remainder (two MFMAs, 16 significant bits).
+// Products are exact (bf16 x e2m1, bf16 x bf16) and accumulate in fp32; the
+// only rounding beyond fp32 is the 2^-17 relative split of p*scale.
+//
+// Register layouts (lane = m + 16 g, m = lane % 16, g = lane / 16):
+//   MFMA A[row][kslot]: lane holds row m, kslots 8g .. 8g+7
+//   MFMA B[kslot][col]: lane holds column m, kslots 8g .. 8g+7
+//   MFMA C[row][col]  : lane holds column m, rows 4g .. 4g+3
+// Logit tile kt (keys 16kt .. 16kt+15 of a step) leaves lane (h=m, g) with keys
+// 16kt + 4g + i (i = 0..3); the output contraction uses kslot 8g+e <-> key
+// 4g+e (e < 4) or 16+4g+(e-4) (e >= 4), which is exactly what the lane holds.
+// Output tile (blk, half) has rows d = 32 blk + 2 row + half, so one code byte
+// (16 blk + row) feeds both halves and every tile lies in one scale block.
+//
+// Splits: the key list is the selection padded to a multiple of 32 followed by
+// the window padded to a multiple of 32; a split is a run of 32-key steps.
+// With one split per row the wave writes the normalised output; otherwise it
+// writes a partial (o, m, l) and attend_combine_kernel merges the partials of
+// a row in split order, so results do not depend on scheduling.
 #include "common.h"
 #include "launch.h"
 
 namespace csa2 {
 
-constexpr int kAttThreads = 256;
-constexpr int kKeysPerSplit = 128;
-constexpr int kMaxOut = 32;  // outputs per thread: Hq*D/256 rounded up to 8-wide groups
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// e2m1 magnitudes (OCP MX FP4)
-__constant__ float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+constexpr int kStep = 32;          // keys per step
+constexpr int kTargetWaves = 1024; // below this many waves a row's keys are split
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
-CSA2_DEV float e2m1(uint32_t c) {
-    const float m = kE2M1[c & 7u];
-    return (c & 8u) ? -m : m;
+CSA2_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Two e2m1 codes of byte `sel` of w -> bf16 pair (low nibble in the low half), exact.
+template <int SEL>
+CSA2_DEV uint32_t fp4x2_bf16(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
 }
 
-// LDS of one workgroup for a sub-chunk of `sub` keys: q [Hq][D+1], K [sub][D+1]
-// (padded: logits walk d with different keys per lane), V [sub][D] (PV reads
-// contiguous d), p [Hq][sub], per-head m, l, alpha, and the key validity list.
-// The q and K regions are rounded up to 4 floats so that V rows stay 16-byte aligned.
-CSA2_DEV_HOST_INLINE int align4(int x) { return (x + 3) & ~3; }
-
-static size_t attend_lds(int Hq, int D, int sub) {
-    return 4u * ((size_t)align4(Hq * (D + 1)) + (size_t)align4(sub * (D + 1)) + (size_t)sub * D +
-                 (size_t)Hq * sub + 3u * Hq + sub);
+// Eight codes of one dword -> eight bf16 values in element order.
+CSA2_DEV u32x4 fp4x8_bf16(uint32_t w) {
+    return u32x4{fp4x2_bf16<0>(w), fp4x2_bf16<1>(w), fp4x2_bf16<2>(w), fp4x2_bf16<3>(w)};
 }
 
-static int attend_sub(int Hq, int D) {
-    for (int sub = 32; sub >= 4; sub >>= 1)
-        if (attend_lds(Hq, D, sub) <= 65536) return sub;
-    return 4;
+// Low (SEL=0) or high (SEL=1) bf16 halves of a and b packed as (a, b).
+CSA2_DEV uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+CSA2_DEV uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): |x - hi - lo| <= 2^-17 |x|.
+CSA2_DEV void split_bf16(const float (&x)[8], u32x4& hi, u32x4& lo) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 hb = (__bf16)x[e];
+        const __bf16 lb = (__bf16)(x[e] - (float)hb);
+        h[e] = __builtin_bit_cast(uint16_t, hb);
+        l[e] = __builtin_bit_cast(uint16_t, lb);
+    }
+    hi = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    lo = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
 }
 
-void attend_splits(int Hq, int D, int k, int W, int* splits_g, int* splits_w) {
-    (void)Hq;
+CSA2_DEV f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+CSA2_DEV int kslot_key(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
+
+void attend_splits(int64_t R, int Hq, int D, int k, int W, int* splits, int* chunk) {
     (void)D;
-    *splits_g = (k + kKeysPerSplit - 1) / kKeysPerSplit;
-    *splits_w = (W + kKeysPerSplit - 1) / kKeysPerSplit;
+    const int kv = ((k + kStep - 1) / kStep + (W + kStep - 1) / kStep) * kStep;
+    const int64_t groups = R * ((Hq + 15) / 16);
+    const int steps = kv / kStep;
+    int64_t want = (kTargetWaves + groups - 1) / groups;  // splits per row to reach the target
+    if (want < 1) want = 1;
+    if (want > (steps + 1) / 2) want = (steps + 1) / 2;   // at least two steps per split
+    if (want < 1) want = 1;
+    const int steps_per = (int)((steps + want - 1) / want);
+    *chunk = steps_per * kStep;
+    *splits = steps == 0 ? 1 : (steps + steps_per - 1) / steps_per;
 }
 
-__global__ __launch_bounds__(kAttThreads) void attend_partial_kernel(AttendArgs a, int sub,
-                                                                     int splits_g, int splits) {
-    extern __shared__ float lds[];
-    const int Hq = a.Hq, D = a.D, DP = D + 1;
-    float* q_s = lds;                       // [Hq][DP]
-    float* k_s = q_s + align4(Hq * DP);     // [sub][DP]
-    float* v_s = k_s + align4(sub * DP);    // [sub][D], 16-byte aligned rows
-    float* p_s = v_s + sub * D;             // [Hq][sub]
-    float* m_s = p_s + Hq * sub;            // [Hq]
-    float* l_s = m_s + Hq;                  // [Hq]
-    float* al_s = l_s + Hq;                 // [Hq]
-    int* valid_s = reinterpret_cast<int*>(al_s + Hq);  // [sub]
+template <int NB>
+__global__ __launch_bounds__(64) void attend_kernel(AttendArgs a, int chunk, int splits) {
+    constexpr int D = 32 * NB;
+    constexpr int PITCH = 4 * NB + 4;  // staged code row, dwords (16-byte aligned rows)
+    __shared__ __attribute__((aligned(16))) uint32_t lcode[kStep * PITCH];
+    __shared__ __attribute__((aligned(16))) float lscale[kStep * NB];
 
+    const int lane = threadIdx.x;
+    const int m = lane & 15, g = lane >> 4;
     const int64_t r = blockIdx.y;
     const int split = blockIdx.x;
-    const int64_t b = r / a.Qs, i = r % a.Qs;
-    const bool is_win = split >= splits_g;
-    const int t0 = (is_win ? split - splits_g : split) * kKeysPerSplit;
-    const int nkeys = is_win ? a.W : a.k;
+    const int h = blockIdx.z * 16 + m;  // head of this lane's MFMA column
+    const bool hvalid = h < a.Hq;
+    const int64_t b = r / a.Qs, qi = r % a.Qs;
+    const int k32 = (a.k + kStep - 1) / kStep * kStep;
+    const int kv = k32 + (a.W + kStep - 1) / kStep * kStep;
+    const int v0 = split * chunk;
+    const int v1 = min(v0 + chunk, kv);
     const int64_t wrows = (int64_t)a.Qs + a.W - 1;
     const int64_t wfirst = a.wlen ? wrows - a.wlen[b] : 0;
+    const float c2 = a.sm_scale * kLog2e;
 
-    // query row, bf16 -> fp32; per-head softmax state
-    const uint16_t* qr = a.q + r * (int64_t)Hq * D;
-    for (int e = threadIdx.x; e < Hq * D; e += kAttThreads) q_s[(e / D) * DP + (e % D)] = bf16_to_f32(qr[e]);
-    for (int h = threadIdx.x; h < Hq; h += kAttThreads) {
-        m_s[h] = -INFINITY;
-        l_s[h] = 0.0f;
+    // q fragment: q[r][h][32 blk + 8g .. +7]
+    u32x4 qf[NB];
+    {
+        const uint16_t* qh = a.q + (r * a.Hq + (hvalid ? h : 0)) * (int64_t)D + 8 * g;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+            qf[blk] = hvalid ? *reinterpret_cast<const u32x4*>(qh + 32 * blk) : u32x4{0u, 0u, 0u, 0u};
     }
 
-    // output ownership: thread t holds 8 consecutive d of one head per pass
-    const int tph = D / 8;                 // threads per head
-    const int hpp = kAttThreads / tph;     // heads per pass
-    const int passes = (Hq + hpp - 1) / hpp;
-    const int my_h0 = threadIdx.x / tph, my_d0 = (threadIdx.x % tph) * 8;
-    const bool owns = my_h0 < hpp;         // when tph does not divide 256, the last threads idle
-    float o[kMaxOut];
+    f32x4 o[NB][2];
 #pragma unroll
-    for (int u = 0; u < kMaxOut; ++u) o[u] = 0.0f;
+    for (int blk = 0; blk < NB; ++blk) o[blk][0] = o[blk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.0f;  // log2 domain; l_run covers this lane's keys only
 
-    const int t_end = min(t0 + kKeysPerSplit, nkeys);
-    for (int tb = t0; tb < t_end; tb += sub) {
-        __syncthreads();  // previous sub-chunk fully consumed (and q_s, m_s ready)
-        if (threadIdx.x < sub) {
-            const int t = tb + threadIdx.x;
-            int v = -1;
-            if (t < t_end) {
-                if (!is_win) {
-                    const int32_t j = a.idx[r * a.k + t];
-                    v = (j >= 0 && j < a.N) ? j : -1;
-                } else {
-                    const int64_t row = i + t;
-                    v = (row >= wfirst && row < wrows) ? t : -1;
+    for (int v = v0; v < v1; v += kStep) {
+        const bool win = v >= k32;
+        float z[2][4];
+        float sc[8][NB];  // scale[kslot_key(g, e)][blk] (selected entries)
+        uint64_t vmask;
+        if (!win) {
+            // ---- stage 32 selected records (codes and scales) in LDS
+            int32_t j = -1;
+            if (lane < kStep) {
+                const int t = v + lane;
+                if (t < a.k) {
+                    j = a.idx[r * a.k + t];
+                    if (j >= a.N) j = -1;
                 }
             }
-            valid_s[threadIdx.x] = v;
-        }
-        __syncthreads();
-        if (!is_win) {
-            const int per_row = D / 8;  // 8 elements (4 code bytes) per task
-            for (int task = threadIdx.x; task < sub * per_row; task += kAttThreads) {
-                const int t = task / per_row, part = task % per_row;
-                const int32_t j = valid_s[t];
-                float v8[8];
-                if (j >= 0) {
-                    const int64_t rec = b * a.N + j;
-                    const uint32_t w = *reinterpret_cast<const uint32_t*>(a.codes + rec * (D / 2) + part * 4);
-                    const float sc = a.scales[rec * (D / 32) + part / 4];
+            vmask = __ballot(j >= 0);
+            if (vmask == 0) continue;  // nothing valid in this step (wave-uniform)
+            {
+                const int x = lane >> 1, part = lane & 1;
+                const int jx = __shfl(j, x);
+                uint32_t* dst = lcode + x * PITCH + part * (2 * NB);
+                if (jx >= 0) {
+                    const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                        a.codes + (b * a.N + jx) * (int64_t)(16 * NB)) + part * (2 * NB);
+                    // a half row is 2*NB dwords at an 8*NB-byte offset: 16-byte
+                    // pieces when NB is even, 8-byte pieces otherwise
+                    if constexpr (NB % 2 == 0) {
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) v8[u] = e2m1((w >> (4 * u)) & 15u) * sc;
+                        for (int c = 0; c < NB / 2; ++c)
+                            *reinterpret_cast<u32x4*>(dst + 4 * c) = *reinterpret_cast<const u32x4*>(src + 4 * c);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < NB; ++c)
+                            *reinterpret_cast<uint2*>(dst + 2 * c) = *reinterpret_cast<const uint2*>(src + 2 * c);
+                    }
                 } else {
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) v8[u] = 0.0f;
+                    for (int c = 0; c < 2 * NB; ++c) dst[c] = 0u;
+                }
+                if (lane < kStep) {
+                    const float* s = a.scales + (b * a.N + (j >= 0 ? j : 0)) * (int64_t)NB;
+#pragma unroll
+                    for (int blk = 0; blk < NB; ++blk) lscale[lane * NB + blk] = j >= 0 ? s[blk] : 0.0f;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk) sc[e][blk] = lscale[kslot_key(g, e) * NB + blk];
+            // ---- logits
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                f32x4 acc[NB];
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk) {
+                    const uint32_t w = lcode[(16 * kt + m) * PITCH + 4 * blk + g];
+                    acc[blk] = mfma(fp4x8_bf16(w), qf[blk], f32x4{0.f, 0.f, 0.f, 0.f});
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    k_s[t * DP + part * 8 + u] = v8[u];
-                    v_s[t * D + part * 8 + u] = v8[u];
+                for (int i = 0; i < 4; ++i) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int blk = 0; blk < NB; ++blk) s = fmaf(acc[blk][i], sc[4 * kt + i][blk], s);
+                    const int x = 16 * kt + 4 * g + i;
+                    z[kt][i] = (vmask >> x) & 1u ? s * c2 : -INFINITY;
                 }
             }
         } else {
-            for (int e = threadIdx.x; e < sub * D; e += kAttThreads) {
-                const int t = e / D, d = e % D;
-                const bool ok = valid_s[t] >= 0;
-                const int64_t row = b * wrows + i + tb + t;
-                k_s[t * DP + d] = ok ? bf16_to_f32(a.wk[row * D + d]) : 0.0f;
-                v_s[t * D + d] = ok ? bf16_to_f32(a.wv[row * D + d]) : 0.0f;
+            // ---- window rows t = v - k32 + x, buffer row qi + t
+            const int t0 = v - k32;
+            {
+                const int t = t0 + lane;
+                const bool ok = lane < kStep && t < a.W && qi + t >= wfirst;
+                vmask = __ballot(ok);
             }
-        }
-        __syncthreads();
-        // logits of this sub-chunk
-        for (int task = threadIdx.x; task < Hq * sub; task += kAttThreads) {
-            const int h = task / sub, t = task % sub;
-            float z = -INFINITY;
-            if (valid_s[t] >= 0) {
-                float acc = 0.0f;
-                const float* qh = q_s + h * DP;
-                const float* kt = k_s + t * DP;
-                for (int d = 0; d < D; ++d) acc = fmaf(qh[d], kt[d], acc);
-                z = a.sm_scale * acc;
-            }
-            p_s[h * sub + t] = z;
-        }
-        __syncthreads();
-        // online softmax update per head
-        for (int h = threadIdx.x; h < Hq; h += kAttThreads) {
-            const float m_old = m_s[h];
-            float m_new = m_old;
-            for (int t = 0; t < sub; ++t) m_new = fmaxf(m_new, p_s[h * sub + t]);
-            float lsum = 0.0f;
-            for (int t = 0; t < sub; ++t) {
-                const float z = p_s[h * sub + t];
-                const float p = (z == -INFINITY) ? 0.0f : expf(z - m_new);
-                p_s[h * sub + t] = p;
-                lsum += p;
-            }
-            const float alpha = (m_old == -INFINITY) ? 0.0f : expf(m_old - m_new);
-            al_s[h] = alpha;
-            l_s[h] = l_s[h] * alpha + lsum;
-            m_s[h] = m_new;
-        }
-        __syncthreads();
-        // o = o * alpha + p V
-        for (int ps = 0; ps < passes && owns; ++ps) {
-            const int h = ps * hpp + my_h0;
-            if (h >= Hq) break;
-            const float alpha = al_s[h];
-            float acc[8];
+            if (vmask == 0) continue;
+            const uint16_t* wkb = a.wk + (b * wrows + qi + t0) * (int64_t)D;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc[u] = o[ps * 8 + u] * alpha;
-            for (int t = 0; t < sub; ++t) {
-                const float p = p_s[h * sub + t];
-                const float4 va = *reinterpret_cast<const float4*>(v_s + t * D + my_d0);
-                const float4 vb = *reinterpret_cast<const float4*>(v_s + t * D + my_d0 + 4);
-                acc[0] = fmaf(p, va.x, acc[0]);
-                acc[1] = fmaf(p, va.y, acc[1]);
-                acc[2] = fmaf(p, va.z, acc[2]);
-                acc[3] = fmaf(p, va.w, acc[3]);
-                acc[4] = fmaf(p, vb.x, acc[4]);
-                acc[5] = fmaf(p, vb.y, acc[5]);
-                acc[6] = fmaf(p, vb.z, acc[6]);
-                acc[7] = fmaf(p, vb.w, acc[7]);
-            }
+            for (int kt = 0; kt < 2; ++kt) {
+                const int x = 16 * kt + m;
+                const bool okx = (vmask >> x) & 1u;
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 8; ++u) o[ps * 8 + u] = acc[u];
+                for (int blk = 0; blk < NB; ++blk) {
+                    const u32x4 kw = okx ? *reinterpret_cast<const u32x4*>(wkb + x * (int64_t)D + 32 * blk + 8 * g)
+                                         : u32x4{0u, 0u, 0u, 0u};
+                    acc = mfma(kw, qf[blk], acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int xi = 16 * kt + 4 * g + i;
+                    z[kt][i] = (vmask >> xi) & 1u ? acc[i] * c2 : -INFINITY;
+                }
+            }
+        }
+
+        // ---- online softmax (per lane: head h, keys kslot_key(g, *))
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, z[kt][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run, tmax);  // finite: the step has a valid key
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float p[8];
+        float psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(z[e >> 2][e & 3] - m_new);
+            psum += p[e];
+        }
+        l_run = fmaf(l_run, alpha, psum);
+        if (__any(m_new != m_run)) {
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) o[blk][hf] *= alpha;
+        }
+        m_run = m_new;
+
+        // ---- output contraction
+        if (!win) {
+            const uint8_t* lbytes = reinterpret_cast<const uint8_t*>(lcode);
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                float pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] = p[e] * sc[e][blk];
+                u32x4 bhi, blo;
+                split_bf16(pv, bhi, blo);
+                uint32_t cv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    cv[e] = fp4x2_bf16<0>(lbytes[kslot_key(g, e) * (PITCH * 4) + 16 * blk + m]);
+                const u32x4 a0{pack_lo(cv[0], cv[1]), pack_lo(cv[2], cv[3]), pack_lo(cv[4], cv[5]),
+                               pack_lo(cv[6], cv[7])};
+                const u32x4 a1{pack_hi(cv[0], cv[1]), pack_hi(cv[2], cv[3]), pack_hi(cv[4], cv[5]),
+                               pack_hi(cv[6], cv[7])};
+                o[blk][0] = mfma(a0, bhi, o[blk][0]);
+                o[blk][0] = mfma(a0, blo, o[blk][0]);
+                o[blk][1] = mfma(a1, bhi, o[blk][1]);
+                o[blk][1] = mfma(a1, blo, o[blk][1]);
+            }
+            __syncthreads();  // staged records consumed before the next step overwrites them
+        } else {
+            u32x4 bhi, blo;
+            split_bf16(p, bhi, blo);
+            const uint16_t* wvb = a.wv + (b * wrows + qi + (v - k32)) * (int64_t)D;
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                uint32_t cv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int x = kslot_key(g, e);
+                    cv[e] = (vmask >> x) & 1u
+                                ? *reinterpret_cast<const uint32_t*>(wvb + x * (int64_t)D + 32 * blk + 2 * m)
+                                : 0u;
+                }
+                const u32x4 a0{pack_lo(cv[0], cv[1]), pack_lo(cv[2], cv[3]), pack_lo(cv[4], cv[5]),
+                               pack_lo(cv[6], cv[7])};
+                const u32x4 a1{pack_hi(cv[0], cv[1]), pack_hi(cv[2], cv[3]), pack_hi(cv[4], cv[5]),
+                               pack_hi(cv[6], cv[7])};
+                o[blk][0] = mfma(a0, bhi, o[blk][0]);
+                o[blk][0] = mfma(a0, blo, o[blk][0]);
+                o[blk][1] = mfma(a1, bhi, o[blk][1]);
+                o[blk][1] = mfma(a1, blo, o[blk][1]);
+            }
         }
     }
-    __syncthreads();
-    float* part = a.part + ((r * splits + split) * (int64_t)Hq) * (D + 2);
-    for (int ps = 0; ps < passes && owns; ++ps) {
-        const int h = ps * hpp + my_h0;
-        if (h >= Hq) break;
+
+    // ---- finish: l over the four lanes of head h, then output or partial
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (!hvalid) return;
+    // lane (h, g) owns d = 32 blk + 8g + e, e = 2i + half
+    if (splits == 1) {
+        const bool empty = m_run == -INFINITY;
+        const float inv = empty ? 0.0f : 1.0f / l_tot;
+        float* out = a.out + (r * a.Hq + h) * (int64_t)D + 8 * g;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) part[h * (D + 2) + my_d0 + u] = o[ps * 8 + u];
-    }
-    for (int h = threadIdx.x; h < Hq; h += kAttThreads) {
-        part[h * (D + 2) + D] = m_s[h];
-        part[h * (D + 2) + D + 1] = l_s[h];
+        for (int blk = 0; blk < NB; ++blk) {
+            const f32x4 lo4{o[blk][0][0] * inv, o[blk][1][0] * inv, o[blk][0][1] * inv, o[blk][1][1] * inv};
+            const f32x4 hi4{o[blk][0][2] * inv, o[blk][1][2] * inv, o[blk][0][3] * inv, o[blk][1][3] * inv};
+            *reinterpret_cast<f32x4*>(out + 32 * blk) = lo4;
+            *reinterpret_cast<f32x4*>(out + 32 * blk + 4) = hi4;
+        }
+        if (g == 0 && a.lse) a.lse[r * a.Hq + h] = empty ? -INFINITY : m_run * kLn2 + logf(l_tot);
+    } else {
+        float* part = a.part + ((r * splits + split) * (int64_t)a.Hq + h) * (D + 2);
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            float* pd = part + 32 * blk + 8 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pd[2 * i] = o[blk][0][i];
+                pd[2 * i + 1] = o[blk][1][i];
+            }
+        }
+        if (g == 0) {
+            part[D] = m_run;
+            part[D + 1] = l_tot;
+        }
     }
 }
 
-// One workgroup per (row, head); thread d owns output element d.
+// One workgroup per (row, head); thread d owns output element d.  Partial
+// maxima are in log2 units.
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, int splits) {
     __shared__ float red[256];
     __shared__ float M_s;
@@ -223,9 +352,9 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, int s
     const int h = blockIdx.y;
     const int Hq = a.Hq, D = a.D;
     const float* part = a.part + r * (int64_t)splits * Hq * (D + 2);
-    float m = -INFINITY;
-    for (int s = threadIdx.x; s < splits; s += blockDim.x) m = fmaxf(m, part[((int64_t)s * Hq + h) * (D + 2) + D]);
-    red[threadIdx.x] = m;
+    float mx = -INFINITY;
+    for (int s = threadIdx.x; s < splits; s += blockDim.x) mx = fmaxf(mx, part[((int64_t)s * Hq + h) * (D + 2) + D]);
+    red[threadIdx.x] = mx;
     __syncthreads();
     if (threadIdx.x == 0) {
         float M = -INFINITY;
@@ -241,30 +370,37 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, int s
             const float* ps = part + ((int64_t)s * Hq + h) * (D + 2);
             const float ms = ps[D];
             if (ms == -INFINITY) continue;
-            const float w = expf(ms - M);
+            const float w = exp2f(ms - M);
             L = fmaf(w, ps[D + 1], L);
             if (d < D) O = fmaf(w, ps[d], O);
         }
     }
     if (d < D) a.out[(r * Hq + h) * D + d] = M == -INFINITY ? 0.0f : O / L;
-    if (d == 0 && a.lse) a.lse[r * Hq + h] = M == -INFINITY ? -INFINITY : M + logf(L);
+    if (d == 0 && a.lse) a.lse[r * Hq + h] = M == -INFINITY ? -INFINITY : M * kLn2 + logf(L);
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
     const int64_t R = (int64_t)a.B * a.Qs;
     if (R == 0) return hipSuccess;
-    const int sub = attend_sub(a.Hq, a.D);
-    int sg, sw;
-    attend_splits(a.Hq, a.D, a.k, a.W, &sg, &sw);
-    const int splits = sg + sw;
-    if (splits > 0) {
-        const size_t lds = attend_lds(a.Hq, a.D, sub);
-        hipLaunchKernelGGL(attend_partial_kernel, dim3((unsigned)splits, (unsigned)R), dim3(kAttThreads),
-                           lds, stream, a, sub, sg, splits);
+    int splits, chunk;
+    attend_splits(R, a.Hq, a.D, a.k, a.W, &splits, &chunk);
+    const dim3 grid((unsigned)splits, (unsigned)R, (unsigned)((a.Hq + 15) / 16));
+    switch (a.D / 32) {
+        case 1: hipLaunchKernelGGL(attend_kernel<1>, grid, dim3(64), 0, stream, a, chunk, splits); break;
+        case 2: hipLaunchKernelGGL(attend_kernel<2>, grid, dim3(64), 0, stream, a, chunk, splits); break;
+        case 3: hipLaunchKernelGGL(attend_kernel<3>, grid, dim3(64), 0, stream, a, chunk, splits); break;
+        case 4: hipLaunchKernelGGL(attend_kernel<4>, grid, dim3(64), 0, stream, a, chunk, splits); break;
+        case 5: hipLaunchKernelGGL(attend_kernel<5>, grid, dim3(64), 0, stream, a, chunk, splits); break;
+        case 6: hipLaunchKernelGGL(attend_kernel<6>, grid, dim3(64), 0, stream, a, chunk, splits); break;
+        case 7: hipLaunchKernelGGL(attend_kernel<7>, grid, dim3(64), 0, stream, a, chunk, splits); break;
+        case 8: hipLaunchKernelGGL(attend_kernel<8>, grid, dim3(64), 0, stream, a, chunk, splits); break;
+        default: return hipErrorInvalidValue;
     }
-    const unsigned threads = a.D <= 64 ? 64u : (a.D <= 128 ? 128u : 256u);
-    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)R, (unsigned)a.Hq), dim3(threads), 0, stream,
-                       a, splits);
+    if (splits > 1) {
+        const unsigned threads = a.D <= 64 ? 64u : (a.D <= 128 ? 128u : 256u);
+        hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)R, (unsigned)a.Hq), dim3(threads), 0,
+                           stream, a, splits);
+    }
     return hipGetLastError();
 }
 

@@ -52,9 +52,9 @@ void add_topk(Layout& L, size_t& off, const TopkShape& t) {
 }
 
 size_t attend_part_bytes(int64_t R, int Hq, int D, int k, int W) {
-    int sg, sw;
-    attend_splits(Hq, D, k, W, &sg, &sw);
-    return (size_t)R * (sg + sw) * Hq * (D + 2) * 4;
+    int splits, chunk;
+    attend_splits(R, Hq, D, k, W, &splits, &chunk);
+    return splits > 1 ? (size_t)R * splits * Hq * (D + 2) * 4 : 0;
 }
 
 Layout layer_layout(const csa2_group* g, int Qs, int Hq, int W) {
@@ -214,7 +214,8 @@ csa2_status csa2_sparse_attend(const void* q, int32_t B, int32_t Qs, int32_t Hq,
     if (!q || !out) return CSA2_ERR_INVALID_ARG;
     if (k > 0 && (!idx || !codes || !scales)) return CSA2_ERR_INVALID_ARG;
     if (W > 0 && (!wk || !wv)) return CSA2_ERR_INVALID_ARG;
-    if (!aligned(q, 4) || !aligned(out, 4) || (codes && !aligned(codes, 4)))
+    if (!aligned(q, 16) || !aligned(out, 16) || (codes && !aligned(codes, 16)) ||
+        (scales && !aligned(scales, 16)) || (wk && !aligned(wk, 16)) || (wv && !aligned(wv, 16)))
         return CSA2_ERR_INVALID_ARG;
     const size_t need = csa2_attend_workspace_bytes(B, Qs, Hq, D, k, W);
     if (!ws || ws_bytes < need) return CSA2_ERR_WORKSPACE;
@@ -268,7 +269,9 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
     if ((int64_t)g->B * Qs > 65535) return CSA2_ERR_UNSUPPORTED;
     if (g->sel_rows < (int64_t)g->B * Qs) return CSA2_ERR_INVALID_ARG;
     if (!a->q || !a->out || (a->W > 0 && (!a->wk || !a->wv))) return CSA2_ERR_INVALID_ARG;
-    if (!aligned(a->q, 4) || !aligned(a->out, 4)) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(a->q, 16) || !aligned(a->out, 16) || (a->wk && !aligned(a->wk, 16)) ||
+        (a->wv && !aligned(a->wv, 16)))
+        return CSA2_ERR_INVALID_ARG;
     const bool selects = mode != CSA2_MODE_REUSE;
     if (selects && (!a->iq || !aligned(a->iq, 16))) return CSA2_ERR_INVALID_ARG;
     if (mode == CSA2_MODE_FULL &&

@@ -78,10 +78,10 @@ struct AttendArgs {
     float sm_scale;
     float* out;           // [R][Hq][D]
     float* lse;           // [R][Hq] or null
-    float* part;          // [R][splits][Hq][D+2]
-    int splits_g, splits_w;
+    float* part;          // [R][splits][Hq][D+2] when a row is split, else unused
 };
-void attend_splits(int Hq, int D, int k, int W, int* splits_g, int* splits_w);
+// Splits per query row (and keys per split) used by launch_attend for R rows.
+void attend_splits(int64_t R, int Hq, int D, int k, int W, int* splits, int* chunk);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
 
 }  // namespace csa2

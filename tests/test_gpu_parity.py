@@ -147,6 +147,11 @@ def test_topk_parity(k):
     (2, 4, 16, 128, 128, 64, None),
     (2, 3, 4, 64, 8, 40, [8, 2]),
     (1, 1, 32, 256, 16, 33, None),
+    (2, 3, 16, 96, 40, 70, [40, 3]),        # odd number of scale blocks
+    (1, 1, 8, 160, 128, 200, None),
+    (1, 1100, 16, 128, 16, 64, None),       # enough rows for one split per row
+    (2, 1, 16, 128, 128, 0, [128, 50]),     # window only
+    (2, 2, 16, 128, 0, 96, None),           # no window
 ])
 def test_attend_parity(B, Qs, Hq, D, W, k, wlen):
     N = 3000
