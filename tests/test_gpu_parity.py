@@ -140,6 +140,18 @@ def test_topk_parity(k):
     assert np.array_equal(host(got), ref)
 
 
+def test_topk_parity_long_row_multi_pass_slices():
+    # beyond 2^24 entries a slice spans several 4096-entry compaction passes
+    N = (1 << 24) + 5000
+    rng = np.random.default_rng(5)
+    s = rng.normal(size=(1, N)).astype(np.float32)
+    s[0, rng.integers(0, N, 4000)] = s[0, rng.integers(0, N, 4000)]
+    for k in (2048, 7000):
+        got = csa2.topk(dev(s), k)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(got), oracle.topk(s, k))
+
+
 # ---------------------------------------------------------------- S5+S6 attend
 @pytest.mark.parametrize("B,Qs,Hq,D,W,k,wlen", [
     (3, 1, 16, 128, 128, 300, None),
