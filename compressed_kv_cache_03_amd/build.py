@@ -15,8 +15,11 @@ ARCH = os.environ.get("CSA2_OFFLOAD_ARCH", "gfx950")
 SOURCES = ["pack.hip", "score.hip", "topk.hip", "attend.hip", "csa2_api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in ordinary VGPRs, so the softmax
+#   arithmetic on them needs no accumulator-register copies.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wno-unused-command-line-argument"]
 
 

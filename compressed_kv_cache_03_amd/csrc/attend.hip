@@ -18,7 +18,7 @@
 //           A = exact codes of 16 d-rows of one block, B = p*scale split into a
 //           bf16 high part and a bf16 remainder (two MFMAs, 16 significant bits).
 // Products are exact (bf16 x e2m1, bf16 x bf16) and accumulate in fp32; the
-// only rounding beyond fp32 is the 2^-17 relative split of p*scale.
+// only rounding beyond fp32 is the 2^-16 relative split of p*scale.
 //
 // Register layouts (lane = m + 16 g, m = lane % 16, g = lane / 16):
 //   MFMA A[row][kslot]: lane holds row m, kslots 8g .. 8g+7
@@ -65,18 +65,20 @@ CSA2_DEV u32x4 fp4x8_bf16(uint32_t w) {
 CSA2_DEV uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 CSA2_DEV uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): |x - hi - lo| <= 2^-17 |x|.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// x = hi + lo in bf16 pairs: hi = x with its low 16 bits cleared, lo = the
+// exact remainder x - hi rounded to bf16, so |x - hi - lo| <= 2^-16 |x|.
 CSA2_DEV void split_bf16(const float (&x)[8], u32x4& hi, u32x4& lo) {
-    uint32_t h[8], l[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 hb = (__bf16)x[e];
-        const __bf16 lb = (__bf16)(x[e] - (float)hb);
-        h[e] = __builtin_bit_cast(uint16_t, hb);
-        l[e] = __builtin_bit_cast(uint16_t, lb);
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t u0 = __float_as_uint(x[2 * q]), u1 = __float_as_uint(x[2 * q + 1]);
+        const float r0 = x[2 * q] - __uint_as_float(u0 & 0xffff0000u);
+        const float r1 = x[2 * q + 1] - __uint_as_float(u1 & 0xffff0000u);
+        hi[q] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        lo[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
     }
-    hi = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    lo = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
 }
 
 CSA2_DEV f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
@@ -99,6 +101,66 @@ void attend_splits(int64_t R, int Hq, int D, int k, int W, int* splits, int* chu
     *splits = steps == 0 ? 1 : (steps + steps_per - 1) / steps_per;
 }
 
+// Online-softmax state of one wave: this lane's head h, its running maximum
+// (log2 units), its share of the normaliser (the lane's own keys) and the
+// unnormalised output tiles O^T[d][h], d = 32 blk + 2(4g+i) + half.
+template <int NB>
+struct SoftmaxState {
+    f32x4 o[NB][2];
+    float m_run, l_run;
+
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) o[blk][0] = o[blk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.0f;
+    }
+
+    // z: log2-scaled logits of the step's keys kslot_key(g, e) (-inf = masked),
+    // at least one finite.  Returns p = 2^(z - m_run) in kslot order.  The
+    // reference m_run moves (and o, l are rescaled) only when a logit exceeds
+    // it by more than kLazy, so p <= 2^kLazy and the common step rescales
+    // nothing; the result is the same softmax since o and l share the factor.
+    __device__ __forceinline__ void update(const float (&z)[8], float (&p)[8]) {
+        constexpr float kLazy = 8.0f;
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, z[e]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        if (__any(tmax > m_run + kLazy)) {  // wave-uniform
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) o[blk][hf] *= alpha;
+            m_run = m_new;
+        }
+        float psum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(z[e] - m_run);
+            psum += p[e];
+        }
+        l_run += psum;
+    }
+
+    // O^T[tile blk] += V^T (bhi + blo) for the two half tiles of block blk;
+    // cv[e] holds the bf16 pair (d even, d odd) of key kslot_key(g, e).
+    __device__ __forceinline__ void accumulate(int blk, const uint32_t (&cv)[8], u32x4 bhi, u32x4 blo) {
+        const u32x4 a0{pack_lo(cv[0], cv[1]), pack_lo(cv[2], cv[3]), pack_lo(cv[4], cv[5]),
+                       pack_lo(cv[6], cv[7])};
+        const u32x4 a1{pack_hi(cv[0], cv[1]), pack_hi(cv[2], cv[3]), pack_hi(cv[4], cv[5]),
+                       pack_hi(cv[6], cv[7])};
+        o[blk][0] = mfma(a0, bhi, o[blk][0]);
+        o[blk][1] = mfma(a1, bhi, o[blk][1]);
+        o[blk][0] = mfma(a0, blo, o[blk][0]);
+        o[blk][1] = mfma(a1, blo, o[blk][1]);
+    }
+};
+
 template <int NB>
 __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a, int chunk, int splits) {
     constexpr int D = 32 * NB;
@@ -117,8 +179,6 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a, int chunk, int
     const int kv = k32 + (a.W + kStep - 1) / kStep * kStep;
     const int v0 = split * chunk;
     const int v1 = min(v0 + chunk, kv);
-    const int64_t wrows = (int64_t)a.Qs + a.W - 1;
-    const int64_t wfirst = a.wlen ? wrows - a.wlen[b] : 0;
     const float c2 = a.sm_scale * kLog2e;
 
     // q fragment: q[r][h][32 blk + 8g .. +7]
@@ -129,202 +189,194 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a, int chunk, int
         for (int blk = 0; blk < NB; ++blk)
             qf[blk] = hvalid ? *reinterpret_cast<const u32x4*>(qh + 32 * blk) : u32x4{0u, 0u, 0u, 0u};
     }
+    SoftmaxState<NB> st;
+    st.init();
 
-    f32x4 o[NB][2];
+    // ------------------------------------------------------------------
+    // Selected entries, software-pipelined: the indices of step s+2 and the
+    // records of step s+1 are in flight while step s computes.  Lanes 0..31
+    // hold one index each; lane (x = lane/2, part = lane%2) carries half of
+    // record x's codes, lane x < 32 its NB scales.  Loads are unconditional,
+    // from clamped in-bounds addresses, so that they issue back to back and
+    // nothing waits for them before it is used: an index slot beyond k reads
+    // slot k-1 and an empty or out-of-range entry reads record 0; such keys get
+    // logit -inf, so p = 0 multiplies finite data.  The last step prefetches a
+    // step it does not use.  With no entries (N = 0) this part is skipped.
+    const int vsel_end = a.N > 0 ? min(v1, k32) : v0;
+    auto load_idx = [&](int v) -> int32_t {
+        return a.idx[r * a.k + min(v + (lane & (kStep - 1)), a.k - 1)];
+    };
+    auto valid_j = [&](int v, int32_t j) -> bool {
+        return lane < kStep && v + lane < a.k && j >= 0 && j < a.N;
+    };
+    uint32_t cw[2 * NB];  // prefetched codes
+    float sw[NB];         // prefetched scales
+    auto load_rec = [&](int v, int32_t jraw) {
+        const int32_t j = valid_j(v, jraw) ? jraw : 0;
+        const int jx = __shfl(j, lane >> 1);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(
+            a.codes + (b * a.N + jx) * (int64_t)(16 * NB)) + (lane & 1) * (2 * NB);
+        // a half row is 2*NB dwords at an 8*NB-byte offset: 16-byte pieces
+        // when NB is even, 8-byte pieces otherwise
+        if constexpr (NB % 2 == 0) {
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) o[blk][0] = o[blk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;  // log2 domain; l_run covers this lane's keys only
-
-    for (int v = v0; v < v1; v += kStep) {
-        const bool win = v >= k32;
-        float z[2][4];
-        float sc[8][NB];  // scale[kslot_key(g, e)][blk] (selected entries)
-        uint64_t vmask;
-        if (!win) {
-            // ---- stage 32 selected records (codes and scales) in LDS
-            int32_t j = -1;
-            if (lane < kStep) {
-                const int t = v + lane;
-                if (t < a.k) {
-                    j = a.idx[r * a.k + t];
-                    if (j >= a.N) j = -1;
-                }
+            for (int c = 0; c < NB / 2; ++c) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(src + 4 * c);
+                cw[4 * c] = w[0]; cw[4 * c + 1] = w[1]; cw[4 * c + 2] = w[2]; cw[4 * c + 3] = w[3];
             }
-            vmask = __ballot(j >= 0);
-            if (vmask == 0) continue;  // nothing valid in this step (wave-uniform)
+        } else {
+#pragma unroll
+            for (int c = 0; c < NB; ++c) {
+                const uint2 w = *reinterpret_cast<const uint2*>(src + 2 * c);
+                cw[2 * c] = w.x; cw[2 * c + 1] = w.y;
+            }
+        }
+        const float* sp = a.scales + (b * a.N + j) * (int64_t)NB;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) sw[blk] = sp[blk];
+    };
+    if (v0 < vsel_end) {
+        int32_t j_cur = load_idx(v0);
+        load_rec(v0, j_cur);
+        int32_t j_nxt = load_idx(v0 + kStep);
+        for (int v = v0; v < vsel_end; v += kStep) {
+            // the prefetched records of this step go to LDS; the next step's loads start
+            const uint64_t vmask = __ballot(valid_j(v, j_cur));
             {
-                const int x = lane >> 1, part = lane & 1;
-                const int jx = __shfl(j, x);
-                uint32_t* dst = lcode + x * PITCH + part * (2 * NB);
-                if (jx >= 0) {
-                    const uint32_t* src = reinterpret_cast<const uint32_t*>(
-                        a.codes + (b * a.N + jx) * (int64_t)(16 * NB)) + part * (2 * NB);
-                    // a half row is 2*NB dwords at an 8*NB-byte offset: 16-byte
-                    // pieces when NB is even, 8-byte pieces otherwise
-                    if constexpr (NB % 2 == 0) {
+                uint32_t* dst = lcode + (lane >> 1) * PITCH + (lane & 1) * (2 * NB);
+                if constexpr (NB % 2 == 0) {
 #pragma unroll
-                        for (int c = 0; c < NB / 2; ++c)
-                            *reinterpret_cast<u32x4*>(dst + 4 * c) = *reinterpret_cast<const u32x4*>(src + 4 * c);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < NB; ++c)
-                            *reinterpret_cast<uint2*>(dst + 2 * c) = *reinterpret_cast<const uint2*>(src + 2 * c);
-                    }
+                    for (int c = 0; c < NB / 2; ++c)
+                        *reinterpret_cast<u32x4*>(dst + 4 * c) = u32x4{cw[4 * c], cw[4 * c + 1], cw[4 * c + 2], cw[4 * c + 3]};
                 } else {
 #pragma unroll
-                    for (int c = 0; c < 2 * NB; ++c) dst[c] = 0u;
+                    for (int c = 0; c < NB; ++c)
+                        *reinterpret_cast<uint2*>(dst + 2 * c) = uint2{cw[2 * c], cw[2 * c + 1]};
                 }
                 if (lane < kStep) {
-                    const float* s = a.scales + (b * a.N + (j >= 0 ? j : 0)) * (int64_t)NB;
 #pragma unroll
-                    for (int blk = 0; blk < NB; ++blk) lscale[lane * NB + blk] = j >= 0 ? s[blk] : 0.0f;
+                    for (int blk = 0; blk < NB; ++blk) lscale[lane * NB + blk] = sw[blk];
                 }
             }
+            load_rec(v + kStep, j_nxt);
+            j_cur = j_nxt;
+            j_nxt = load_idx(v + 2 * kStep);
             __syncthreads();
+            if (vmask != 0) {  // wave-uniform
+                float sc[8][NB];  // scale[kslot_key(g, e)][blk]
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+#pragma unroll
+                    for (int blk = 0; blk < NB; ++blk) sc[e][blk] = lscale[kslot_key(g, e) * NB + blk];
+                // logits S^T = K q^T, block by block, scaled per (key, block)
+                float z[8];
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    f32x4 acc[NB];
+#pragma unroll
+                    for (int blk = 0; blk < NB; ++blk) {
+                        const uint32_t w = lcode[(16 * kt + m) * PITCH + 4 * blk + g];
+                        acc[blk] = mfma(fp4x8_bf16(w), qf[blk], f32x4{0.f, 0.f, 0.f, 0.f});
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float sz = 0.0f;
+#pragma unroll
+                        for (int blk = 0; blk < NB; ++blk) sz = fmaf(acc[blk][i], sc[4 * kt + i][blk], sz);
+                        const int x = 16 * kt + 4 * g + i;
+                        z[4 * kt + i] = (vmask >> x) & 1u ? sz * c2 : -INFINITY;
+                    }
+                }
+                float p[8];
+                st.update(z, p);
+                // output: O^T += V^T (P scale)^T, one scale block at a time
+                const uint8_t* lbytes = reinterpret_cast<const uint8_t*>(lcode);
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk) {
+                    float pv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pv[e] = p[e] * sc[e][blk];
+                    u32x4 bhi, blo;
+                    split_bf16(pv, bhi, blo);
+                    uint32_t cv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        cv[e] = fp4x2_bf16<0>(lbytes[kslot_key(g, e) * (PITCH * 4) + 16 * blk + m]);
+                    st.accumulate(blk, cv, bhi, blo);
+                }
+            }
+            __syncthreads();  // staged records consumed before the next step overwrites them
+        }
+    }
+
+    // ------------------------------------------------------------------
+    // Window rows: step keys x = 0..31 are window slots t = v - k32 + x, buffer
+    // row qi + t, valid when t < W and the row is among the last wlen[b] rows.
+    // Rows are clamped to the last window row for the loads.
+    {
+        const int64_t wrows = (int64_t)a.Qs + a.W - 1;
+        const int64_t wfirst = a.wlen ? wrows - a.wlen[b] : 0;
+        for (int v = max(v0, k32); v < v1; v += kStep) {
+            const int t0 = v - k32;
+            const int t = t0 + lane;
+            const uint64_t vmask = __ballot(lane < kStep && t < a.W && qi + t >= wfirst);
+            if (vmask == 0) continue;  // wave-uniform
+            auto wrow = [&](int x) -> int64_t { return b * wrows + qi + min(t0 + x, a.W - 1); };
+            u32x4 kw[2][NB];
+            uint32_t wvv[8][NB];  // bf16 pair (32 blk + 2m, +1) of key kslot_key(g, e)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk)
+                    kw[kt][blk] = *reinterpret_cast<const u32x4*>(a.wk + wrow(16 * kt + m) * D + 32 * blk + 8 * g);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
 #pragma unroll
-                for (int blk = 0; blk < NB; ++blk) sc[e][blk] = lscale[kslot_key(g, e) * NB + blk];
-            // ---- logits
+                for (int blk = 0; blk < NB; ++blk)
+                    wvv[e][blk] = *reinterpret_cast<const uint32_t*>(a.wv + wrow(kslot_key(g, e)) * D + 32 * blk + 2 * m);
+            float z[8];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                f32x4 acc[NB];
-#pragma unroll
-                for (int blk = 0; blk < NB; ++blk) {
-                    const uint32_t w = lcode[(16 * kt + m) * PITCH + 4 * blk + g];
-                    acc[blk] = mfma(fp4x8_bf16(w), qf[blk], f32x4{0.f, 0.f, 0.f, 0.f});
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float s = 0.0f;
-#pragma unroll
-                    for (int blk = 0; blk < NB; ++blk) s = fmaf(acc[blk][i], sc[4 * kt + i][blk], s);
-                    const int x = 16 * kt + 4 * g + i;
-                    z[kt][i] = (vmask >> x) & 1u ? s * c2 : -INFINITY;
-                }
-            }
-        } else {
-            // ---- window rows t = v - k32 + x, buffer row qi + t
-            const int t0 = v - k32;
-            {
-                const int t = t0 + lane;
-                const bool ok = lane < kStep && t < a.W && qi + t >= wfirst;
-                vmask = __ballot(ok);
-            }
-            if (vmask == 0) continue;
-            const uint16_t* wkb = a.wk + (b * wrows + qi + t0) * (int64_t)D;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const int x = 16 * kt + m;
-                const bool okx = (vmask >> x) & 1u;
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int blk = 0; blk < NB; ++blk) {
-                    const u32x4 kw = okx ? *reinterpret_cast<const u32x4*>(wkb + x * (int64_t)D + 32 * blk + 8 * g)
-                                         : u32x4{0u, 0u, 0u, 0u};
-                    acc = mfma(kw, qf[blk], acc);
-                }
+                for (int blk = 0; blk < NB; ++blk) acc = mfma(kw[kt][blk], qf[blk], acc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int xi = 16 * kt + 4 * g + i;
-                    z[kt][i] = (vmask >> xi) & 1u ? acc[i] * c2 : -INFINITY;
+                    const int x = 16 * kt + 4 * g + i;
+                    z[4 * kt + i] = (vmask >> x) & 1u ? acc[i] * c2 : -INFINITY;
                 }
             }
-        }
-
-        // ---- online softmax (per lane: head h, keys kslot_key(g, *))
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, z[kt][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);  // finite: the step has a valid key
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float p[8];
-        float psum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(z[e >> 2][e & 3] - m_new);
-            psum += p[e];
-        }
-        l_run = fmaf(l_run, alpha, psum);
-        if (__any(m_new != m_run)) {
-#pragma unroll
-            for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) o[blk][hf] *= alpha;
-        }
-        m_run = m_new;
-
-        // ---- output contraction
-        if (!win) {
-            const uint8_t* lbytes = reinterpret_cast<const uint8_t*>(lcode);
-#pragma unroll
-            for (int blk = 0; blk < NB; ++blk) {
-                float pv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = p[e] * sc[e][blk];
-                u32x4 bhi, blo;
-                split_bf16(pv, bhi, blo);
-                uint32_t cv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    cv[e] = fp4x2_bf16<0>(lbytes[kslot_key(g, e) * (PITCH * 4) + 16 * blk + m]);
-                const u32x4 a0{pack_lo(cv[0], cv[1]), pack_lo(cv[2], cv[3]), pack_lo(cv[4], cv[5]),
-                               pack_lo(cv[6], cv[7])};
-                const u32x4 a1{pack_hi(cv[0], cv[1]), pack_hi(cv[2], cv[3]), pack_hi(cv[4], cv[5]),
-                               pack_hi(cv[6], cv[7])};
-                o[blk][0] = mfma(a0, bhi, o[blk][0]);
-                o[blk][0] = mfma(a0, blo, o[blk][0]);
-                o[blk][1] = mfma(a1, bhi, o[blk][1]);
-                o[blk][1] = mfma(a1, blo, o[blk][1]);
-            }
-            __syncthreads();  // staged records consumed before the next step overwrites them
-        } else {
+            float p[8];
+            st.update(z, p);
             u32x4 bhi, blo;
             split_bf16(p, bhi, blo);
-            const uint16_t* wvb = a.wv + (b * wrows + qi + (v - k32)) * (int64_t)D;
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk) {
                 uint32_t cv[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int x = kslot_key(g, e);
-                    cv[e] = (vmask >> x) & 1u
-                                ? *reinterpret_cast<const uint32_t*>(wvb + x * (int64_t)D + 32 * blk + 2 * m)
-                                : 0u;
-                }
-                const u32x4 a0{pack_lo(cv[0], cv[1]), pack_lo(cv[2], cv[3]), pack_lo(cv[4], cv[5]),
-                               pack_lo(cv[6], cv[7])};
-                const u32x4 a1{pack_hi(cv[0], cv[1]), pack_hi(cv[2], cv[3]), pack_hi(cv[4], cv[5]),
-                               pack_hi(cv[6], cv[7])};
-                o[blk][0] = mfma(a0, bhi, o[blk][0]);
-                o[blk][0] = mfma(a0, blo, o[blk][0]);
-                o[blk][1] = mfma(a1, bhi, o[blk][1]);
-                o[blk][1] = mfma(a1, blo, o[blk][1]);
+                for (int e = 0; e < 8; ++e) cv[e] = wvv[e][blk];
+                st.accumulate(blk, cv, bhi, blo);
             }
         }
     }
 
     // ---- finish: l over the four lanes of head h, then output or partial
-    float l_tot = l_run + __shfl_xor(l_run, 16);
+    float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
     if (!hvalid) return;
     // lane (h, g) owns d = 32 blk + 8g + e, e = 2i + half
     if (splits == 1) {
-        const bool empty = m_run == -INFINITY;
+        const bool empty = st.m_run == -INFINITY;
         const float inv = empty ? 0.0f : 1.0f / l_tot;
         float* out = a.out + (r * a.Hq + h) * (int64_t)D + 8 * g;
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
-            const f32x4 lo4{o[blk][0][0] * inv, o[blk][1][0] * inv, o[blk][0][1] * inv, o[blk][1][1] * inv};
-            const f32x4 hi4{o[blk][0][2] * inv, o[blk][1][2] * inv, o[blk][0][3] * inv, o[blk][1][3] * inv};
+            const f32x4 lo4{st.o[blk][0][0] * inv, st.o[blk][1][0] * inv, st.o[blk][0][1] * inv, st.o[blk][1][1] * inv};
+            const f32x4 hi4{st.o[blk][0][2] * inv, st.o[blk][1][2] * inv, st.o[blk][0][3] * inv, st.o[blk][1][3] * inv};
             *reinterpret_cast<f32x4*>(out + 32 * blk) = lo4;
             *reinterpret_cast<f32x4*>(out + 32 * blk + 4) = hi4;
         }
-        if (g == 0 && a.lse) a.lse[r * a.Hq + h] = empty ? -INFINITY : m_run * kLn2 + logf(l_tot);
+        if (g == 0 && a.lse) a.lse[r * a.Hq + h] = empty ? -INFINITY : st.m_run * kLn2 + logf(l_tot);
     } else {
         float* part = a.part + ((r * splits + split) * (int64_t)a.Hq + h) * (D + 2);
 #pragma unroll
@@ -332,51 +384,61 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a, int chunk, int
             float* pd = part + 32 * blk + 8 * g;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pd[2 * i] = o[blk][0][i];
-                pd[2 * i + 1] = o[blk][1][i];
+                pd[2 * i] = st.o[blk][0][i];
+                pd[2 * i + 1] = st.o[blk][1][i];
             }
         }
         if (g == 0) {
-            part[D] = m_run;
+            part[D] = st.m_run;
             part[D + 1] = l_tot;
         }
     }
 }
 
-// One workgroup per (row, head); thread d owns output element d.  Partial
-// maxima are in log2 units.
+// One workgroup of 256 threads per (row, head).  Thread t owns element
+// d = t % Dp of split group t / Dp (Dp = D rounded up to 64); each group takes
+// every G-th split with several loads in flight, and the groups are summed in
+// a fixed order.  Partial maxima are in log2 units.
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, int splits) {
-    __shared__ float red[256];
-    __shared__ float M_s;
+    __shared__ float red[4];
+    __shared__ float accO[256], accL[256];
     const int64_t r = blockIdx.x;
     const int h = blockIdx.y;
     const int Hq = a.Hq, D = a.D;
-    const float* part = a.part + r * (int64_t)splits * Hq * (D + 2);
+    const int Dp = (D + 63) / 64 * 64;
+    const int G = 256 / Dp;
+    const int t = threadIdx.x, d = t % Dp, grp = t / Dp;
+    const int64_t stride = (int64_t)Hq * (D + 2);
+    const float* part = a.part + (r * (int64_t)splits * Hq + h) * (D + 2);
     float mx = -INFINITY;
-    for (int s = threadIdx.x; s < splits; s += blockDim.x) mx = fmaxf(mx, part[((int64_t)s * Hq + h) * (D + 2) + D]);
-    red[threadIdx.x] = mx;
+    for (int s = t; s < splits; s += 256) mx = fmaxf(mx, part[s * stride + D]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((t & 63) == 0) red[t >> 6] = mx;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        float M = -INFINITY;
-        for (int t = 0; t < (int)blockDim.x; ++t) M = fmaxf(M, red[t]);
-        M_s = M;
-    }
-    __syncthreads();
-    const float M = M_s;
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     float L = 0.0f, O = 0.0f;
-    const int d = threadIdx.x;
-    if (M != -INFINITY) {
-        for (int s = 0; s < splits; ++s) {
-            const float* ps = part + ((int64_t)s * Hq + h) * (D + 2);
+    if (M != -INFINITY && grp < G) {
+#pragma unroll 4
+        for (int s = grp; s < splits; s += G) {
+            const float* ps = part + s * stride;
             const float ms = ps[D];
-            if (ms == -INFINITY) continue;
-            const float w = exp2f(ms - M);
+            const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
             L = fmaf(w, ps[D + 1], L);
             if (d < D) O = fmaf(w, ps[d], O);
         }
     }
-    if (d < D) a.out[(r * Hq + h) * D + d] = M == -INFINITY ? 0.0f : O / L;
-    if (d == 0 && a.lse) a.lse[r * Hq + h] = M == -INFINITY ? -INFINITY : M * kLn2 + logf(L);
+    accO[t] = O;
+    accL[t] = L;
+    __syncthreads();
+    if (grp == 0 && d < D) {
+        for (int q = 1; q < G; ++q) {
+            O += accO[q * Dp + d];
+            L += accL[q * Dp + d];
+        }
+        a.out[(r * Hq + h) * D + d] = M == -INFINITY ? 0.0f : O / L;
+        if (d == 0 && a.lse) a.lse[r * Hq + h] = M == -INFINITY ? -INFINITY : M * kLn2 + logf(L);
+    }
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
@@ -396,11 +458,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
         case 8: hipLaunchKernelGGL(attend_kernel<8>, grid, dim3(64), 0, stream, a, chunk, splits); break;
         default: return hipErrorInvalidValue;
     }
-    if (splits > 1) {
-        const unsigned threads = a.D <= 64 ? 64u : (a.D <= 128 ? 128u : 256u);
-        hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)R, (unsigned)a.Hq), dim3(threads), 0,
+    if (splits > 1)
+        hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)R, (unsigned)a.Hq), dim3(256), 0,
                            stream, a, splits);
-    }
     return hipGetLastError();
 }
 
