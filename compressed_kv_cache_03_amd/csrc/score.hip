@@ -25,8 +25,9 @@
 //     2^L with L = lsb(min|q|) + lsb(min|k|) (bf16 value = M * 2^(E-134)), so if
 //     sum|p| < 2^(L+53) every partial sum, in any order, is representable and
 //     the fp64 result is the exact sum: rounding it once is the answer, ties
-//     included.  The kernel tracks min|k| and sum|p| per entry (two extra VALU
-//     ops per element).  When that proof fails it falls back to an interval
+//     included.  The kernel tracks sum|p| (one extra fp64 FMA per element) and
+//     the smallest exponent field of k (a packed 16-bit minimum per two
+//     elements) per entry.  When that proof fails it falls back to an interval
 //     certificate (error <= gamma_(K-1) sum|p| for any order; both ends of
 //     [s - bound, s + bound] must round to the same fp32), and when both fail
 //     (a tie together with a > 53-bit exponent spread) the entry is recomputed
@@ -39,7 +40,17 @@ namespace csa2 {
 constexpr int kScoreThreads = 256;
 constexpr int kScoreRounds = 8;                                   // rounds of 8 entries per wave
 constexpr int kScoreEntriesPerWave = 8 * kScoreRounds;            // 64
-constexpr int kScoreEntriesPerBlock = 4 * kScoreEntriesPerWave;   // 256
+constexpr int kScoreEntriesPerChunk = 4 * kScoreEntriesPerWave;   // 256 per pass of the workgroup
+constexpr int kScoreChunks = 1;                                   // passes per workgroup
+constexpr int kScoreEntriesPerBlock = kScoreChunks * kScoreEntriesPerChunk;  // 256
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Per-half minimum of two packed 16-bit fields.
+CSA2_DEV uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
 
 CSA2_DEV int64_t row_valid(const ScoreArgs& a, int64_t r) {
     if (!a.nvb) return a.N;
@@ -201,88 +212,93 @@ __global__ __launch_bounds__(kScoreThreads) void score_exact_kernel(ScoreArgs a)
     }
 
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.ik) + b * a.N_cap * (int64_t)EB;
-    const int64_t e_wave = e_block + wave * kScoreEntriesPerWave;
+    if (with_hist) __syncthreads();  // histogram zeroed before any chunk adds to it
 
-    double keep = 0.0, keep_abs = 0.0;
-    float keep_min = 0.0f;
+    for (int chunk = 0; chunk < kScoreChunks; ++chunk) {
+        const int64_t e_wave = e_block + chunk * kScoreEntriesPerChunk + wave * kScoreEntriesPerWave;
+        if (e_wave >= nv) break;  // wave-uniform
+        double keep = 0.0, keep_abs = 0.0;
+        uint32_t keep_ex = 0;
 #pragma unroll 2
-    for (int t = 0; t < kScoreRounds; ++t) {
-        const int64_t e = e_wave + t * 8 + g;
-        u32x4 w[CPL];
-        if (e < nv) {
-            const uint8_t* src = kbase + e * EB + sub * 16;
+        for (int t = 0; t < kScoreRounds; ++t) {
+            const int64_t e = e_wave + t * 8 + g;
+            u32x4 w[CPL];
+            if (e < nv) {
+                const uint8_t* src = kbase + e * EB + sub * 16;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
-        } else {
+                for (int c = 0; c < CPL; ++c)
+                    w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
+            } else {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) w[c] = u32x4{0u, 0u, 0u, 0u};
-        }
-        double acc = 0.0, aacc = 0.0;
-        float kmin = INFINITY;
+                for (int c = 0; c < CPL; ++c) w[c] = u32x4{0u, 0u, 0u, 0u};
+            }
+            double acc = 0.0, aacc = 0.0;
+            uint32_t kex = 0x7fff7fffu;  // packed minimum of the two bf16 exponent fields
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
+            for (int c = 0; c < CPL; ++c) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (DT == 0) {
-                    const float lof = bf16_lo(w[c][u]), hif = bf16_hi(w[c][u]);
-                    const double lo = lof, hi = hif;
-                    const double q0 = qd[c * EPC + 2 * u], q1 = qd[c * EPC + 2 * u + 1];
-                    acc = fma(q0, lo, acc);
-                    aacc = fma(fabs(q0), fabs(lo), aacc);
-                    acc = fma(q1, hi, acc);
-                    aacc = fma(fabs(q1), fabs(hi), aacc);
-                    kmin = fminf(kmin, fminf(fabsf(lof), fabsf(hif)));
-                } else {
-                    const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[c][u], false);
-                    const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[c][u], true);
-                    acc = fma(qd[c * EPC + 4 * u + 0], (double)p0[0], acc);
-                    acc = fma(qd[c * EPC + 4 * u + 1], (double)p0[1], acc);
-                    acc = fma(qd[c * EPC + 4 * u + 2], (double)p1[0], acc);
-                    acc = fma(qd[c * EPC + 4 * u + 3], (double)p1[1], acc);
+                for (int u = 0; u < 4; ++u) {
+                    if (DT == 0) {
+                        const double lo = bf16_lo(w[c][u]), hi = bf16_hi(w[c][u]);
+                        const double q0 = qd[c * EPC + 2 * u], q1 = qd[c * EPC + 2 * u + 1];
+                        acc = fma(q0, lo, acc);
+                        aacc = fma(fabs(q0), fabs(lo), aacc);
+                        acc = fma(q1, hi, acc);
+                        aacc = fma(fabs(q1), fabs(hi), aacc);
+                        kex = pk_min_u16(kex, w[c][u] & 0x7f807f80u);
+                    } else {
+                        const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[c][u], false);
+                        const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[c][u], true);
+                        acc = fma(qd[c * EPC + 4 * u + 0], (double)p0[0], acc);
+                        acc = fma(qd[c * EPC + 4 * u + 1], (double)p0[1], acc);
+                        acc = fma(qd[c * EPC + 4 * u + 2], (double)p1[0], acc);
+                        acc = fma(qd[c * EPC + 4 * u + 3], (double)p1[1], acc);
+                    }
                 }
             }
-        }
-        acc += swz_xor<1>(acc);
-        acc += swz_xor<2>(acc);
-        acc += swz_xor<4>(acc);
-        if (DT == 0) {
-            aacc += swz_xor<1>(aacc);
-            aacc += swz_xor<2>(aacc);
-            aacc += swz_xor<4>(aacc);
-            kmin = fminf(kmin, swz_xor<1>(kmin));
-            kmin = fminf(kmin, swz_xor<2>(kmin));
-            kmin = fminf(kmin, swz_xor<4>(kmin));
-        }
-        if (sub == t) {
-            keep = acc;
-            keep_abs = aacc;
-            keep_min = kmin;
-        }
-    }
-
-    // lane (g, sub) now owns entry e_wave + 8*sub + g
-    const int64_t e = e_wave + 8 * sub + g;
-    if (with_hist) __syncthreads();
-    if (e < nv) {
-        float res;
-        bool ok = true;
-        if (DT == 0) {
-            res = (float)keep;
-            if (!sum_is_exact(keep_abs, lq + bf16_lsb_exp(keep_min))) {
-                const double eb = bound_scale * keep_abs + fabs(keep) * 0x1p-52;
-                const float lo = (float)(keep - eb), hi = (float)(keep + eb);
-                ok = __float_as_uint(lo) == __float_as_uint(hi);
-                res = lo;
+            acc += swz_xor<1>(acc);
+            acc += swz_xor<2>(acc);
+            acc += swz_xor<4>(acc);
+            if (DT == 0) {
+                aacc += swz_xor<1>(aacc);
+                aacc += swz_xor<2>(aacc);
+                aacc += swz_xor<4>(aacc);
+                kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (1 << 10) | 0x1f));
+                kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (2 << 10) | 0x1f));
+                kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (4 << 10) | 0x1f));
             }
-        } else {
-            res = (float)keep;
+            if (sub == t) {
+                keep = acc;
+                keep_abs = aacc;
+                keep_ex = kex;
+            }
         }
-        if (!ok)
-            res = exact_bf16_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * a.K,
-                                 reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + e) * a.K, a.K);
-        a.scores[r * a.ld + e] = res;
-        if (with_hist) atomicAdd(&lhist[sort_key(res) >> (32 - kHistBits)], 1u);
+
+        // lane (g, sub) now owns entry e_wave + 8*sub + g
+        const int64_t e = e_wave + 8 * sub + g;
+        if (e < nv) {
+            float res;
+            bool ok = true;
+            if (DT == 0) {
+                res = (float)keep;
+                // smallest exponent field among the entry's elements (0 = zero or subnormal)
+                const uint32_t ex = min(keep_ex & 0xffffu, keep_ex >> 16) >> 7;
+                const int lk = (int)(ex > 0 ? ex : 1u) - 134;
+                if (!sum_is_exact(keep_abs, lq + lk)) {
+                    const double eb = bound_scale * keep_abs + fabs(keep) * 0x1p-52;
+                    const float lo = (float)(keep - eb), hi = (float)(keep + eb);
+                    ok = __float_as_uint(lo) == __float_as_uint(hi);
+                    res = lo;
+                }
+            } else {
+                res = (float)keep;
+            }
+            if (!ok)
+                res = exact_bf16_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * a.K,
+                                     reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + e) * a.K, a.K);
+            a.scores[r * a.ld + e] = res;
+            if (with_hist) atomicAdd(&lhist[sort_key(res) >> (32 - kHistBits)], 1u);
+        }
     }
     if (with_hist) {
         __syncthreads();
