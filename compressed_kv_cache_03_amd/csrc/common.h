@@ -81,4 +81,39 @@ CSA2_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds, uint32_t* tota
     return excl;
 }
 
+// Find, within a histogram of `nbins` bins (highest bin = largest keys), the
+// bin holding the `need`-th largest element: the largest b with
+// sum_{b' >= b} h[b'] >= need.  Writes b and the count strictly above b to
+// out[0], out[1].  need >= 1 and sum h >= need are required.  All threads of
+// the block must call it; h may live in global or shared memory.
+template <int THREADS>
+CSA2_DEV void find_digit(const uint32_t* h, int nbins, uint32_t need, uint32_t* scan_lds,
+                         uint32_t* out) {
+    if (threadIdx.x == 0) {
+        out[0] = 0;
+        out[1] = 0;
+    }
+    const int per = (nbins + THREADS - 1) / THREADS;
+    // thread t owns bins [nbins - per*(t+1), nbins - per*t), i.e. thread 0 the top
+    const int hi = nbins - per * (int)threadIdx.x;
+    const int lo = hi - per;
+    uint32_t local = 0;
+    for (int bin = hi - 1; bin >= lo && bin >= 0; --bin) local += h[bin];
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan(local, scan_lds, &total);
+    if (before < need && before + local >= need) {
+        uint32_t run = before;
+        for (int bin = hi - 1; bin >= lo && bin >= 0; --bin) {
+            const uint32_t c = h[bin];
+            if (run + c >= need) {
+                out[0] = (uint32_t)bin;
+                out[1] = run;
+                break;
+            }
+            run += c;
+        }
+    }
+    __syncthreads();
+}
+
 }  // namespace csa2

@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -31,9 +32,21 @@ struct Layout {
     size_t scores = 0;                   // [R][N] f32
     size_t cand_idx = 0, cand_key = 0;   // [R][N]
     size_t slice_cnt = 0;                // [R][slices]
+    // prefill selection on MFMA (e4m3 index keys, Qs > 1)
+    size_t samp = 0, theta = 0, cand = 0, cand_cnt = 0, flag = 0, flag_count = 0, knorm = 0;
+    int cap = 0, nblk = 0;
     size_t part = 0;                     // attention partials
     size_t total = 0;
 };
+
+constexpr int64_t kSampleCols = 2048;  // threshold samples per prefill row
+
+// Prefill chunks with e4m3 keys select through the MFMA candidate path.
+bool mfma_prefill(const csa2_group* g, int Qs) {
+    const int K = g->H_I * g->d_I;
+    return Qs > 1 && g->idx_dtype == CSA2_IDX_FP8_E4M3 && (K == 128 || K == 256) &&
+           g->k <= band_max_k();
+}
 
 struct TopkShape {
     int64_t R, N, slices;
@@ -63,7 +76,26 @@ Layout layer_layout(const csa2_group* g, int Qs, int Hq, int W) {
     size_t off = 0;
     L.scores = off;
     off = align_up(off + (size_t)R * N * 4);
-    add_topk(L, off, TopkShape{R, N, (N + topk_slice_len(N) - 1) / topk_slice_len(N)});
+    if (mfma_prefill(g, Qs)) {
+        L.cap = (int)std::min<int64_t>(band_cap(g->k), N);
+        L.nblk = (int)((N + 255) / 256);
+        L.samp = off;
+        off = align_up(off + (size_t)R * std::min<int64_t>(N, kSampleCols) * 4);
+        L.theta = off;
+        off = align_up(off + (size_t)R * 4);
+        L.cand_cnt = off;
+        off = align_up(off + (size_t)R * 4);
+        L.flag = off;
+        off = align_up(off + (size_t)R * 4);
+        L.flag_count = off;
+        off = align_up(off + 4);
+        L.knorm = off;
+        off = align_up(off + (size_t)g->B * L.nblk * 4);
+        L.cand = off;
+        off = align_up(off + (size_t)R * L.cap * 8);
+    } else {
+        add_topk(L, off, TopkShape{R, N, (N + topk_slice_len(N) - 1) / topk_slice_len(N)});
+    }
     L.part = off;
     off = align_up(off + attend_part_bytes(R, Hq, g->D, g->k, W));
     L.total = off;
@@ -296,7 +328,65 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
             e = launch_store_rows(a->new_ikey, R, K * idx_elem_bytes(g->idx_dtype), g->ikeys,
                                   g->n_valid, Qs, g->N_cap, s);
     }
-    if (e == hipSuccess && selects) {
+    if (e == hipSuccess && selects && mfma_prefill(g, Qs)) {
+        // S2 + S3 for a prefill chunk: sampled thresholds, MFMA score GEMM with a
+        // candidate filter, exact selection (index_gemm.hip)
+        const int64_t N = g->n_valid_max;
+        const int64_t stride = (N + kSampleCols - 1) / kSampleCols;
+        GemmArgs ga{};
+        ga.iq = static_cast<const uint8_t*>(a->iq);
+        ga.ik = static_cast<const uint8_t*>(g->ikeys);
+        ga.K = K;
+        ga.B = g->B;
+        ga.Qs = Qs;
+        ga.N = N;
+        ga.N_cap = g->N_cap;
+        ga.nvb = g->n_valid;
+        ga.stride = stride;
+        ga.ncols = (N + stride - 1) / stride;
+        ga.nsub = 1;
+        ga.out = at<float>(ws, L.samp);
+        BandArgs ba{};
+        ba.B = g->B;
+        ba.Qs = Qs;
+        ba.K = K;
+        ba.k = g->k;
+        ba.N = N;
+        ba.N_cap = g->N_cap;
+        ba.nvb = g->n_valid;
+        ba.iq = ga.iq;
+        ba.ik = ga.ik;
+        ba.stride = stride;
+        ba.ncols = ga.ncols;
+        ba.samp = ga.out;
+        ba.theta = at<float>(ws, L.theta);
+        ba.cand = at<uint2>(ws, L.cand);
+        ba.cand_cnt = at<uint32_t>(ws, L.cand_cnt);
+        ba.cap = L.cap;
+        ba.knorm = at<float>(ws, L.knorm);
+        ba.nblk = (int)((N + 255) / 256);
+        ba.idx = g->sel;
+        ba.flag = at<int32_t>(ws, L.flag);
+        ba.flag_count = at<uint32_t>(ws, L.flag_count);
+        ba.scores = at<float>(ws, L.scores);
+        ba.ld = g->N_cap;
+        e = launch_gemm_fp8(ga, 0, s);
+        if (e == hipSuccess) e = launch_key_norm(ga.ik, K, g->B, N, g->N_cap, ba.nblk, ba.knorm, s);
+        if (e == hipSuccess) e = launch_sample_select(ba, s);
+        if (e == hipSuccess) {
+            GemmArgs fa = ga;
+            fa.stride = 1;
+            fa.ncols = N;
+            fa.nsub = 8;
+            fa.out = nullptr;
+            fa.theta = ba.theta;
+            fa.cand = ba.cand ? const_cast<uint2*>(ba.cand) : nullptr;
+            fa.cand_cnt = ba.cand_cnt;
+            fa.cap = ba.cap;
+            e = launch_gemm_fp8(fa, 1, s);
+        }
+        if (e == hipSuccess) e = launch_band_final(ba, s);
+    } else if (e == hipSuccess && selects) {
         // S2 + S3: exact scores of the valid entries, digit histogram, selection
         TopkArgs t{};
         t.scores = at<float>(ws, L.scores);

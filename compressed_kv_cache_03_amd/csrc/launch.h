@@ -84,4 +84,54 @@ struct AttendArgs {
 void attend_splits(int64_t R, int Hq, int D, int k, int W, int* splits, int* chunk);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
 
+// S2+S3 for prefill chunks with e4m3 index keys (index_gemm.hip).
+struct GemmArgs {
+    const uint8_t* iq;     // [B][Qs][K] e4m3
+    const uint8_t* ik;     // [B][N_cap][K] e4m3
+    int K;                 // 128 or 256
+    int B, Qs;
+    int64_t N;             // entries considered per sequence (<= N_cap)
+    int64_t N_cap;
+    const int32_t* nvb;    // [B]: row i sees j < nvb[b] - Qs + i + 1 (or null: j < N)
+    int64_t stride;        // column c is entry c * stride
+    int64_t ncols;         // columns per sequence
+    int nsub;              // 128-column tiles per workgroup (1 when storing)
+    // filled by launch_gemm_fp8
+    int n_rowblk;
+    int64_t n_colblk, tiles, per_xcd;
+    float* out;            // mode 0: [B*Qs][ncols] scores (-inf where not visible)
+    const float* theta;    // mode 1: [B*Qs] thresholds
+    uint2* cand;           // mode 1: [B*Qs][cap] (key with 8 low bits cleared, entry)
+    uint32_t* cand_cnt;    // mode 1: [B*Qs] (zeroed beforehand)
+    int cap;
+};
+hipError_t launch_gemm_fp8(GemmArgs a, int mode, hipStream_t stream);
+
+struct BandArgs {
+    int B, Qs, K, k;
+    int64_t N, N_cap;
+    const int32_t* nvb;
+    const uint8_t* iq;
+    const uint8_t* ik;
+    int64_t stride, ncols;
+    const float* samp;     // [B*Qs][ncols]
+    float* theta;          // [B*Qs]
+    const uint2* cand;
+    uint32_t* cand_cnt;
+    int cap;
+    float* knorm;          // [B][nblk] bounds on max ||k||^2 per 256 entries
+    int nblk;
+    int32_t* idx;          // [B*Qs][k] selection
+    int32_t* flag;         // [B*Qs] rows recomputed exactly
+    uint32_t* flag_count;
+    float* scores;         // [B*Qs][ld] exact scores of flagged rows
+    int64_t ld;
+};
+hipError_t launch_sample_select(const BandArgs& a, hipStream_t stream);
+hipError_t launch_key_norm(const uint8_t* ik, int K, int B, int64_t N, int64_t N_cap, int nblk, float* out,
+                           hipStream_t stream);
+hipError_t launch_band_final(const BandArgs& a, hipStream_t stream);
+int band_cap(int k);    // candidate list length per row
+int band_max_k();       // largest k the candidate path handles
+
 }  // namespace csa2

@@ -195,9 +195,15 @@ def test_attend_parity(B, Qs, Hq, D, W, k, wlen):
 class Run:
     """One workload run through both sides, layer by layer."""
 
-    def __init__(self, wl, n_valid=None):
+    def __init__(self, wl, n_valid=None, ikeys=None, iq=None):
         self.wl = wl
         self.inp = make_inputs(wl, n_valid=n_valid)
+        if ikeys is not None:  # replace every group's index keys (same shape and dtype)
+            self.inp.ikeys = [ikeys(g, k) for g, k in enumerate(self.inp.ikeys)]
+        if iq is not None:
+            for L in self.inp.layers:
+                if L["iq"] is not None:
+                    L["iq"] = iq(L["iq"])
         B, N, D, H, d = wl.B, wl.N, wl.D, wl.H_I, wl.d_I
         self.g_gpu, self.g_orc = [], []
         for g in range(wl.groups):
@@ -254,6 +260,37 @@ def test_w3_scaled_fp8():
 
 def test_prefill_w4_scaled():
     Run(W4.scaled(N=6000, Qs=96, k=512)).check_all()
+
+
+# Prefill chunks with e4m3 index keys select through the MFMA candidate path
+# (sampled threshold, filtered score GEMM, exact band) or its exact row fallback.
+def test_prefill_mfma_large_k_ragged():
+    Run(W4.scaled(B=2, N=40000, Qs=300, k=2048), n_valid=[40000, 23456]).check_all()
+
+
+def test_prefill_mfma_k128_every_entry_a_candidate():
+    # k close to the visible count: the threshold admits every entry
+    Run(W4.scaled(N=3000, Qs=64, k=2048, H_I=1, d_I=128)).check_all()
+
+
+def _e4m3_small_ints(a, seed):
+    # keys and queries in {-1, 0, +1}: integer scores with many exact ties
+    rng = np.random.default_rng(seed)
+    vals = np.array([0xB8, 0x00, 0x38], np.uint8)  # -1, 0, +1 in e4m3
+    return vals[rng.integers(0, 3, a.shape)]
+
+
+def test_prefill_mfma_exact_ties_take_lower_index():
+    Run(W4.scaled(N=20000, Qs=128, k=512),
+        ikeys=lambda g, k: _e4m3_small_ints(k, 7 + g),
+        iq=lambda q: _e4m3_small_ints(q, 99)).check_all()
+
+
+def test_prefill_mfma_all_equal_scores_fall_back():
+    # identical keys: every score ties, the candidate list overflows, and every
+    # row is recomputed by the exact row kernel
+    Run(W4.scaled(N=20000, Qs=32, k=512),
+        ikeys=lambda g, k: np.full_like(k, 0x38)).check_all()
 
 
 def test_stack_w5_scaled():
