@@ -35,13 +35,15 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGThreads = 256;     // 4 waves
-constexpr int kGRows = 256;        // query rows per workgroup, 64 per wave
+constexpr int kGQG = 2;            // 16-row query groups per wave
+constexpr int kGRows = 4 * 16 * kGQG;  // query rows per workgroup (128)
 constexpr int kGCols = 128;        // entries per staged tile
-constexpr int kGSlots = 32;        // candidates staged per row between flushes
+constexpr int kGSlots = 16;        // candidates per (row, lane group) list between flushes
 constexpr int kGFlushTiles = 2;    // tiles per flush: 256 columns, 8-bit offsets
 constexpr int kBandThreads = 1024;
-constexpr int kBandCap = 12288;    // candidates the final kernel holds in LDS
-constexpr int kBandMaxValid = 1 << 18;  // rows up to this many entries use the LDS bitmap
+constexpr int kBandCap = 8192;     // candidates the final kernel holds in LDS
+constexpr int kBandMaxValid = 1 << 18;  // rows up to this many entries (LDS bitmap)
+constexpr int kBandList = 2048;    // band entries resolved in LDS
 
 CSA2_DEV f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
     // e4m3 x e4m3 with E8M0 scales 127 = 2^0
@@ -67,13 +69,23 @@ CSA2_DEV int64_t gemm_row_valid(const GemmArgs& a, int b, int64_t qrow) {
 // MODE 1 appends candidates s^ >= theta[row].  Workgroups map to tiles so that
 // the workgroups an XCD runs together share one column block (and its keys in
 // that XCD's L2): tile t = (w % 8) * per_xcd + w / 8, row block fastest.
+//
+// The MFMA computes S^T = K Q^T (A = 16 staged entries, B = 16 query rows held
+// in registers), so lane (n, g) owns query row qg*16 + n of each of its row
+// groups and entries 4g + i of each 16-entry group.  In MODE 1 a passing score
+// goes to the lane's own LDS list for (row, g), with the count in a register:
+// the float bits with the low 8 mantissa bits replaced by the column offset in
+// the 256-column flush window (|change| < 2^-15 |s^|).  The flush adds one
+// global atomic per row per window.  A list that overflows (far rarer than one
+// row per call) marks its row for the exact recomputation.
 template <int KB, int MODE>
 __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(GemmArgs a) {
     constexpr int RB = KB * 128;    // bytes per row
     constexpr int PITCH = RB + 16;  // staged entry pitch, bytes
+    constexpr int LIST = kGSlots + 1;  // the last slot of a list takes overflow writes
     __shared__ __attribute__((aligned(16))) uint8_t btile[kGCols * PITCH];
-    __shared__ uint32_t stage[MODE ? kGRows * kGSlots : 1];
-    __shared__ uint32_t scnt[MODE ? kGRows : 1];
+    __shared__ uint32_t stage[MODE ? kGRows * 4 * LIST : 1];  // [row][g][slot]
+    __shared__ uint32_t scnt[MODE ? kGRows * 4 : 1];          // [row][g] at a flush
 
     const int64_t w = blockIdx.x;
     const int64_t t = (w & 7) * a.per_xcd + (w >> 3);
@@ -87,38 +99,31 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(GemmArgs a) {
     const int n = lane & 15, g = lane >> 4;
     const int64_t row0 = (int64_t)rb * kGRows;
     const int64_t col0 = cb * a.nsub * kGCols;
-    // entries visible to some row of the block (rows see more as they advance)
+    // entries visible to the last and to the first row of the block
     const int64_t nv_blk = gemm_row_valid(a, b, min(row0 + kGRows, (int64_t)a.Qs) - 1);
+    const int64_t nv_first = gemm_row_valid(a, b, row0);
     if (col0 >= a.ncols || col0 * a.stride >= nv_blk) return;
 
-    if (MODE) {
-        scnt[tid] = 0;
-    }
-    // A fragments (rows row0 + wave*64 + rg*16 + n, bytes kb*128 + 32g ..+32)
-    i32x8 af[4][KB];
+    // query fragments: row wave*(16*kGQG) + qg*16 + n, bytes kb*128 + 32g .. +32
+    i32x8 qf[kGQG][KB];
+    int32_t nvr[kGQG];
+    float th[kGQG];
+    uint32_t cnt[kGQG];
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-        const int64_t qrow = row0 + wave * 64 + rg * 16 + n;
+    for (int qg = 0; qg < kGQG; ++qg) {
+        const int64_t qrow = row0 + wave * 16 * kGQG + qg * 16 + n;
         const bool ok = qrow < a.Qs;
         const uint8_t* src = a.iq + ((int64_t)b * a.Qs + (ok ? qrow : 0)) * RB + 32 * g;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const u32x4 lo = *reinterpret_cast<const u32x4*>(src + kb * 128);
             const u32x4 hi = *reinterpret_cast<const u32x4*>(src + kb * 128 + 16);
-            af[rg][kb] = ok ? join(lo, hi) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            qf[qg][kb] = ok ? join(lo, hi) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
+        nvr[qg] = (int32_t)gemm_row_valid(a, b, qrow);
+        th[qg] = (MODE && ok) ? a.theta[(int64_t)b * a.Qs + qrow] : INFINITY;
+        cnt[qg] = 0;
     }
-    // rows of this lane's accumulators: row0 + wave*64 + rg*16 + 4g + i
-    int32_t nvr[4][4];
-    float th[4][4];
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t qr = row0 + wave * 64 + rg * 16 + 4 * g + i;
-            nvr[rg][i] = (int32_t)gemm_row_valid(a, b, qr);
-            th[rg][i] = (MODE && qr < a.Qs) ? a.theta[(int64_t)b * a.Qs + qr] : INFINITY;
-        }
 
     const int ntiles = MODE ? a.nsub : 1;
     for (int sub = 0; sub < ntiles; ++sub) {
@@ -140,39 +145,63 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(GemmArgs a) {
         __syncthreads();
         // the window of the current flush starts at column fc0
         const int64_t fc0 = col0 + (int64_t)(sub - sub % kGFlushTiles) * kGCols;
+        // every column of the tile visible to every row of the block: no per-score test
+        const bool all_visible = (tc0 + kGCols) <= a.ncols && (tc0 + kGCols - 1) * a.stride < nv_first;
+        if (MODE == 1 && all_visible) {
+#pragma unroll 2
+            for (int eg = 0; eg < kGCols / 16; ++eg) {
+                i32x8 kf[KB];
+                const uint8_t* ks = btile + (eg * 16 + n) * PITCH + 32 * g;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    kf[kb] = join(*reinterpret_cast<const u32x4*>(ks + kb * 128),
+                                  *reinterpret_cast<const u32x4*>(ks + kb * 128 + 16));
+                const uint32_t off = (uint32_t)(tc0 - fc0) + eg * 16 + 4 * g;  // column offset in the window
+#pragma unroll
+                for (int qg = 0; qg < kGQG; ++qg) {
+                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) acc = mfma_fp8(kf[kb], qf[qg][kb], acc);
+                    uint32_t* list = stage + ((wave * 16 * kGQG + qg * 16 + n) * 4 + g) * LIST;
+                    // branch-free: a score that does not pass is written to the trash slot
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool p = acc[i] >= th[qg];
+                        list[p ? min(cnt[qg], (uint32_t)kGSlots) : (uint32_t)kGSlots] =
+                            (__float_as_uint(acc[i]) & 0xffffff00u) | (off + i);
+                        cnt[qg] += p ? 1u : 0u;
+                    }
+                }
+            }
+        } else {
 #pragma unroll 1
-        for (int eg = 0; eg < kGCols / 16; ++eg) {
-            i32x8 bf[KB];
-            const uint8_t* bs = btile + (eg * 16 + n) * PITCH + 32 * g;
+            for (int eg = 0; eg < kGCols / 16; ++eg) {
+                i32x8 kf[KB];
+                const uint8_t* ks = btile + (eg * 16 + n) * PITCH + 32 * g;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                bf[kb] = join(*reinterpret_cast<const u32x4*>(bs + kb * 128),
-                              *reinterpret_cast<const u32x4*>(bs + kb * 128 + 16));
-            const int64_t col = tc0 + eg * 16 + n;
-            const int64_t j = col * a.stride;
-            const bool colok = col < a.ncols;
+                for (int kb = 0; kb < KB; ++kb)
+                    kf[kb] = join(*reinterpret_cast<const u32x4*>(ks + kb * 128),
+                                  *reinterpret_cast<const u32x4*>(ks + kb * 128 + 16));
+                const int64_t cbase = tc0 + eg * 16 + 4 * g;  // this lane's first column
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int qg = 0; qg < kGQG; ++qg) {
+                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) acc = mfma_fp8(af[rg][kb], bf[kb], acc);
+                    for (int kb = 0; kb < KB; ++kb) acc = mfma_fp8(kf[kb], qf[qg][kb], acc);
+                    const int lr = wave * 16 * kGQG + qg * 16 + n;
+                    uint32_t* list = stage + (lr * 4 + g) * LIST;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool valid = colok && j < nvr[rg][i];
-                    const int lr = wave * 64 + rg * 16 + 4 * g + i;
-                    const int64_t qr = row0 + lr;
-                    if (MODE == 0) {
-                        if (colok && qr < a.Qs)
-                            a.out[((int64_t)b * a.Qs + qr) * a.ncols + col] = valid ? acc[i] : -INFINITY;
-                    } else if (valid && acc[i] >= th[rg][i]) {
-                        const uint32_t key = sort_key(acc[i]) & 0xffffff00u;
-                        const uint32_t slot = atomicAdd(&scnt[lr], 1u);
-                        if (slot < (uint32_t)kGSlots) {
-                            stage[lr * kGSlots + slot] = key | (uint32_t)(col - fc0);
-                        } else {  // staging full: append directly
-                            const int64_t r = (int64_t)b * a.Qs + qr;
-                            const uint32_t pos = atomicAdd(&a.cand_cnt[r], 1u);
-                            if (pos < (uint32_t)a.cap) a.cand[r * a.cap + pos] = make_uint2(key, (uint32_t)j);
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t col = cbase + i;
+                        const bool valid = col < a.ncols && col * a.stride < nvr[qg];
+                        if (MODE == 0) {
+                            const int64_t qr = row0 + lr;
+                            if (col < a.ncols && qr < a.Qs)
+                                a.out[((int64_t)b * a.Qs + qr) * a.ncols + col] = valid ? acc[i] : -INFINITY;
+                        } else if (valid && acc[i] >= th[qg]) {
+                            list[min(cnt[qg], (uint32_t)kGSlots)] =
+                                (__float_as_uint(acc[i]) & 0xffffff00u) | (uint32_t)(col - fc0);
+                            ++cnt[qg];
                         }
                     }
                 }
@@ -182,21 +211,39 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(GemmArgs a) {
             const bool last = sub + 1 == ntiles || tc0 + kGCols >= a.ncols ||
                               (tc0 + kGCols) * a.stride >= nv_blk;
             if (last || sub % kGFlushTiles == kGFlushTiles - 1) {
+#pragma unroll
+                for (int qg = 0; qg < kGQG; ++qg) {
+                    scnt[(wave * 16 * kGQG + qg * 16 + n) * 4 + g] = cnt[qg];
+                    cnt[qg] = 0;
+                }
                 __syncthreads();
-                const int64_t qr = row0 + tid;
-                const uint32_t c = min(scnt[tid], (uint32_t)kGSlots);
-                if (c > 0 && qr < a.Qs) {
-                    const int64_t r = (int64_t)b * a.Qs + qr;
-                    const uint32_t base = atomicAdd(&a.cand_cnt[r], c);
-                    for (uint32_t s = 0; s < c; ++s) {
-                        const uint32_t pos = base + s;
-                        if (pos >= (uint32_t)a.cap) break;
-                        const uint32_t v = stage[tid * kGSlots + s];
-                        a.cand[r * a.cap + pos] =
-                            make_uint2(v & 0xffffff00u, (uint32_t)((fc0 + (v & 0xffu)) * a.stride));
+                if (tid < kGRows) {
+                    const int64_t qr = row0 + tid;
+                    uint32_t c4[4], tot = 0;
+                    bool over = false;
+#pragma unroll
+                    for (int gg = 0; gg < 4; ++gg) {
+                        c4[gg] = scnt[tid * 4 + gg];
+                        over |= c4[gg] > (uint32_t)kGSlots;
+                        tot += c4[gg];
+                    }
+                    if (qr < a.Qs && tot > 0) {
+                        const int64_t r = (int64_t)b * a.Qs + qr;
+                        if (over) {
+                            // candidates were lost: push the count past the list length so
+                            // that the final kernel recomputes the row exactly
+                            atomicAdd(&a.cand_cnt[r], (uint32_t)a.cap + 1u);
+                        } else {
+                            uint32_t pos = atomicAdd(&a.cand_cnt[r], tot);
+#pragma unroll
+                            for (int gg = 0; gg < 4; ++gg)
+                                for (uint32_t sl = 0; sl < c4[gg] && pos < (uint32_t)a.cap; ++sl, ++pos) {
+                                    const uint32_t v = stage[(tid * 4 + gg) * LIST + sl];
+                                    a.cand[r * a.cap + pos] = make_uint2(v, (uint32_t)(fc0 + (v & 0xffu)));
+                                }
+                        }
                     }
                 }
-                scnt[tid] = 0;
             }
         }
     }
@@ -222,30 +269,27 @@ hipError_t launch_gemm_fp8(GemmArgs a, int mode, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Radix select among LDS-resident keys: the `need`-th largest key T among the
-// positions p < C for which key_at(p, &k) returns true, and the count of such
-// keys strictly above T.  Digits 12 / 12 / 8 bits.  Block-wide; `hist` holds
-// 4096 words.  need >= 1 and at least `need` participating keys are required.
+// Radix select: the `need`-th largest key T among the positions p < C for
+// which key_at(p, &k) returns true, and the count of such keys strictly above
+// T.  Four 8-bit digits; block-wide; `hist` holds 256 words.  need >= 1 and at
+// least `need` participating keys are required.
 template <int THREADS, typename KeyAt>
 CSA2_DEV void block_radix_select(uint32_t C, uint32_t need, KeyAt key_at, uint32_t* hist,
                                  uint32_t* scan_lds, uint32_t* dig, uint32_t* T_out,
                                  uint32_t* above_out) {
     uint32_t prefix = 0, fixed = 0, above = 0;
-    const int shifts[3] = {20, 8, 0};
-    const int bits[3] = {12, 12, 8};
 #pragma unroll
-    for (int ps = 0; ps < 3; ++ps) {
-        const int nb = 1 << bits[ps];
-        for (int i = threadIdx.x; i < nb; i += THREADS) hist[i] = 0;
+    for (int sh = 24; sh >= 0; sh -= 8) {
+        for (int i = threadIdx.x; i < 256; i += THREADS) hist[i] = 0;
         __syncthreads();
         for (uint32_t p = threadIdx.x; p < C; p += THREADS) {
             uint32_t k;
-            if (key_at(p, &k) && (k & fixed) == prefix) atomicAdd(&hist[(k >> shifts[ps]) & (nb - 1)], 1u);
+            if (key_at(p, &k) && (k & fixed) == prefix) atomicAdd(&hist[(k >> sh) & 0xffu], 1u);
         }
         __syncthreads();
-        find_digit<THREADS>(hist, nb, need, scan_lds, dig);
-        prefix |= dig[0] << shifts[ps];
-        fixed |= (uint32_t)(nb - 1) << shifts[ps];
+        find_digit<THREADS>(hist, 256, need, scan_lds, dig);
+        prefix |= dig[0] << sh;
+        fixed |= 0xffu << sh;
         need -= dig[1];
         above += dig[1];
         __syncthreads();
@@ -255,8 +299,10 @@ CSA2_DEV void block_radix_select(uint32_t C, uint32_t need, KeyAt key_at, uint32
 }
 
 // Per row: zero the candidate counter and pick theta (see the top of the file).
+constexpr int kSampleMax = 2048;
 __global__ __launch_bounds__(256) void sample_select_kernel(BandArgs a) {
-    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t keys[kSampleMax];
+    __shared__ uint32_t hist[256];
     __shared__ uint32_t scan_lds[256 / 64 + 1];
     __shared__ uint32_t dig[2];
     const int64_t r = blockIdx.x;
@@ -274,7 +320,7 @@ __global__ __launch_bounds__(256) void sample_select_kernel(BandArgs a) {
         if (threadIdx.x == 0) a.theta[r] = INFINITY;
         return;
     }
-    const int64_t ns = min((nv + a.stride - 1) / a.stride, a.ncols);  // valid samples
+    const int64_t ns = min((nv + a.stride - 1) / a.stride, a.ncols);  // valid samples (<= 2048)
     const double kp = (double)keff * (double)ns / (double)nv;
     const int64_t rank = (int64_t)ceil(kp + 4.0 * sqrt(kp) + 8.0);
     if (rank > ns) {
@@ -282,10 +328,12 @@ __global__ __launch_bounds__(256) void sample_select_kernel(BandArgs a) {
         return;
     }
     const float* sv = a.samp + r * a.ncols;
+    for (int p = threadIdx.x; p < ns; p += 256) keys[p] = sort_key(sv[p]);
+    __syncthreads();
     uint32_t T, above;
     block_radix_select<256>((uint32_t)ns, (uint32_t)rank,
-                            [&](uint32_t p, uint32_t* k) { *k = sort_key(sv[p]); return true; }, hist,
-                            scan_lds, dig, &T, &above);
+                            [&](uint32_t p, uint32_t* k) { *k = keys[p]; return true; }, hist, scan_lds,
+                            dig, &T, &above);
     if (threadIdx.x == 0) a.theta[r] = key_to_float(T);
 }
 
@@ -331,9 +379,18 @@ CSA2_DEV float exact_score_fp8(const uint8_t* q, const uint8_t* k) {
     constexpr int RB = KB * 128;
     constexpr int PER = RB / 64;  // bytes per lane: 2 or 4
     const int lane = threadIdx.x & 63;
+    uint32_t qw, kw;
+    if constexpr (PER == 4) {
+        qw = reinterpret_cast<const uint32_t*>(q)[lane];
+        kw = reinterpret_cast<const uint32_t*>(k)[lane];
+    } else {
+        qw = reinterpret_cast<const uint16_t*>(q)[lane];
+        kw = reinterpret_cast<const uint16_t*>(k)[lane];
+    }
     double acc = 0.0;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc = fma(e4m3_to_f64(q[lane * PER + e]), e4m3_to_f64(k[lane * PER + e]), acc);
+    for (int e = 0; e < PER; ++e)
+        acc = fma(e4m3_to_f64((qw >> (8 * e)) & 0xffu), e4m3_to_f64((kw >> (8 * e)) & 0xffu), acc);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
     const float f = (float)acc;
@@ -341,18 +398,22 @@ CSA2_DEV float exact_score_fp8(const uint8_t* q, const uint8_t* k) {
 }
 
 // Per row: exact selection from the candidate list, or a fallback flag.
+// Candidates arrive as (float bits of s^ with the low 8 bits replaced, entry).
 template <int KB>
 __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
     constexpr int RB = KB * 128;
-    __shared__ uint32_t s_key[kBandCap];
-    __shared__ int32_t s_idx[kBandCap];
+    __shared__ uint32_t s_key[kBandCap];   // sort keys minus the smallest; later the output bitmap
+    __shared__ int32_t s_idx[kBandCap];    // entry index; bit 31 = selected
+    __shared__ uint32_t band[kBandList];   // positions of band entries
+    __shared__ uint32_t bkey[kBandList];   // their exact sort keys
+    __shared__ int32_t bidx[kBandList];    // and entries
     __shared__ uint32_t hist[kHistBins];
-    __shared__ uint32_t bitmap[kBandMaxValid / 32];
     __shared__ uint32_t scan_lds[kBandThreads / 64 + 1];
     __shared__ uint32_t dig[2];
-    __shared__ uint32_t cnt_in, cnt_band;
-    __shared__ double red_d[kBandThreads / 64];
-    __shared__ int bad;
+    __shared__ uint32_t red_u[kBandThreads / 64];
+    __shared__ double red_q[kBandThreads / 64];
+    __shared__ float red_k[kBandThreads / 64];
+    static_assert(kBandCap * 4 >= kBandMaxValid / 8, "the output bitmap overlays s_key");
 
     const int64_t r = blockIdx.x;
     const int b = (int)(r / a.Qs);
@@ -365,8 +426,7 @@ __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
     if (keff == 0) return;
 
     const uint32_t C = a.cand_cnt[r];
-    auto flag_row = [&]() {
-        // the exact row kernel recomputes this row
+    auto flag_row = [&]() {  // the exact row kernel recomputes this row
         if (threadIdx.x == 0) {
             a.flag[r] = 1;
             atomicAdd(a.flag_count, 1u);
@@ -376,11 +436,16 @@ __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
         flag_row();
         return;
     }
+    // keys relative to the smallest candidate key: they span few bits
     const uint2* cand = a.cand + r * a.cap;
+    uint32_t kmin = 0xffffffffu, kmax = 0;
     for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
-        const uint2 v = cand[p];
-        s_key[p] = v.x;
-        s_idx[p] = (int32_t)v.y;
+        const uint2 c = cand[p];
+        const uint32_t k = sort_key(__uint_as_float(c.x & 0xffffff00u));
+        s_key[p] = k;
+        s_idx[p] = (int32_t)c.y;
+        kmin = min(kmin, k);
+        kmax = max(kmax, k);
     }
     // ||q||^2 (exact in fp64) and the sequence's bound on max ||k||^2
     double q2 = 0.0;
@@ -390,28 +455,76 @@ __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
             const double v = e4m3_to_f64(q[e]);
             q2 = fma(v, v, q2);
         }
-        for (int o = 32; o >= 1; o >>= 1) q2 += __shfl_xor(q2, o);
-        if ((threadIdx.x & 63) == 0) red_d[threadIdx.x >> 6] = q2;
     }
     float k2 = 0.0f;
     for (int i = threadIdx.x; i < a.nblk; i += kBandThreads) k2 = fmaxf(k2, a.knorm[(int64_t)b * a.nblk + i]);
-    for (int o = 32; o >= 1; o >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, o));
-    __shared__ float red_k[kBandThreads / 64];
-    if ((threadIdx.x & 63) == 0) red_k[threadIdx.x >> 6] = k2;
+    for (int o = 32; o >= 1; o >>= 1) {
+        q2 += __shfl_xor(q2, o);
+        k2 = fmaxf(k2, __shfl_xor(k2, o));
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        red_q[threadIdx.x >> 6] = q2;
+        red_k[threadIdx.x >> 6] = k2;
+        red_u[threadIdx.x >> 6] = kmin;
+        scan_lds[threadIdx.x >> 6] = kmax;
+    }
     __syncthreads();
     double Q2 = 0.0;
     float K2 = 0.0f;
+    uint32_t K0 = 0xffffffffu, K1 = 0;
     for (int wv = 0; wv < kBandThreads / 64; ++wv) {
-        Q2 += red_d[wv];
+        Q2 += red_q[wv];
         K2 = fmaxf(K2, red_k[wv]);
+        K0 = min(K0, red_u[wv]);
+        K1 = max(K1, scan_lds[wv]);
     }
+    __syncthreads();
+    for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) s_key[p] -= K0;
 
-    // T^ = keff-th largest candidate key
-    uint32_t Tk, above;
-    block_radix_select<kBandThreads>(C, (uint32_t)keff,
-                                     [&](uint32_t p, uint32_t* k) { *k = s_key[p]; return true; }, hist,
-                                     scan_lds, dig, &Tk, &above);
-    const double That = key_to_float(Tk);
+    // T^: the keff-th largest key.  12-bit digits from the top of the used range;
+    // once the digit's bin holds few keys, they are ranked directly.
+    const int bits = 32 - __clz((int)(K1 - K0) | 1);
+    uint32_t prefix = 0, fixed = 0, need = (uint32_t)keff;
+    for (int sh = bits > 12 ? bits - 12 : 0;; sh = sh > 12 ? sh - 12 : 0) {
+        for (int i = threadIdx.x; i < kHistBins; i += kBandThreads) hist[i] = 0;
+        __syncthreads();
+        for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
+            const uint32_t k = s_key[p];
+            if ((k & fixed) == prefix) atomicAdd(&hist[(k >> sh) & 0xfffu], 1u);
+        }
+        __syncthreads();
+        find_digit<kBandThreads>(hist, kHistBins, need, scan_lds, dig);
+        const uint32_t inbin = hist[dig[0]];
+        prefix |= dig[0] << sh;
+        fixed |= 0xfffu << sh;
+        need -= dig[1];
+        if (sh == 0) break;
+        if (inbin <= (uint32_t)kBandList) {
+            // gather the bin's keys and find the need-th largest by counting
+            if (threadIdx.x == 0) dig[0] = 0;
+            __syncthreads();
+            for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
+                const uint32_t k = s_key[p];
+                if ((k & fixed) == prefix) bkey[atomicAdd(&dig[0], 1u)] = k;
+            }
+            __syncthreads();
+            for (uint32_t t = threadIdx.x; t < inbin; t += kBandThreads) {
+                const uint32_t kt = bkey[t];
+                uint32_t gt = 0, ge = 0;
+                for (uint32_t u = 0; u < inbin; ++u) {
+                    gt += bkey[u] > kt ? 1u : 0u;
+                    ge += bkey[u] >= kt ? 1u : 0u;
+                }
+                if (gt < need && need <= ge) dig[1] = kt;  // every writer writes the same key
+            }
+            __syncthreads();
+            prefix = dig[1];
+            break;
+        }
+    }
+    const double That = key_to_float(prefix + K0);
     // |approximation - s| <= delta: MFMA fp32 summation of K exact products with
     // unit roundoff 2^-23 per addition (covers truncation), doubled, by
     // Cauchy-Schwarz sum|p| <= ||q|| ||k||; plus the 2^-15 relative key truncation
@@ -425,80 +538,82 @@ __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
         flag_row();
         return;
     }
-    if (threadIdx.x == 0) {
-        cnt_in = 0;
-        cnt_band = 0;
-    }
-    for (int i = threadIdx.x; i < kBandMaxValid / 32; i += kBandThreads) bitmap[i] = 0;
-    __syncthreads();
-    // classify; band positions are collected at the front of hist (reused as a list)
-    uint32_t my_in = 0;
-    for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
-        const double v = key_to_float(s_key[p]);
-        if (v > hi) {
-            ++my_in;
-            const int32_t j = s_idx[p];
-            atomicOr(&bitmap[j >> 5], 1u << (j & 31));
-        } else if (v >= lo) {
-            const uint32_t slot = atomicAdd(&cnt_band, 1u);
-            if (slot < (uint32_t)kHistBins) hist[slot] = p;
-        }
-    }
-    atomicAdd(&cnt_in, my_in);
-    __syncthreads();
-    const uint32_t nband = cnt_band, nin = cnt_in;
-    if (nband > (uint32_t)kHistBins || nin > (uint32_t)keff) {
-        flag_row();
-        return;
-    }
-    const uint32_t need = (uint32_t)keff - nin;
-    if (need > nband) {  // the error bound did not hold
-        flag_row();
-        return;
-    }
-    // exact rescoring of the band, one wave per entry
+    // classify: above the band -> selected (bit 31); inside -> band list (block-scan compaction)
+    uint32_t nin_mine = 0;
     {
-        const int wv = threadIdx.x >> 6;
+        uint32_t inb[kBandCap / kBandThreads];
+        uint32_t nb_mine = 0;
+#pragma unroll
+        for (int u = 0; u < kBandCap / kBandThreads; ++u) {
+            const uint32_t p = threadIdx.x * (kBandCap / kBandThreads) + u;  // contiguous per thread
+            inb[u] = 0;
+            if (p < C) {
+                const double v = key_to_float(s_key[p] + K0);
+                if (v > hi) {
+                    ++nin_mine;
+                    s_idx[p] |= (int32_t)0x80000000;
+                } else if (v >= lo) {
+                    inb[u] = 1;
+                    ++nb_mine;
+                }
+            }
+        }
+        uint32_t nband_tot;
+        uint32_t pos = block_exclusive_scan(nb_mine, scan_lds, &nband_tot);
+#pragma unroll
+        for (int u = 0; u < kBandCap / kBandThreads; ++u)
+            if (inb[u]) {
+                if (pos < (uint32_t)kBandList) band[pos] = threadIdx.x * (kBandCap / kBandThreads) + u;
+                ++pos;
+            }
+        if (threadIdx.x == 0) dig[0] = nband_tot;
+    }
+    uint32_t nin;
+    block_exclusive_scan(nin_mine, scan_lds, &nin);
+    const uint32_t nband = dig[0];
+    if (nband > (uint32_t)kBandList || nin > (uint32_t)keff || (uint32_t)keff - nin > nband) {
+        flag_row();  // a very wide band, or the error bound did not hold
+        return;
+    }
+    const uint32_t need_b = (uint32_t)keff - nin;
+    if (need_b > 0) {
+        // exact rescoring of the band, one wave per entry
         const uint8_t* q = a.iq + r * RB;
-        for (uint32_t t = wv; t < nband; t += kBandThreads / 64) {
-            const uint32_t p = hist[t];
-            const float s = exact_score_fp8<KB>(q, a.ik + ((int64_t)b * a.N_cap + s_idx[p]) * RB);
-            if ((threadIdx.x & 63) == 0) s_key[p] = sort_key(s);
+        for (uint32_t t = threadIdx.x >> 6; t < nband; t += kBandThreads / 64) {
+            const int32_t j = s_idx[band[t]];
+            const float sc = exact_score_fp8<KB>(q, a.ik + ((int64_t)b * a.N_cap + j) * RB);
+            if ((threadIdx.x & 63) == 0) {
+                bkey[t] = sort_key(sc);
+                bidx[t] = j;
+            }
         }
-    }
-    __syncthreads();
-    if (need > 0) {
-        // move the band list out of hist (block_radix_select reuses hist)
-        __shared__ uint32_t band_pos[2048];
-        if (nband > 2048) {
-            flag_row();
-            return;
-        }
-        for (uint32_t t = threadIdx.x; t < nband; t += kBandThreads) band_pos[t] = hist[t];
         __syncthreads();
-        uint32_t Tb, above_b;
-        block_radix_select<kBandThreads>(nband, need,
-                                         [&](uint32_t t, uint32_t* k) { *k = s_key[band_pos[t]]; return true; },
-                                         hist, scan_lds, dig, &Tb, &above_b);
-        const uint32_t quota = need - above_b;  // band keys == Tb to take, lowest indices first
-        // among ties, the quota smallest indices: the quota-th largest of ~index
-        uint32_t Ti = 0, above_i = 0;
-        block_radix_select<kBandThreads>(nband, quota,
-                                         [&](uint32_t t, uint32_t* k) {
-                                             *k = ~(uint32_t)s_idx[band_pos[t]];
-                                             return s_key[band_pos[t]] == Tb;
-                                         },
-                                         hist, scan_lds, dig, &Ti, &above_i);
+        // rank in the band by (exact score desc, index asc); the first need_b are taken
         for (uint32_t t = threadIdx.x; t < nband; t += kBandThreads) {
-            const uint32_t p = band_pos[t];
-            const uint32_t k = s_key[p];
-            const int32_t j = s_idx[p];
-            if (k > Tb || (k == Tb && ~(uint32_t)j >= Ti)) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+            const uint32_t kt = bkey[t];
+            const int32_t jt = bidx[t];
+            uint32_t rank = 0;
+            for (uint32_t v = 0; v < nband; ++v) {
+                const uint32_t kv = bkey[v];
+                rank += (kv > kt || (kv == kt && bidx[v] < jt)) ? 1u : 0u;
+            }
+            if (rank < need_b) s_idx[band[t]] = jt | (int32_t)0x80000000;
         }
     }
     __syncthreads();
-    // ascending output from the bitmap
+    // ascending output from a bitmap of the selected entries (over s_key)
+    uint32_t* bitmap = s_key;
     const int nwords = (int)((nv + 31) / 32);
+    for (int i = threadIdx.x; i < nwords; i += kBandThreads) bitmap[i] = 0;
+    __syncthreads();
+    for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
+        const int32_t v = s_idx[p];
+        if (v < 0) {
+            const int32_t j = v & 0x7fffffff;
+            atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+        }
+    }
+    __syncthreads();
     const int per = (nwords + kBandThreads - 1) / kBandThreads;
     uint32_t mine = 0;
     for (int wi = threadIdx.x * per; wi < min(nwords, (int)(threadIdx.x + 1) * per); ++wi) mine += __popc(bitmap[wi]);
@@ -513,8 +628,7 @@ __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
         while (word) {
             const int bit = __ffs(word) - 1;
             word &= word - 1;
-            if (pos < (uint32_t)keff) out[pos] = wi * 32 + bit;
-            ++pos;
+            out[pos++] = wi * 32 + bit;
         }
     }
 }
@@ -597,7 +711,7 @@ hipError_t launch_band_final(const BandArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-int band_cap(int k) { return 4 * k + 4096 < kBandCap ? 4 * k + 4096 : kBandCap; }
-int band_max_k() { return (kBandCap - 4096) / 4; }
+int band_cap(int k) { return 3 * k + 2048 < kBandCap ? 3 * k + 2048 : kBandCap; }
+int band_max_k() { return (kBandCap - 2048) / 3; }
 
 }  // namespace csa2
