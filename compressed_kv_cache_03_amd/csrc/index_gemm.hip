@@ -34,9 +34,9 @@ namespace csa2 {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGThreads = 256;     // 4 waves
-constexpr int kGQG = 2;            // 16-row query groups per wave
-constexpr int kGRows = 4 * 16 * kGQG;  // query rows per workgroup (128)
+constexpr int kGThreads = 512;     // 8 waves
+constexpr int kGQG = 1;            // 16-row query groups per wave
+constexpr int kGRows = kGThreads / 64 * 16 * kGQG;  // query rows per workgroup (128)
 constexpr int kGCols = 128;        // entries per staged tile
 constexpr int kGSlots = 16;        // candidates per (row, lane group) list between flushes
 constexpr int kGFlushTiles = 2;    // tiles per flush: 256 columns, 8-bit offsets
@@ -126,22 +126,30 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(GemmArgs a) {
     }
 
     const int ntiles = MODE ? a.nsub : 1;
+    // key tiles are prefetched one tile ahead into registers: two threads per
+    // entry, out-of-range entries load entry 0 (masked in the epilogue)
+    constexpr int TPE = kGThreads / kGCols;  // threads per staged entry
+    constexpr int BPT = RB / TPE;            // bytes per thread
+    u32x4 pf[BPT / 16];
+    auto load_tile = [&](int64_t tc) {
+        const int64_t col = tc + tid / TPE;
+        int64_t j = col * a.stride;
+        if (col >= a.ncols || j >= a.N) j = 0;
+        const uint8_t* src = a.ik + ((int64_t)b * a.N_cap + j) * RB + (tid % TPE) * BPT;
+#pragma unroll
+        for (int q = 0; q < BPT / 16; ++q) pf[q] = *reinterpret_cast<const u32x4*>(src + 16 * q);
+    };
+    load_tile(col0);
     for (int sub = 0; sub < ntiles; ++sub) {
         const int64_t tc0 = col0 + (int64_t)sub * kGCols;  // first column of the tile
         if (tc0 >= a.ncols || tc0 * a.stride >= nv_blk) break;  // workgroup-uniform
         __syncthreads();  // previous tile consumed (and staging flushed)
         {
-            // two threads per entry; out-of-range entries load entry 0 (masked below)
-            const int c = tid >> 1, part = tid & 1;
-            const int64_t col = tc0 + c;
-            int64_t j = col * a.stride;
-            if (col >= a.ncols || j >= a.N) j = 0;
-            const uint8_t* src = a.ik + ((int64_t)b * a.N_cap + j) * RB + part * (RB / 2);
-            uint8_t* dst = btile + c * PITCH + part * (RB / 2);
+            uint8_t* dst = btile + (tid / TPE) * PITCH + (tid % TPE) * BPT;
 #pragma unroll
-            for (int q = 0; q < RB / 32; ++q)
-                *reinterpret_cast<u32x4*>(dst + 16 * q) = *reinterpret_cast<const u32x4*>(src + 16 * q);
+            for (int q = 0; q < BPT / 16; ++q) *reinterpret_cast<u32x4*>(dst + 16 * q) = pf[q];
         }
+        if (sub + 1 < ntiles) load_tile(tc0 + kGCols);
         __syncthreads();
         // the window of the current flush starts at column fc0
         const int64_t fc0 = col0 + (int64_t)(sub - sub % kGFlushTiles) * kGCols;
