@@ -23,6 +23,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wno-unused-command-line-argument"]
 
 
+# Per-file flags.  index_gemm.hip software-pipelines its MFMAs ahead of an
+# epilogue with branches; machine sinking would move them back below it.
+EXTRA = {"index_gemm.hip": ["-mllvm", "-disable-machine-sink"]}
+
+
 def _hipcc() -> str:
     for cand in ("/opt/rocm/bin/hipcc", "hipcc"):
         if os.path.isabs(cand) and os.path.exists(cand):
@@ -32,7 +37,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

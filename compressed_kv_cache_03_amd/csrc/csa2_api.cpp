@@ -34,6 +34,7 @@ struct Layout {
     size_t slice_cnt = 0;                // [R][slices]
     // prefill selection on MFMA (e4m3 index keys, Qs > 1)
     size_t samp = 0, theta = 0, cand = 0, cand_cnt = 0, flag = 0, flag_count = 0, knorm = 0;
+    size_t blk = 0, blkcnt = 0;
     int cap = 0, nblk = 0;
     size_t part = 0;                     // attention partials
     size_t total = 0;
@@ -93,6 +94,10 @@ Layout layer_layout(const csa2_group* g, int Qs, int Hq, int W) {
         off = align_up(off + (size_t)g->B * L.nblk * 4);
         L.cand = off;
         off = align_up(off + (size_t)R * L.cap * 8);
+        L.blkcnt = off;
+        off = align_up(off + (size_t)R * filter_colblks(N) * 4);
+        L.blk = off;
+        off = align_up(off + (size_t)R * filter_colblks(N) * filter_blk_cap() * 8);
     } else {
         add_topk(L, off, TopkShape{R, N, (N + topk_slice_len(N) - 1) / topk_slice_len(N)});
     }
@@ -344,7 +349,6 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         ga.nvb = g->n_valid;
         ga.stride = stride;
         ga.ncols = (N + stride - 1) / stride;
-        ga.nsub = 1;
         ga.out = at<float>(ws, L.samp);
         BandArgs ba{};
         ba.B = g->B;
@@ -360,6 +364,9 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         ba.ncols = ga.ncols;
         ba.samp = ga.out;
         ba.theta = at<float>(ws, L.theta);
+        ba.blk = at<uint2>(ws, L.blk);
+        ba.blkcnt = at<uint32_t>(ws, L.blkcnt);
+        ba.n_colblk = filter_colblks(N);
         ba.cand = at<uint2>(ws, L.cand);
         ba.cand_cnt = at<uint32_t>(ws, L.cand_cnt);
         ba.cap = L.cap;
@@ -377,10 +384,11 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
             GemmArgs fa = ga;
             fa.stride = 1;
             fa.ncols = N;
-            fa.nsub = 8;
             fa.out = nullptr;
             fa.theta = ba.theta;
-            fa.cand = ba.cand ? const_cast<uint2*>(ba.cand) : nullptr;
+            fa.blk = at<uint2>(ws, L.blk);
+            fa.blkcnt = at<uint32_t>(ws, L.blkcnt);
+            fa.cand = at<uint2>(ws, L.cand);
             fa.cand_cnt = ba.cand_cnt;
             fa.cap = ba.cap;
             e = launch_gemm_fp8(fa, 1, s);

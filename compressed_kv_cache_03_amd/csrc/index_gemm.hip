@@ -26,6 +26,8 @@
 //      The argument needs theta <= T^ - 2 delta and at least k candidates;
 //   4. any row where a check fails (too few or too many candidates, theta too
 //      high) is flagged and recomputed by an exact row kernel.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -34,16 +36,28 @@ namespace csa2 {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGThreads = 512;     // 8 waves
-constexpr int kGQG = 1;            // 16-row query groups per wave
-constexpr int kGRows = kGThreads / 64 * 16 * kGQG;  // query rows per workgroup (128)
-constexpr int kGCols = 128;        // entries per staged tile
-constexpr int kGSlots = 16;        // candidates per (row, lane group) list between flushes
-constexpr int kGFlushTiles = 2;    // tiles per flush: 256 columns, 8-bit offsets
+constexpr int kGCols = 128;         // entries per staged key tile
+// sample GEMM: 8 waves of 16 query rows, one key tile per workgroup
+constexpr int kSThreads = 512;
+constexpr int kSRows = kSThreads / 64 * 16;
+// filter GEMM: 4 waves of 64 query rows, 8 key tiles (a 1024-entry column block)
+constexpr int kFWaves = 4;
+constexpr int kFThreads = kFWaves * 64;
+constexpr int kFQG = 4;                          // 16-row query groups per wave
+constexpr int kFRows = kFWaves * 16 * kFQG;      // 256 query rows per workgroup
+constexpr int kFSub = 8;
+constexpr int kFBlkCols = kFSub * kGCols;        // 1024
+constexpr int kFList = 640;                      // quads in a wave's staging list
+constexpr int kFBlkCap = 64;                     // candidates per (row, column block) region
+static_assert(kFThreads == kFRows, "one thread per query row of the workgroup");
+static_assert(kFBlkCols / 16 <= 256 && kFQG * 64 <= 256, "tags fit 8 bits");
 constexpr int kBandThreads = 1024;
 constexpr int kBandCap = 8192;     // candidates the final kernel holds in LDS
 constexpr int kBandMaxValid = 1 << 18;  // rows up to this many entries (LDS bitmap)
-constexpr int kBandList = 2048;    // band entries resolved in LDS
+constexpr int kBandList = 1024;    // band entries resolved in LDS
+constexpr int kBandBits = 11;      // radix digit of the final selection
+constexpr int kBandHist = 1 << kBandBits;
+constexpr int kBandMaxBlk = kBandMaxValid / kFBlkCols;
 
 CSA2_DEV f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
     // e4m3 x e4m3 with E8M0 scales 127 = 2^0
@@ -65,53 +79,141 @@ CSA2_DEV int64_t gemm_row_valid(const GemmArgs& a, int b, int64_t qrow) {
     return v < 0 ? 0 : (v > a.N ? a.N : v);
 }
 
-// MODE 0 stores every score s^[row][col] (col = sample index, entry col*stride);
-// MODE 1 appends candidates s^ >= theta[row].  Workgroups map to tiles so that
-// the workgroups an XCD runs together share one column block (and its keys in
-// that XCD's L2): tile t = (w % 8) * per_xcd + w / 8, row block fastest.
-//
-// The MFMA computes S^T = K Q^T (A = 16 staged entries, B = 16 query rows held
-// in registers), so lane (n, g) owns query row qg*16 + n of each of its row
-// groups and entries 4g + i of each 16-entry group.  In MODE 1 a passing score
-// goes to the lane's own LDS list for (row, g), with the count in a register:
-// the float bits with the low 8 mantissa bits replaced by the column offset in
-// the 256-column flush window (|change| < 2^-15 |s^|).  The flush adds one
-// global atomic per row per window.  A list that overflows (far rarer than one
-// row per call) marks its row for the exact recomputation.
-template <int KB, int MODE>
-__global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(GemmArgs a) {
-    constexpr int RB = KB * 128;    // bytes per row
-    constexpr int PITCH = RB + 16;  // staged entry pitch, bytes
-    constexpr int LIST = kGSlots + 1;  // the last slot of a list takes overflow writes
-    __shared__ __attribute__((aligned(16))) uint8_t btile[kGCols * PITCH];
-    __shared__ uint32_t stage[MODE ? kGRows * 4 * LIST : 1];  // [row][g][slot]
-    __shared__ uint32_t scnt[MODE ? kGRows * 4 : 1];          // [row][g] at a flush
-
+// Workgroup w takes tile t = (w % 8) * per_xcd + w / 8 (row block fastest), so
+// the workgroups one XCD runs together share a column block and its keys in
+// that XCD's L2.
+struct GemmTile {
+    int rb, b;
+    int64_t cb;
+    bool ok;
+};
+CSA2_DEV GemmTile gemm_tile(const GemmArgs& a) {
     const int64_t w = blockIdx.x;
     const int64_t t = (w & 7) * a.per_xcd + (w >> 3);
-    if (t >= a.tiles) return;
-    const int rb = (int)(t % a.n_rowblk);
+    GemmTile r;
+    r.ok = t < a.tiles;
+    r.rb = (int)(t % a.n_rowblk);
     const int64_t rest = t / a.n_rowblk;
-    const int64_t cb = rest % a.n_colblk;
-    const int b = (int)(rest / a.n_colblk);
+    r.cb = rest % a.n_colblk;
+    r.b = (int)(rest / a.n_colblk);
+    return r;
+}
 
+// Sample scores: out[row][col] = s^(row, entry col*stride), -inf where the
+// entry is not visible to the row.  The MFMA computes S^T = K Q^T (A = 16
+// staged entries, B = 16 query rows in registers): lane (n, g) holds query
+// row n of its wave and entries 4g + i of each 16-entry group.
+template <int KB>
+__global__ __launch_bounds__(kSThreads) void sample_gemm_kernel(GemmArgs a) {
+    constexpr int RB = KB * 128;    // bytes per row
+    constexpr int PITCH = RB + 16;  // staged entry pitch, bytes
+    __shared__ __attribute__((aligned(16))) uint8_t btile[kGCols * PITCH];
+    const GemmTile tl = gemm_tile(a);
+    if (!tl.ok) return;
+    const int b = tl.b;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int64_t row0 = (int64_t)rb * kGRows;
-    const int64_t col0 = cb * a.nsub * kGCols;
-    // entries visible to the last and to the first row of the block
-    const int64_t nv_blk = gemm_row_valid(a, b, min(row0 + kGRows, (int64_t)a.Qs) - 1);
-    const int64_t nv_first = gemm_row_valid(a, b, row0);
+    const int64_t row0 = (int64_t)tl.rb * kSRows;
+    const int64_t col0 = tl.cb * kGCols;
+    const int64_t nv_blk = gemm_row_valid(a, b, min(row0 + kSRows, (int64_t)a.Qs) - 1);
     if (col0 >= a.ncols || col0 * a.stride >= nv_blk) return;
 
-    // query fragments: row wave*(16*kGQG) + qg*16 + n, bytes kb*128 + 32g .. +32
-    i32x8 qf[kGQG][KB];
-    int32_t nvr[kGQG];
-    float th[kGQG];
-    uint32_t cnt[kGQG];
+    const int64_t qrow = row0 + wave * 16 + n;
+    const bool qok = qrow < a.Qs;
+    i32x8 qf[KB];
+    {
+        const uint8_t* src = a.iq + ((int64_t)b * a.Qs + (qok ? qrow : 0)) * RB + 32 * g;
 #pragma unroll
-    for (int qg = 0; qg < kGQG; ++qg) {
-        const int64_t qrow = row0 + wave * 16 * kGQG + qg * 16 + n;
+        for (int kb = 0; kb < KB; ++kb) {
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(src + kb * 128);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(src + kb * 128 + 16);
+            qf[kb] = qok ? join(lo, hi) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+    const int64_t nvr = gemm_row_valid(a, b, qrow);
+    {
+        constexpr int TPE = kSThreads / kGCols;  // threads per staged entry
+        constexpr int BPT = RB / TPE;            // bytes per thread
+        const int64_t col = col0 + tid / TPE;
+        int64_t j = col * a.stride;
+        if (col >= a.ncols || j >= a.N) j = 0;  // masked below
+        const uint8_t* src = a.ik + ((int64_t)b * a.N_cap + j) * RB + (tid % TPE) * BPT;
+        uint8_t* dst = btile + (tid / TPE) * PITCH + (tid % TPE) * BPT;
+#pragma unroll
+        for (int q = 0; q < BPT / 16; ++q)
+            *reinterpret_cast<u32x4*>(dst + 16 * q) = *reinterpret_cast<const u32x4*>(src + 16 * q);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int eg = 0; eg < kGCols / 16; ++eg) {
+        const uint8_t* ks = btile + (eg * 16 + n) * PITCH + 32 * g;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            acc = mfma_fp8(join(*reinterpret_cast<const u32x4*>(ks + kb * 128),
+                                *reinterpret_cast<const u32x4*>(ks + kb * 128 + 16)),
+                           qf[kb], acc);
+        const int64_t cbase = col0 + eg * 16 + 4 * g;
+        if (qok) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t col = cbase + i;
+                if (col < a.ncols)
+                    a.out[((int64_t)b * a.Qs + qrow) * a.ncols + col] = col * a.stride < nvr ? acc[i] : -INFINITY;
+            }
+        }
+    }
+}
+
+// Candidate filter over every visible entry (stride 1): the (key, entry) of
+// every score with s^ >= theta[row] goes to the row's region for this column
+// block, blk[cb][row][0 .. kFBlkCap), with the count in blkcnt[cb][row];
+// entries past a region's capacity go to the row's overflow list cand[row]
+// (count cand_cnt[row], zeroed beforehand).  Keys are the float bits of s^
+// with the low 8 bits cleared (|change| < 2^-15 |s^|).
+//
+// Each wave holds 64 query rows (four 16-row groups) in registers, so every
+// key fragment it reads from LDS feeds 4 * KB MFMAs.  Lane (n, g) owns, per
+// group, four consecutive entries of one query row (a quad).  A quad whose
+// largest score reaches theta is appended to the wave's LDS list, compacted
+// with a ballot; the score bits carry tags in their low 8 bits (lane and group
+// in the first, the 16-entry group of the block in the second).  When the list
+// fills up the wave alone drains it: per quad it tests the four truncated keys,
+// takes positions from a per-row LDS counter and writes the survivors.  No
+// workgroup barrier, no global atomic unless a region overflows.
+template <int KB>
+__global__ __launch_bounds__(kFThreads) void filter_gemm_kernel(GemmArgs a) {
+    constexpr int RB = KB * 128;
+    constexpr int PITCH = RB + 16;
+    __shared__ __attribute__((aligned(16))) uint8_t btile[kGCols * PITCH];
+    __shared__ u32x4 wlist[kFWaves][kFList];
+    __shared__ uint2 s_row[kFRows];      // (theta bits, visible columns) per row
+    __shared__ uint32_t s_cnt[kFRows];   // candidates per row in this column block
+    const GemmTile tl = gemm_tile(a);
+    if (!tl.ok) return;
+    const int b = tl.b;
+    const int64_t cb = tl.cb;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int64_t row0 = (int64_t)tl.rb * kFRows;
+    const int64_t col0 = cb * kFBlkCols;
+    const int64_t nv_blk = gemm_row_valid(a, b, min(row0 + kFRows, (int64_t)a.Qs) - 1);
+    const int64_t nv_first = gemm_row_valid(a, b, row0);
+    const int64_t cend = min(a.ncols, nv_blk);  // columns some row of the block sees
+    if (col0 >= cend) return;
+    {
+        const int64_t qrow = row0 + tid;  // thread tid belongs to the wave that owns row tid
+        const float thr = qrow < a.Qs ? a.theta[(int64_t)b * a.Qs + qrow] : INFINITY;
+        s_row[tid] = make_uint2(__float_as_uint(thr), (uint32_t)min(a.ncols, gemm_row_valid(a, b, qrow)));
+        s_cnt[tid] = 0;
+    }
+
+    i32x8 qf[kFQG][KB];
+    uint32_t lim[kFQG];  // visible columns of the lane's row in each group
+    float th[kFQG];
+#pragma unroll
+    for (int qg = 0; qg < kFQG; ++qg) {
+        const int64_t qrow = row0 + wave * 64 + qg * 16 + n;
         const bool ok = qrow < a.Qs;
         const uint8_t* src = a.iq + ((int64_t)b * a.Qs + (ok ? qrow : 0)) * RB + 32 * g;
 #pragma unroll
@@ -120,162 +222,244 @@ __global__ __launch_bounds__(kGThreads) void gemm_fp8_kernel(GemmArgs a) {
             const u32x4 hi = *reinterpret_cast<const u32x4*>(src + kb * 128 + 16);
             qf[qg][kb] = ok ? join(lo, hi) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
-        nvr[qg] = (int32_t)gemm_row_valid(a, b, qrow);
-        th[qg] = (MODE && ok) ? a.theta[(int64_t)b * a.Qs + qrow] : INFINITY;
-        cnt[qg] = 0;
+        lim[qg] = (uint32_t)min(a.ncols, gemm_row_valid(a, b, qrow));
+        th[qg] = ok ? a.theta[(int64_t)b * a.Qs + qrow] : INFINITY;
     }
 
-    const int ntiles = MODE ? a.nsub : 1;
-    // key tiles are prefetched one tile ahead into registers: two threads per
-    // entry, out-of-range entries load entry 0 (masked in the epilogue)
-    constexpr int TPE = kGThreads / kGCols;  // threads per staged entry
-    constexpr int BPT = RB / TPE;            // bytes per thread
-    u32x4 pf[BPT / 16];
-    auto load_tile = [&](int64_t tc) {
-        const int64_t col = tc + tid / TPE;
-        int64_t j = col * a.stride;
-        if (col >= a.ncols || j >= a.N) j = 0;
-        const uint8_t* src = a.ik + ((int64_t)b * a.N_cap + j) * RB + (tid % TPE) * BPT;
+    u32x4* wl = wlist[wave];
+    // thresholds all positive: the pretest may compare float bits as integers
+    bool all_pos = true;
 #pragma unroll
-        for (int q = 0; q < BPT / 16; ++q) pf[q] = *reinterpret_cast<const u32x4*>(src + 16 * q);
+    for (int qg = 0; qg < kFQG; ++qg) all_pos = all_pos && th[qg] > 0.0f;
+    const bool ipre = __ballot(!all_pos) == 0;
+    // the tag mask and the lane tags live in VGPRs, so that each tag costs one v_and_or
+    uint32_t vmask = 0xffffff00u, ltag[kFQG];
+    asm volatile("" : "+v"(vmask));
+#pragma unroll
+    for (int qg = 0; qg < kFQG; ++qg) {
+        ltag[qg] = (uint32_t)(lane | (qg << 6));
+        asm volatile("" : "+v"(ltag[qg]));
+    }
+    // the block's regions, one per row, consecutive from wg_blk
+    uint2* const wg_blk = a.blk + (cb * a.B * a.Qs + (int64_t)b * a.Qs + row0) * kFBlkCap;
+    constexpr uint32_t row_pitch = kFBlkCap;  // the block's rows are consecutive regions
+    // Drain: each lane takes four quads at a time, so that the LDS round trips
+    // (quad, row data, row counter) of the four overlap.
+    auto drain = [&](uint32_t cq) __attribute__((always_inline)) {
+        constexpr int U = 4;
+        __builtin_amdgcn_wave_barrier();
+        for (uint32_t j0 = 0; j0 < cq; j0 += 64 * U) {
+            u32x4 v[U];
+            uint32_t lr[U], c0[U], pm[U], pos[U];
+            uint2 rw[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t j = j0 + u * 64 + lane;
+                v[u] = wl[j < cq ? j : 0u];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t lid = v[u][0] & 63u, qg = (v[u][0] >> 6) & 3u;
+                lr[u] = (uint32_t)wave * 64u + qg * 16u + (lid & 15u);
+                c0[u] = (uint32_t)col0 + (v[u][1] & 0xffu) * 16u + 4u * (lid >> 4);
+                rw[u] = s_row[lr[u]];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                // branch-free: bitwise and of the three tests
+                const uint32_t lim_u = j0 + u * 64 + lane < cq ? rw[u].y : 0u;
+                pm[u] = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pm[u] |= (uint32_t)((c0[u] + i < lim_u) & (__uint_as_float(v[u][i] & vmask) >= __uint_as_float(rw[u].x))) << i;
+                pos[u] = atomicAdd(&s_cnt[lr[u]], (uint32_t)__popc(pm[u]));  // adding 0 is harmless
+            }
+            bool over = false;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                uint2* dst = wg_blk + lr[u] * row_pitch;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t q = pos[u] + (uint32_t)__popc(pm[u] & ((1u << i) - 1u));
+                    if (((pm[u] >> i) & 1u) && q < (uint32_t)kFBlkCap) dst[q] = make_uint2(v[u][i] & vmask, c0[u] + i);
+                }
+                over |= pos[u] + (uint32_t)__popc(pm[u]) > (uint32_t)kFBlkCap;
+            }
+            if (over) {  // a region is full: the row's overflow list
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t r = (int64_t)b * a.Qs + row0 + lr[u];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t q = pos[u] + (uint32_t)__popc(pm[u] & ((1u << i) - 1u));
+                        if (((pm[u] >> i) & 1u) && q >= (uint32_t)kFBlkCap) {
+                            const uint32_t o = atomicAdd(&a.cand_cnt[r], 1u);
+                            if (o < (uint32_t)a.cap) a.cand[r * a.cap + o] = make_uint2(v[u][i] & vmask, c0[u] + i);
+                        }
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
     };
+
+    // A quad that finds the list full: its passing scores go straight to the
+    // row's overflow list (global atomics; only when candidates are dense).
+    auto spill = [&](const f32x4& v, int qg, uint32_t c0) __attribute__((always_inline)) {
+        const int64_t r = (int64_t)b * a.Qs + row0 + wave * 64 + qg * 16 + n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t key = __float_as_uint(v[i]) & 0xffffff00u;
+            if (c0 + (uint32_t)i < lim[qg] && __uint_as_float(key) >= th[qg]) {
+                const uint32_t o = atomicAdd(&a.cand_cnt[r], 1u);
+                if (o < (uint32_t)a.cap) a.cand[r * a.cap + o] = make_uint2(key, c0 + (uint32_t)i);
+            }
+        }
+    };
+
+    // the key tile is kGCols consecutive entries, one contiguous run of bytes:
+    // load c (16-byte chunk q * kFThreads + tid) lands at entry c / CPE, piece c % CPE
+    constexpr int CPE = RB / 16;                   // chunks per entry
+    constexpr int NLD = kGCols * CPE / kFThreads;  // chunks per thread
+    u32x4 pf[NLD];
+    auto load_tile = [&](int64_t tc) __attribute__((always_inline)) {  // the next key tile, into registers
+#pragma unroll
+        for (int q = 0; q < NLD; ++q) {
+            const int c = q * kFThreads + tid;
+            int64_t j = tc + c / CPE;
+            if (j >= a.ncols) j = 0;  // masked in the epilogue
+            pf[q] = *reinterpret_cast<const u32x4*>(a.ik + ((int64_t)b * a.N_cap + j) * RB + (c % CPE) * 16);
+        }
+    };
+    const int ntiles = (int)min<int64_t>(kFSub, (cend - col0 + kGCols - 1) / kGCols);
+    uint32_t wcnt = 0;  // quads in the wave's list (wave-uniform)
     load_tile(col0);
     for (int sub = 0; sub < ntiles; ++sub) {
-        const int64_t tc0 = col0 + (int64_t)sub * kGCols;  // first column of the tile
-        if (tc0 >= a.ncols || tc0 * a.stride >= nv_blk) break;  // workgroup-uniform
-        __syncthreads();  // previous tile consumed (and staging flushed)
-        {
-            uint8_t* dst = btile + (tid / TPE) * PITCH + (tid % TPE) * BPT;
+        const int64_t tc0 = col0 + (int64_t)sub * kGCols;
+        __syncthreads();  // previous tile consumed
 #pragma unroll
-            for (int q = 0; q < BPT / 16; ++q) *reinterpret_cast<u32x4*>(dst + 16 * q) = pf[q];
+        for (int q = 0; q < NLD; ++q) {
+            const int c = q * kFThreads + tid;
+            *reinterpret_cast<u32x4*>(btile + (c / CPE) * PITCH + (c % CPE) * 16) = pf[q];
+        }
+        __syncthreads();
+        // drain here, before the next tile's loads are issued: the wait for those
+        // loads (vmcnt counts stores too) then never waits for fresh stores
+        if (wcnt) {
+            drain(wcnt);
+            wcnt = 0;
         }
         if (sub + 1 < ntiles) load_tile(tc0 + kGCols);
-        __syncthreads();
-        // the window of the current flush starts at column fc0
-        const int64_t fc0 = col0 + (int64_t)(sub - sub % kGFlushTiles) * kGCols;
         // every column of the tile visible to every row of the block: no per-score test
-        const bool all_visible = (tc0 + kGCols) <= a.ncols && (tc0 + kGCols - 1) * a.stride < nv_first;
-        if (MODE == 1 && all_visible) {
-#pragma unroll 2
-            for (int eg = 0; eg < kGCols / 16; ++eg) {
-                i32x8 kf[KB];
-                const uint8_t* ks = btile + (eg * 16 + n) * PITCH + 32 * g;
+        const bool all_visible = tc0 + kGCols <= a.ncols && tc0 + kGCols <= nv_first;
+        auto read_kf = [&](i32x8 (&kf)[KB], int eg) {
+            const uint8_t* ks = btile + (eg * 16 + n) * PITCH + 32 * g;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    kf[kb] = join(*reinterpret_cast<const u32x4*>(ks + kb * 128),
-                                  *reinterpret_cast<const u32x4*>(ks + kb * 128 + 16));
-                const uint32_t off = (uint32_t)(tc0 - fc0) + eg * 16 + 4 * g;  // column offset in the window
+            for (int kb = 0; kb < KB; ++kb)
+                kf[kb] = join(*reinterpret_cast<const u32x4*>(ks + kb * 128),
+                              *reinterpret_cast<const u32x4*>(ks + kb * 128 + 16));
+        };
+        auto mma = [&](const i32x8 (&kf)[KB], f32x4 (&acc)[kFQG]) {
 #pragma unroll
-                for (int qg = 0; qg < kGQG; ++qg) {
-                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int qg = 0; qg < kFQG; ++qg) acc[qg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) acc = mfma_fp8(kf[kb], qf[qg][kb], acc);
-                    uint32_t* list = stage + ((wave * 16 * kGQG + qg * 16 + n) * 4 + g) * LIST;
-                    // branch-free: a score that does not pass is written to the trash slot
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool p = acc[i] >= th[qg];
-                        list[p ? min(cnt[qg], (uint32_t)kGSlots) : (uint32_t)kGSlots] =
-                            (__float_as_uint(acc[i]) & 0xffffff00u) | (off + i);
-                        cnt[qg] += p ? 1u : 0u;
+                for (int qg = 0; qg < kFQG; ++qg) acc[qg] = mfma_fp8(kf[kb], qf[qg][kb], acc[qg]);
+        };
+        // MASK: some column of the tile is hidden from some row.  IPRE: every
+        // threshold of the wave is positive, so s >= theta is a signed integer
+        // comparison of the float bits (no NaN handling, -0 below any theta).
+        auto run_tile = [&](auto mask_c, auto ipre_c) __attribute__((always_inline)) {
+            constexpr bool MASK = decltype(mask_c)::value, IPRE = decltype(ipre_c)::value;
+            auto epilogue = [&](f32x4 (&acc)[kFQG], int eg) {
+                const uint32_t grp = __builtin_amdgcn_readfirstlane((uint32_t)(sub * (kGCols / 16) + eg));
+                const uint32_t c0 = (uint32_t)tc0 + eg * 16 + 4 * g;
+                bool p[kFQG];
+                uint64_t bal[kFQG];
+#pragma unroll
+                for (int qg = 0; qg < kFQG; ++qg) {
+                    if constexpr (MASK) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (c0 + (uint32_t)i >= lim[qg]) acc[qg][i] = -INFINITY;
                     }
+                    if constexpr (IPRE) {
+                        const int32_t m = max(max(__float_as_int(acc[qg][0]), __float_as_int(acc[qg][1])),
+                                              max(__float_as_int(acc[qg][2]), __float_as_int(acc[qg][3])));
+                        p[qg] = m >= __float_as_int(th[qg]);
+                    } else {
+                        p[qg] = acc[qg][0] >= th[qg] || acc[qg][1] >= th[qg] || acc[qg][2] >= th[qg] ||
+                                acc[qg][3] >= th[qg];
+                    }
+                    bal[qg] = __ballot(p[qg]);
                 }
-            }
-        } else {
+#pragma unroll
+                for (int qg = 0; qg < kFQG; ++qg) {
+                    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[qg] >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal[qg], 0u));
+                    const uint32_t pos = wcnt + below;
+                    if (p[qg]) {
+                        if (pos < (uint32_t)kFList)
+                            wl[pos] = u32x4{(__float_as_uint(acc[qg][0]) & vmask) | ltag[qg],
+                                            (__float_as_uint(acc[qg][1]) & vmask) | grp, __float_as_uint(acc[qg][2]),
+                                            __float_as_uint(acc[qg][3])};
+                        else
+                            spill(acc[qg], qg, c0);  // the list is full (dense candidates)
+                    }
+                    wcnt = min(wcnt + (uint32_t)__popcll(bal[qg]), (uint32_t)kFList);
+                }
+            };
+            // the key fragments of group e + 1 are read while group e computes
+            // (VALU and MFMA issue do not overlap on this chip, so the MFMAs
+            // themselves are not pipelined against the epilogue)
+            i32x8 kfA[KB], kfB[KB];
+            f32x4 acc[kFQG];
+            read_kf(kfA, 0);
 #pragma unroll 1
-            for (int eg = 0; eg < kGCols / 16; ++eg) {
-                i32x8 kf[KB];
-                const uint8_t* ks = btile + (eg * 16 + n) * PITCH + 32 * g;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    kf[kb] = join(*reinterpret_cast<const u32x4*>(ks + kb * 128),
-                                  *reinterpret_cast<const u32x4*>(ks + kb * 128 + 16));
-                const int64_t cbase = tc0 + eg * 16 + 4 * g;  // this lane's first column
-#pragma unroll
-                for (int qg = 0; qg < kGQG; ++qg) {
-                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) acc = mfma_fp8(kf[kb], qf[qg][kb], acc);
-                    const int lr = wave * 16 * kGQG + qg * 16 + n;
-                    uint32_t* list = stage + (lr * 4 + g) * LIST;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t col = cbase + i;
-                        const bool valid = col < a.ncols && col * a.stride < nvr[qg];
-                        if (MODE == 0) {
-                            const int64_t qr = row0 + lr;
-                            if (col < a.ncols && qr < a.Qs)
-                                a.out[((int64_t)b * a.Qs + qr) * a.ncols + col] = valid ? acc[i] : -INFINITY;
-                        } else if (valid && acc[i] >= th[qg]) {
-                            list[min(cnt[qg], (uint32_t)kGSlots)] =
-                                (__float_as_uint(acc[i]) & 0xffffff00u) | (uint32_t)(col - fc0);
-                            ++cnt[qg];
-                        }
-                    }
-                }
+            for (int eg = 0; eg < kGCols / 16; eg += 2) {
+                read_kf(kfB, eg + 1);
+                mma(kfA, acc);
+                epilogue(acc, eg);
+                if (eg + 2 < kGCols / 16) read_kf(kfA, eg + 2);
+                mma(kfB, acc);
+                epilogue(acc, eg + 1);
             }
-        }
-        if (MODE) {
-            const bool last = sub + 1 == ntiles || tc0 + kGCols >= a.ncols ||
-                              (tc0 + kGCols) * a.stride >= nv_blk;
-            if (last || sub % kGFlushTiles == kGFlushTiles - 1) {
-#pragma unroll
-                for (int qg = 0; qg < kGQG; ++qg) {
-                    scnt[(wave * 16 * kGQG + qg * 16 + n) * 4 + g] = cnt[qg];
-                    cnt[qg] = 0;
-                }
-                __syncthreads();
-                if (tid < kGRows) {
-                    const int64_t qr = row0 + tid;
-                    uint32_t c4[4], tot = 0;
-                    bool over = false;
-#pragma unroll
-                    for (int gg = 0; gg < 4; ++gg) {
-                        c4[gg] = scnt[tid * 4 + gg];
-                        over |= c4[gg] > (uint32_t)kGSlots;
-                        tot += c4[gg];
-                    }
-                    if (qr < a.Qs && tot > 0) {
-                        const int64_t r = (int64_t)b * a.Qs + qr;
-                        if (over) {
-                            // candidates were lost: push the count past the list length so
-                            // that the final kernel recomputes the row exactly
-                            atomicAdd(&a.cand_cnt[r], (uint32_t)a.cap + 1u);
-                        } else {
-                            uint32_t pos = atomicAdd(&a.cand_cnt[r], tot);
-#pragma unroll
-                            for (int gg = 0; gg < 4; ++gg)
-                                for (uint32_t sl = 0; sl < c4[gg] && pos < (uint32_t)a.cap; ++sl, ++pos) {
-                                    const uint32_t v = stage[(tid * 4 + gg) * LIST + sl];
-                                    a.cand[r * a.cap + pos] = make_uint2(v, (uint32_t)(fc0 + (v & 0xffu)));
-                                }
-                        }
-                    }
-                }
-            }
-        }
+        };
+        if (all_visible && ipre) run_tile(std::false_type{}, std::true_type{});
+        else run_tile(std::true_type{}, std::false_type{});
+    }
+    if (wcnt) drain(wcnt);
+    {
+        const int lr = wave * 64 + lane;  // the wave's own rows
+        const int64_t qrow = row0 + lr;
+        if (qrow < a.Qs) a.blkcnt[cb * a.B * a.Qs + (int64_t)b * a.Qs + qrow] = s_cnt[lr];
     }
 }
 
 hipError_t launch_gemm_fp8(GemmArgs a, int mode, hipStream_t stream) {
     if (a.Qs == 0 || a.B == 0 || a.ncols == 0) return hipSuccess;
-    a.n_rowblk = (int)((a.Qs + kGRows - 1) / kGRows);
-    const int64_t cols_per_wg = (int64_t)a.nsub * kGCols;
-    a.n_colblk = (a.ncols + cols_per_wg - 1) / cols_per_wg;
+    if (a.K != 128 && a.K != 256) return hipErrorInvalidValue;
+    const int rows = mode == 0 ? kSRows : kFRows;
+    const int64_t cols = mode == 0 ? kGCols : kFBlkCols;
+    if (mode != 0 && a.stride != 1) return hipErrorInvalidValue;
+    a.n_rowblk = (int)((a.Qs + rows - 1) / rows);
+    a.n_colblk = (a.ncols + cols - 1) / cols;
     a.tiles = (int64_t)a.B * a.n_colblk * a.n_rowblk;
     a.per_xcd = (a.tiles + 7) / 8;
     const dim3 grid((unsigned)(8 * a.per_xcd));
-    if (a.K == 128) {
-        if (mode == 0) hipLaunchKernelGGL((gemm_fp8_kernel<1, 0>), grid, dim3(kGThreads), 0, stream, a);
-        else hipLaunchKernelGGL((gemm_fp8_kernel<1, 1>), grid, dim3(kGThreads), 0, stream, a);
-    } else if (a.K == 256) {
-        if (mode == 0) hipLaunchKernelGGL((gemm_fp8_kernel<2, 0>), grid, dim3(kGThreads), 0, stream, a);
-        else hipLaunchKernelGGL((gemm_fp8_kernel<2, 1>), grid, dim3(kGThreads), 0, stream, a);
+    if (mode == 0) {
+        if (a.K == 128) hipLaunchKernelGGL(sample_gemm_kernel<1>, grid, dim3(kSThreads), 0, stream, a);
+        else hipLaunchKernelGGL(sample_gemm_kernel<2>, grid, dim3(kSThreads), 0, stream, a);
     } else {
-        return hipErrorInvalidValue;
+        if (a.K == 128) hipLaunchKernelGGL(filter_gemm_kernel<1>, grid, dim3(kFThreads), 0, stream, a);
+        else hipLaunchKernelGGL(filter_gemm_kernel<2>, grid, dim3(kFThreads), 0, stream, a);
     }
     return hipGetLastError();
 }
+
+int64_t filter_colblks(int64_t ncols) { return (ncols + kFBlkCols - 1) / kFBlkCols; }
+int filter_blk_cap() { return kFBlkCap; }
 
 // Radix select: the `need`-th largest key T among the positions p < C for
 // which key_at(p, &k) returns true, and the count of such keys strictly above
@@ -406,18 +590,25 @@ CSA2_DEV float exact_score_fp8(const uint8_t* q, const uint8_t* k) {
 }
 
 // Per row: exact selection from the candidate list, or a fallback flag.
-// Candidates arrive as (float bits of s^ with the low 8 bits replaced, entry).
+// Candidates arrive as (float bits of s^ with the low 8 bits cleared, entry) in
+// the row's column-block regions and its overflow list.
 template <int KB>
-__global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
+__global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a) {
     constexpr int RB = KB * 128;
     __shared__ uint32_t s_key[kBandCap];   // sort keys minus the smallest; later the output bitmap
     __shared__ int32_t s_idx[kBandCap];    // entry index; bit 31 = selected
-    __shared__ uint32_t band[kBandList];   // positions of band entries
-    __shared__ uint32_t bkey[kBandList];   // their exact sort keys
-    __shared__ int32_t bidx[kBandList];    // and entries
-    __shared__ uint32_t hist[kHistBins];
+    // the digit histogram is dead once T^ is known; the band list and its
+    // entries then reuse its words (80 KB in all: two workgroups per CU)
+    __shared__ uint32_t s_hist[kBandHist];
+    static_assert(kBandHist >= 2 * kBandList, "band and bidx overlay the histogram");
+    uint32_t* const hist = s_hist;
+    uint32_t* const band = s_hist;                                        // positions of band entries
+    int32_t* const bidx = reinterpret_cast<int32_t*>(s_hist + kBandList);  // and their entries
+    __shared__ uint32_t bkey[kBandList];   // exact sort keys of the band (also the bin gather)
     __shared__ uint32_t scan_lds[kBandThreads / 64 + 1];
     __shared__ uint32_t dig[2];
+    __shared__ uint32_t s_off[kBandMaxBlk];  // first candidate of each column-block region
+    __shared__ uint32_t s_cnt[kBandMaxBlk];  // and its count
     __shared__ uint32_t red_u[kBandThreads / 64];
     __shared__ double red_q[kBandThreads / 64];
     __shared__ float red_k[kBandThreads / 64];
@@ -433,29 +624,18 @@ __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
     for (int64_t t = keff + threadIdx.x; t < a.k; t += kBandThreads) out[t] = -1;
     if (keff == 0) return;
 
-    const uint32_t C = a.cand_cnt[r];
     auto flag_row = [&]() {  // the exact row kernel recomputes this row
         if (threadIdx.x == 0) {
             a.flag[r] = 1;
             atomicAdd(a.flag_count, 1u);
         }
     };
-    if (C < (uint32_t)keff || C > (uint32_t)a.cap || C > (uint32_t)kBandCap || nv > kBandMaxValid) {
-        flag_row();
-        return;
-    }
-    // keys relative to the smallest candidate key: they span few bits
-    const uint2* cand = a.cand + r * a.cap;
-    uint32_t kmin = 0xffffffffu, kmax = 0;
-    for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
-        const uint2 c = cand[p];
-        const uint32_t k = sort_key(__uint_as_float(c.x & 0xffffff00u));
-        s_key[p] = k;
-        s_idx[p] = (int32_t)c.y;
-        kmin = min(kmin, k);
-        kmax = max(kmax, k);
-    }
-    // ||q||^2 (exact in fp64) and the sequence's bound on max ||k||^2
+    // every independent load first: overflow count, region counts, ||q||^2
+    // (exact in fp64) and the sequence's bound on max ||k||^2
+    const int64_t R = (int64_t)a.B * a.Qs;
+    const int nreg = (int)((min(nv, (int64_t)kBandMaxValid) + kFBlkCols - 1) / kFBlkCols);
+    const uint32_t novf = a.cand_cnt[r];
+    const uint32_t mine_c = threadIdx.x < nreg ? min(a.blkcnt[threadIdx.x * R + r], (uint32_t)kFBlkCap) : 0u;
     double q2 = 0.0;
     {
         const uint8_t* q = a.iq + r * RB;
@@ -466,6 +646,39 @@ __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
     }
     float k2 = 0.0f;
     for (int i = threadIdx.x; i < a.nblk; i += kBandThreads) k2 = fmaxf(k2, a.knorm[(int64_t)b * a.nblk + i]);
+    if (nv > kBandMaxValid || novf > (uint32_t)a.cap) {
+        flag_row();
+        return;
+    }
+    // the candidates: the row's column-block regions in order, then its overflow list
+    uint32_t nblkc;
+    const uint32_t my_off = block_exclusive_scan(mine_c, scan_lds, &nblkc);
+    const uint32_t C = nblkc + novf;
+    if (C < (uint32_t)keff || C > (uint32_t)kBandCap) {
+        flag_row();
+        return;
+    }
+    if (threadIdx.x < nreg) {
+        s_off[threadIdx.x] = my_off;
+        s_cnt[threadIdx.x] = mine_c;
+    }
+    __syncthreads();
+    // keys relative to the smallest candidate key: they span few bits.  One
+    // wave per region (at most kFBlkCap = 64 entries), so the loads are independent.
+    static_assert(kFBlkCap <= 64, "one lane per region entry");
+    uint32_t kmin = 0xffffffffu, kmax = 0;
+    const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
+    auto put = [&](uint32_t p, uint2 c) {
+        const uint32_t k = sort_key(__uint_as_float(c.x));
+        s_key[p] = k;
+        s_idx[p] = (int32_t)c.y;
+        kmin = min(kmin, k);
+        kmax = max(kmax, k);
+    };
+#pragma unroll 4
+    for (int i = wv; i < nreg; i += kBandThreads / 64)
+        if ((uint32_t)ln < s_cnt[i]) put(s_off[i] + ln, a.blk[((int64_t)i * R + r) * kFBlkCap + ln]);
+    for (uint32_t p = threadIdx.x; p < novf; p += kBandThreads) put(nblkc + p, a.cand[r * a.cap + p]);
     for (int o = 32; o >= 1; o >>= 1) {
         q2 += __shfl_xor(q2, o);
         k2 = fmaxf(k2, __shfl_xor(k2, o));
@@ -482,6 +695,7 @@ __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
     double Q2 = 0.0;
     float K2 = 0.0f;
     uint32_t K0 = 0xffffffffu, K1 = 0;
+#pragma unroll 2
     for (int wv = 0; wv < kBandThreads / 64; ++wv) {
         Q2 += red_q[wv];
         K2 = fmaxf(K2, red_k[wv]);
@@ -491,23 +705,25 @@ __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
     __syncthreads();
     for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) s_key[p] -= K0;
 
-    // T^: the keff-th largest key.  12-bit digits from the top of the used range;
+    // T^: the keff-th largest key.  11-bit digits from the top of the used range;
     // once the digit's bin holds few keys, they are ranked directly.
+    constexpr uint32_t DM = kBandHist - 1;
     const int bits = 32 - __clz((int)(K1 - K0) | 1);
     uint32_t prefix = 0, fixed = 0, need = (uint32_t)keff;
-    for (int sh = bits > 12 ? bits - 12 : 0;; sh = sh > 12 ? sh - 12 : 0) {
-        for (int i = threadIdx.x; i < kHistBins; i += kBandThreads) hist[i] = 0;
+    for (int sh = bits > kBandBits ? bits - kBandBits : 0;; sh = sh > kBandBits ? sh - kBandBits : 0) {
+        for (int i = threadIdx.x; i < kBandHist; i += kBandThreads) hist[i] = 0;
         __syncthreads();
         for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
             const uint32_t k = s_key[p];
-            if ((k & fixed) == prefix) atomicAdd(&hist[(k >> sh) & 0xfffu], 1u);
+            if ((k & fixed) == prefix) atomicAdd(&hist[(k >> sh) & DM], 1u);
         }
         __syncthreads();
-        find_digit<kBandThreads>(hist, kHistBins, need, scan_lds, dig);
+        find_digit<kBandThreads>(hist, kBandHist, need, scan_lds, dig);
         const uint32_t inbin = hist[dig[0]];
         prefix |= dig[0] << sh;
-        fixed |= 0xfffu << sh;
+        fixed |= DM << sh;
         need -= dig[1];
+        __syncthreads();  // every thread has read dig and hist
         if (sh == 0) break;
         if (inbin <= (uint32_t)kBandList) {
             // gather the bin's keys and find the need-th largest by counting
@@ -549,31 +765,32 @@ __global__ __launch_bounds__(kBandThreads) void band_final_kernel(BandArgs a) {
     // classify: above the band -> selected (bit 31); inside -> band list (block-scan compaction)
     uint32_t nin_mine = 0;
     {
-        uint32_t inb[kBandCap / kBandThreads];
+        uint32_t inb = 0;  // bit u: position threadIdx.x * PER + u is in the band
         uint32_t nb_mine = 0;
+        constexpr int PER = kBandCap / kBandThreads;
+        static_assert(PER <= 32, "one bit per position");
 #pragma unroll
-        for (int u = 0; u < kBandCap / kBandThreads; ++u) {
-            const uint32_t p = threadIdx.x * (kBandCap / kBandThreads) + u;  // contiguous per thread
-            inb[u] = 0;
+        for (int u = 0; u < PER; ++u) {
+            const uint32_t p = threadIdx.x * PER + u;  // contiguous per thread
             if (p < C) {
                 const double v = key_to_float(s_key[p] + K0);
                 if (v > hi) {
                     ++nin_mine;
                     s_idx[p] |= (int32_t)0x80000000;
                 } else if (v >= lo) {
-                    inb[u] = 1;
+                    inb |= 1u << u;
                     ++nb_mine;
                 }
             }
         }
         uint32_t nband_tot;
         uint32_t pos = block_exclusive_scan(nb_mine, scan_lds, &nband_tot);
-#pragma unroll
-        for (int u = 0; u < kBandCap / kBandThreads; ++u)
-            if (inb[u]) {
-                if (pos < (uint32_t)kBandList) band[pos] = threadIdx.x * (kBandCap / kBandThreads) + u;
-                ++pos;
-            }
+        while (inb) {
+            const int u = __ffs(inb) - 1;
+            inb &= inb - 1;
+            if (pos < (uint32_t)kBandList) band[pos] = threadIdx.x * PER + u;
+            ++pos;
+        }
         if (threadIdx.x == 0) dig[0] = nband_tot;
     }
     uint32_t nin;

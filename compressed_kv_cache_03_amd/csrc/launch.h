@@ -95,17 +95,20 @@ struct GemmArgs {
     const int32_t* nvb;    // [B]: row i sees j < nvb[b] - Qs + i + 1 (or null: j < N)
     int64_t stride;        // column c is entry c * stride
     int64_t ncols;         // columns per sequence
-    int nsub;              // 128-column tiles per workgroup (1 when storing)
     // filled by launch_gemm_fp8
     int n_rowblk;
     int64_t n_colblk, tiles, per_xcd;
     float* out;            // mode 0: [B*Qs][ncols] scores (-inf where not visible)
-    const float* theta;    // mode 1: [B*Qs] thresholds
-    uint2* cand;           // mode 1: [B*Qs][cap] (key with 8 low bits cleared, entry)
-    uint32_t* cand_cnt;    // mode 1: [B*Qs] (zeroed beforehand)
+    const float* theta;    // mode 1 (stride 1): [B*Qs] thresholds
+    uint2* blk;            // mode 1: [filter_colblks(ncols)][B*Qs][filter_blk_cap()] (key, entry)
+    uint32_t* blkcnt;      // mode 1: [filter_colblks(ncols)][B*Qs] candidates per region
+    uint2* cand;           // mode 1: [B*Qs][cap] overflow beyond a region's capacity
+    uint32_t* cand_cnt;    // mode 1: [B*Qs] overflow counts (zeroed beforehand)
     int cap;
 };
 hipError_t launch_gemm_fp8(GemmArgs a, int mode, hipStream_t stream);
+int64_t filter_colblks(int64_t ncols);  // column-block regions per row of the filter
+int filter_blk_cap();                   // candidates per region
 
 struct BandArgs {
     int B, Qs, K, k;
@@ -116,7 +119,10 @@ struct BandArgs {
     int64_t stride, ncols;
     const float* samp;     // [B*Qs][ncols]
     float* theta;          // [B*Qs]
-    const uint2* cand;
+    const uint2* blk;      // filter regions and counts (see GemmArgs)
+    const uint32_t* blkcnt;
+    int64_t n_colblk;
+    const uint2* cand;     // overflow lists
     uint32_t* cand_cnt;
     int cap;
     float* knorm;          // [B][nblk] bounds on max ||k||^2 per 256 entries
