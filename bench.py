@@ -6,12 +6,19 @@ modes Full, Reindex, Reuse, Reuse, top-k 2048, 16 bf16 heads of dim 128, window 
 Inputs are seeded synthetic N(0,1) data already resident in HBM when timing starts.
 
 Prints one JSON line with tokens/s, the roofline of the dominant kernel (the exact
-index-score stream) measured with HIP events, and the CPU oracle timed on a bounded
-sample of the same workload on this host's cores.
+index-score stream) measured with HIP events, the HBM traffic of that kernel from the
+committed rocprofv3 counter summary (null when the kernel source has changed since),
+a prefill-chunk leg (4,096 queries against 131,072 causal entries, e4m3 index keys on
+MFMA), and the CPU oracle timed on a bounded sample of the same workload on this
+host's cores.
+
+`--traffic-probe` runs only a 1 GiB device copy and five launches of the dominant
+kernel, for `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,6 +30,30 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_exact_w2_hbm_traffic.md")
+SCORE_SOURCE = os.path.join(ROOT, "compressed_kv_cache_03_amd", "csrc", "score.hip")
+
+
+def measured_traffic():
+    """Bytes per launch of the dominant kernel from the committed counter summary, or None
+    when the summary is missing or was taken on another version of the kernel source."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        src = hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.startswith("- "):
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("score.hip sha256") != src:
+        return None
+    try:
+        return int(fields["traffic bytes per launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _dev(a, device):
@@ -118,6 +149,67 @@ def run_gpu(wl, steps, warmup, device):
     return ms_step, ms_scan, inp
 
 
+def traffic_probe(wl, device):
+    """A plain 1 GiB device copy (the counter calibration) and five launches of the
+    dominant kernel on one group of the workload, nothing else."""
+    import torch
+
+    import compressed_kv_cache_03_amd as csa2
+    from synth.inputs import make_inputs
+
+    inp = make_inputs(wl)
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    first = next(L for L in inp.layers if L["mode"] == "F")
+    iq = _dev(first["iq"], device)
+    keys = _dev(inp.ikeys[first["group"]], device)
+    scores = torch.empty(wl.B, wl.Qs, wl.N, dtype=torch.float32, device=device)
+    for _ in range(5):
+        csa2.index_score(iq, keys, wl.idx_dtype, out=scores)
+    torch.cuda.synchronize()
+    print("traffic probe: 3 copies of 1073741824 B, 5 index-score launches", flush=True)
+
+
+def run_prefill(wl, steps, warmup, device):
+    """One Full layer over a prefill chunk; returns ms per chunk."""
+    import torch
+
+    import compressed_kv_cache_03_amd as csa2
+    from synth.inputs import make_inputs
+
+    inp = make_inputs(wl)
+    gc, gs = csa2.fp4_pack(_dev(inp.cache_x[0], device))
+    grp = csa2.Group(gc, gs, _dev(inp.ikeys[0], device), _dev(inp.n_valid, device), wl.idx_dtype, wl.k,
+                     sel_rows=wl.B * wl.Qs)
+    L = inp.layers[0]
+    kw = dict(q=_dev(L["q"], device), iq=_dev(L["iq"], device), wk=_dev(L["wk"], device),
+              wv=_dev(L["wv"], device), W=wl.W, sm_scale=wl.sm_scale,
+              new_entry=_dev(L["new_entry"], device), new_ikey=_dev(L["new_ikey"], device))
+    grp.workspace(wl.Qs, wl.Hq, wl.W)
+    for _ in range(warmup):
+        grp.layer_step("F", **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        grp.layer_step("F", **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def prefill_index_flops(wl):
+    """Useful MFMA work of the causal index scoring: 2 K flops per visible (query, entry)."""
+    K = wl.H_I * wl.d_I
+    visible = sum(wl.N - wl.Qs + i + 1 for i in range(wl.Qs)) * wl.B
+    return 2 * K * visible
+
+
 def cpu_baseline(wl, inp, target_seconds=12.0, max_reps=50):
     """The oracle, as it stands, on a bounded sample of the same workload: whole decode steps
     over (up to) 32 sequences, repeated until about target_seconds of host time have run."""
@@ -167,6 +259,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this implementation runs on one GPU; --gpus {args.gpus} is not supported "
@@ -180,6 +274,9 @@ def main():
     wl = ALL[args.workload]
     device = "cuda:0"
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.traffic_probe:
+        traffic_probe(wl, device)
+        return
     ms_step, ms_scan, inp = run_gpu(wl, args.steps, args.warmup, device)
     total_bytes, scan_bytes = algorithmic_bytes(wl)
     achieved = scan_bytes / (ms_scan * 1e-3) / 1e9
@@ -207,9 +304,20 @@ def main():
                      "frac": round(total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "roofline": {"kernel": "score_exact_kernel (exact index-score stream)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": scan_bytes, "avg_launch_us": round(ms_scan * 1e3, 2)},
     }
+    if not args.no_prefill:
+        pw = ALL[4]
+        ms_chunk = run_prefill(pw, 5, 2, device)
+        flops = prefill_index_flops(pw)
+        res["prefill"] = {
+            "workload": pw.name, "ms_per_chunk": round(ms_chunk, 4),
+            "tokens_per_s": round(pw.Qs / (ms_chunk * 1e-3), 1),
+            "index_flops": flops,
+            "index_tflops_over_whole_chunk": round(flops / (ms_chunk * 1e-3) / 1e12, 1),
+            "note": "whole Full layer (sampled threshold, MFMA score filter, exact band selection, "
+                    "attention); per-kernel MFMA figures are in profiles/"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(res), flush=True)
