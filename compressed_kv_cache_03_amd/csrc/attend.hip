@@ -395,13 +395,26 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a, int chunk, int
     }
 }
 
-// One workgroup of 256 threads per (row, head).  Thread t owns element
-// d = t % Dp of split group t / Dp (Dp = D rounded up to 64); each group takes
-// every G-th split with several loads in flight, and the groups are summed in
-// a fixed order.  Partial maxima are in log2 units.
+// Merge of the split partials of one (row, head): thread (grp, d) folds the
+// splits grp, grp + G, ... in that order with an online maximum (the loads of
+// eight splits are issued together, so one memory round trip covers them),
+// then group 0 folds groups 1 .. G-1 in order.  The order is fixed, so results
+// do not depend on scheduling.  Partial maxima are in log2 units.
+CSA2_DEV void fold(float& M, float& O, float& L, float m, float o, float l) {
+    if (m == -INFINITY) return;  // a split that saw no key
+    if (m > M) {
+        const float c = exp2f(M - m);  // 0 while M is -inf
+        O *= c;
+        L *= c;
+        M = m;
+    }
+    const float w = exp2f(m - M);
+    O = fmaf(w, o, O);
+    L = fmaf(w, l, L);
+}
+
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, int splits) {
-    __shared__ float red[4];
-    __shared__ float accO[256], accL[256];
+    __shared__ float sM[4], sO[256], sL[256];
     const int64_t r = blockIdx.x;
     const int h = blockIdx.y;
     const int Hq = a.Hq, D = a.D;
@@ -410,32 +423,29 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, int s
     const int t = threadIdx.x, d = t % Dp, grp = t / Dp;
     const int64_t stride = (int64_t)Hq * (D + 2);
     const float* part = a.part + (r * (int64_t)splits * Hq + h) * (D + 2);
-    float mx = -INFINITY;
-    for (int s = t; s < splits; s += 256) mx = fmaxf(mx, part[s * stride + D]);
+    float M = -INFINITY, O = 0.0f, L = 0.0f;
+    if (grp < G) {
+        constexpr int U = 8;
+        for (int s0 = grp; s0 < splits; s0 += U * G) {
+            float ms[U], os[U], ls[U];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if ((t & 63) == 0) red[t >> 6] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float L = 0.0f, O = 0.0f;
-    if (M != -INFINITY && grp < G) {
-#pragma unroll 4
-        for (int s = grp; s < splits; s += G) {
-            const float* ps = part + s * stride;
-            const float ms = ps[D];
-            const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-            L = fmaf(w, ps[D + 1], L);
-            if (d < D) O = fmaf(w, ps[d], O);
+            for (int u = 0; u < U; ++u) {
+                const int s = s0 + u * G;
+                const float* ps = part + (int64_t)(s < splits ? s : 0) * stride;
+                ms[u] = s < splits ? ps[D] : -INFINITY;
+                ls[u] = ps[D + 1];
+                os[u] = d < D ? ps[d] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) fold(M, O, L, ms[u], os[u], ls[u]);
         }
     }
-    accO[t] = O;
-    accL[t] = L;
+    sO[t] = O;
+    sL[t] = L;
+    if (d == 0 && grp < G) sM[grp] = M;
     __syncthreads();
     if (grp == 0 && d < D) {
-        for (int q = 1; q < G; ++q) {
-            O += accO[q * Dp + d];
-            L += accL[q * Dp + d];
-        }
+        for (int q = 1; q < G; ++q) fold(M, O, L, sM[q], sO[q * Dp + d], sL[q * Dp + d]);
         a.out[(r * Hq + h) * D + d] = M == -INFINITY ? 0.0f : O / L;
         if (d == 0 && a.lse) a.lse[r * Hq + h] = M == -INFINITY ? -INFINITY : M * kLn2 + logf(L);
     }
