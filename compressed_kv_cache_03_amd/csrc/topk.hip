@@ -228,6 +228,167 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(TopkArgs a) {
     }
 }
 
+// Rows of up to kRowMaxN entries: the whole selection in one workgroup per
+// row and one pass over the scores (what the compact + final pair does in two
+// launches).  Steps:
+//   1. b1 = the digit-1 bin of the keff-th largest key, from the row histogram;
+//   2. one coalesced pass: digit above b1 -> bit in an LDS bitmap of selected
+//      entries; digit == b1 -> (key, index) into an LDS candidate list;
+//   3. digits 2 and 3 over the candidates give the exact keff-th key T and the
+//      number `quota` of entries equal to T to take;
+//   4. candidates above T join the bitmap; entries equal to T join it too when
+//      all of them are taken, otherwise the first `quota` in index order are
+//      found with an ordered scan of the row;
+//   5. the bitmap is written out in index order.
+// A threshold bin with more than kRowCand entries (heavy ties) is resolved
+// from the scores in global memory instead of the LDS list: slower, same result.
+constexpr int kRowThreads = 1024;
+constexpr int kRowCand = 4096;
+constexpr int64_t kRowMaxN = 1 << 19;  // the bitmap (64 KiB) lives in LDS
+
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
+    __shared__ uint32_t s_hist[kHistBins];
+    __shared__ uint32_t s_ckey[kRowCand];
+    __shared__ int32_t s_cidx[kRowCand];
+    __shared__ uint32_t s_bits[kRowMaxN / 32];
+    __shared__ uint32_t scan_lds[kRowThreads / 64 + 1];
+    __shared__ uint32_t dig[2];
+    __shared__ uint32_t s_ncand;
+    const int64_t r = blockIdx.x;
+    const int64_t nv = topk_row_valid(a, r);
+    const int64_t keff = nv < a.k ? nv : a.k;
+    int32_t* out = a.idx + r * a.k;
+    for (int64_t t = keff + threadIdx.x; t < a.k; t += kRowThreads) out[t] = -1;
+    if (keff == 0) return;
+    const float* s = a.scores + r * a.ld;
+    const int nwords = (int)((nv + 31) / 32);
+    // the first batch of the row's scores is requested before anything else,
+    // so its latency overlaps the histogram's
+    const int64_t nv4 = (reinterpret_cast<uintptr_t>(s) & 15) == 0 ? nv / 4 : 0;
+    const float4* s4 = reinterpret_cast<const float4*>(s);
+    constexpr int U = 16;  // 16-byte loads per thread per batch: 64K entries
+    float4 v[U];
+    auto load_batch = [&](int64_t q0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t q = q0 + u * kRowThreads + threadIdx.x;
+            v[u] = s4[q < nv4 ? q : 0];
+        }
+    };
+    if (nv4 > 0) load_batch(0);
+
+    // 1. digit 1
+    for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) s_hist[i] = a.hist[r * kHistBins + i];
+    for (int i = threadIdx.x; i < nwords; i += kRowThreads) s_bits[i] = 0;
+    if (threadIdx.x == 0) s_ncand = 0;
+    __syncthreads();
+    find_digit<kRowThreads>(s_hist, kHistBins, (uint32_t)keff, scan_lds, dig);
+    const uint32_t b1 = dig[0];
+    const uint32_t need2 = (uint32_t)keff - dig[1];  // still to take from bin b1
+    const bool in_lds = s_hist[b1] <= (uint32_t)kRowCand;
+    __syncthreads();
+
+    // 2. one pass over the row
+    auto visit = [&](uint32_t key, int64_t j) {
+        const uint32_t d = key >> (32 - kHistBits);
+        if (d > b1) {
+            atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+        } else if (d == b1 && in_lds) {
+            const uint32_t p = atomicAdd(&s_ncand, 1u);
+            if (p < (uint32_t)kRowCand) {  // always, given the histogram of these scores
+                s_ckey[p] = key;
+                s_cidx[p] = (int32_t)j;
+            }
+        }
+    };
+    for (int64_t q0 = 0; q0 < nv4; q0 += (int64_t)U * kRowThreads) {
+        if (q0 > 0) load_batch(q0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t q = q0 + u * kRowThreads + threadIdx.x;
+            if (q < nv4) {
+                visit(sort_key(v[u].x), 4 * q);
+                visit(sort_key(v[u].y), 4 * q + 1);
+                visit(sort_key(v[u].z), 4 * q + 2);
+                visit(sort_key(v[u].w), 4 * q + 3);
+            }
+        }
+    }
+    for (int64_t j = 4 * nv4 + threadIdx.x; j < nv; j += kRowThreads) visit(sort_key(s[j]), j);
+    __syncthreads();
+    const uint32_t C = min(s_ncand, (uint32_t)kRowCand);
+
+    // the threshold bin's keys: from LDS, or filtered from the row
+    auto for_each_cand = [&](auto f) {
+        if (in_lds) {
+            for (uint32_t p = threadIdx.x; p < C; p += kRowThreads) f(s_ckey[p], (int64_t)s_cidx[p]);
+        } else {
+            for (int64_t j = threadIdx.x; j < nv; j += kRowThreads) {
+                const uint32_t key = sort_key(s[j]);
+                if ((key >> (32 - kHistBits)) == b1) f(key, j);
+            }
+        }
+    };
+    // 3. digits 2 (bits 19..8) and 3 (bits 7..0)
+    uint32_t prefix = b1 << (32 - kHistBits), need = need2;
+    {
+        for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) s_hist[i] = 0;
+        __syncthreads();
+        for_each_cand([&](uint32_t key, int64_t) { atomicAdd(&s_hist[(key >> 8) & 0xfffu], 1u); });
+        __syncthreads();
+        find_digit<kRowThreads>(s_hist, kHistBins, need, scan_lds, dig);
+        prefix |= dig[0] << 8;
+        need -= dig[1];
+        __syncthreads();
+        for (int i = threadIdx.x; i < 256; i += kRowThreads) s_hist[i] = 0;
+        __syncthreads();
+        for_each_cand([&](uint32_t key, int64_t) {
+            if ((key & 0xffffff00u) == prefix) atomicAdd(&s_hist[key & 0xffu], 1u);
+        });
+        __syncthreads();
+        find_digit<kRowThreads>(s_hist, 256, need, scan_lds, dig);
+        prefix |= dig[0];
+        need -= dig[1];
+    }
+    const uint32_t T = prefix, quota = need;  // take every key > T and `quota` keys == T
+    const uint32_t ties = s_hist[T & 0xffu];
+    __syncthreads();
+
+    // 4. candidates above T; ties when all of them are taken
+    for_each_cand([&](uint32_t key, int64_t j) {
+        if (key > T || (key == T && quota == ties)) atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+    });
+    if (quota != ties) {
+        // the first `quota` entries equal to T in index order: ordered scan of the row
+        uint32_t before = 0;
+        for (int64_t j0 = 0; j0 < nv && before < quota; j0 += kRowThreads) {
+            const int64_t j = j0 + threadIdx.x;
+            const uint32_t tie = (j < nv && sort_key(s[j]) == T) ? 1u : 0u;
+            uint32_t n;
+            const uint32_t rank = before + block_exclusive_scan(tie, scan_lds, &n);
+            if (tie && rank < quota) atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+            before += n;
+        }
+    }
+    __syncthreads();
+
+    // 5. ascending output
+    const int per = (nwords + kRowThreads - 1) / kRowThreads;
+    uint32_t mine = 0;
+    for (int wi = threadIdx.x * per; wi < min(nwords, (int)(threadIdx.x + 1) * per); ++wi) mine += __popc(s_bits[wi]);
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan(mine, scan_lds, &total);
+    for (int wi = threadIdx.x * per; wi < min(nwords, (int)(threadIdx.x + 1) * per); ++wi) {
+        uint32_t word = s_bits[wi];
+        while (word) {
+            const int bit = __ffs(word) - 1;
+            word &= word - 1;
+            if (pos < (uint32_t)keff) out[pos] = wi * 32 + bit;
+            ++pos;
+        }
+    }
+}
+
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t stream) {
     if (a.R == 0 || a.N == 0) return hipSuccess;
     dim3 grid((unsigned)a.slices, (unsigned)a.R);
@@ -237,6 +398,10 @@ hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t stream) {
 
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t stream) {
     if (a.R == 0) return hipSuccess;
+    if (a.N <= kRowMaxN) {
+        hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)a.R), dim3(kRowThreads), 0, stream, a);
+        return hipGetLastError();
+    }
     if (a.N > 0) {
         dim3 grid((unsigned)a.slices, (unsigned)a.R);
         hipLaunchKernelGGL(topk_compact_kernel, grid, dim3(kSliceThreads), 0, stream, a);

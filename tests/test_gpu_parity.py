@@ -140,6 +140,18 @@ def test_topk_parity(k):
     assert np.array_equal(host(got), ref)
 
 
+@pytest.mark.parametrize("k", [1, 700, 4099])
+def test_topk_parity_unaligned_rows(k):
+    # an odd row length: rows start off 16-byte boundaries, so every score is
+    # read one at a time
+    R, N = 5, 4099
+    s = _topk_scores(R, N, 11 + k)
+    nv = np.array([N, 4098, 17, N, 1], np.int32)
+    got = csa2.topk(dev(s), k, n_valid=dev(nv))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got), oracle.topk(s, k, n_valid=nv.astype(np.int64)))
+
+
 def test_topk_parity_long_row_multi_pass_slices():
     # beyond 2^24 entries a slice spans several 4096-entry compaction passes
     N = (1 << 24) + 5000
