@@ -82,7 +82,7 @@ def algorithmic_bytes(wl):
     return total, scan
 
 
-def run_gpu(wl, steps, warmup, device):
+def run_gpu(wl, steps, warmup, device, scan_loop=True):
     import torch
 
     import compressed_kv_cache_03_amd as csa2
@@ -130,6 +130,8 @@ def run_gpu(wl, steps, warmup, device):
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / steps
+    if not scan_loop:
+        return ms_step, None, inp, groups
 
     # dominant kernel: the exact index-score stream over one group's keys (same kernel the
     # Full/Reindex layers launch), timed over its own loop on the same stream
@@ -146,7 +148,31 @@ def run_gpu(wl, steps, warmup, device):
     e1.record(stream)
     torch.cuda.synchronize()
     ms_scan = e0.elapsed_time(e1) / reps
-    return ms_step, ms_scan, inp
+    return ms_step, ms_scan, inp, groups
+
+
+def host_tier(grp, reps=3):
+    """Save a group to a pinned host image and restore it: GB/s each way."""
+    import torch
+
+    image = grp.save()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record(stream)
+    for _ in range(reps):
+        grp.save(image)
+    e[1].record(stream)
+    for _ in range(reps):
+        grp.restore(image)
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    n = image.numel()
+    ms_save, ms_restore = e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
+    return {"image_bytes": n, "save_GBps": round(n / (ms_save * 1e-3) / 1e9, 1),
+            "restore_GBps": round(n / (ms_restore * 1e-3) / 1e9, 1),
+            "note": "pinned host image of the w2 sharing group (FP4 codes, scales, bf16 index keys, "
+                    "selection); device <-> host copies, restored bits checked by the GPU tests"}
 
 
 def traffic_probe(wl, device):
@@ -260,6 +286,7 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -277,7 +304,7 @@ def main():
     if args.traffic_probe:
         traffic_probe(wl, device)
         return
-    ms_step, ms_scan, inp = run_gpu(wl, args.steps, args.warmup, device)
+    ms_step, ms_scan, inp, groups = run_gpu(wl, args.steps, args.warmup, device)
     total_bytes, scan_bytes = algorithmic_bytes(wl)
     achieved = scan_bytes / (ms_scan * 1e-3) / 1e9
     tokens = wl.B * wl.Qs
@@ -307,6 +334,16 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": scan_bytes, "avg_launch_us": round(ms_scan * 1e3, 2)},
     }
+    res["host_tier"] = host_tier(groups[0])
+    del groups
+    if not args.no_verify:
+        vw = ALL[6]
+        ms_v, _, _, _ = run_gpu(vw, max(args.steps // 2, 3), 2, device, scan_loop=False)
+        res["verify5"] = {
+            "workload": vw.name, "ms_per_step": round(ms_v, 4),
+            "tokens_per_s": round(vw.B * vw.Qs / (ms_v * 1e-3), 1),
+            "note": "draft block of 5 queries per sequence through the same 4-layer group; tokens/s "
+                    "counts the 5 verified positions of each of the 32 sequences per step"}
     if not args.no_prefill:
         pw = ALL[4]
         ms_chunk = run_prefill(pw, 5, 2, device)

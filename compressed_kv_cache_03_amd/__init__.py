@@ -69,10 +69,14 @@ def _load():
     lib.csa2_layer_workspace_bytes.restype = sz
     lib.csa2_layer_step.argtypes = [ctypes.c_int, ctypes.POINTER(CLayerArgs), ctypes.POINTER(CGroup),
                                     vp, sz, vp]
+    lib.csa2_group_image_bytes.argtypes = [ctypes.POINTER(CGroup)]
+    lib.csa2_group_image_bytes.restype = sz
+    lib.csa2_group_save.argtypes = [ctypes.POINTER(CGroup), vp, sz, vp]
+    lib.csa2_group_restore.argtypes = [ctypes.POINTER(CGroup), vp, sz, vp]
     lib.csa2_cache_bytes.argtypes = [i64, i64, i64, i64]
     lib.csa2_cache_bytes.restype = i64
     for name in ("csa2_fp4_pack", "csa2_index_score", "csa2_topk", "csa2_sparse_attend",
-                 "csa2_layer_step"):
+                 "csa2_layer_step", "csa2_group_save", "csa2_group_restore"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -239,6 +243,30 @@ class Group:
                                      ws.numel(), _stream(stream))
         _check(st, f"csa2_layer_step({mode})")
         return out, lse
+
+    def image_bytes(self) -> int:
+        """Size of the group's host-tier image (entries, keys and selection)."""
+        return int(_load().csa2_group_image_bytes(ctypes.byref(self.c)))
+
+    def save(self, host: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Copy the group into a host byte tensor (pinned by default); asynchronous."""
+        n = self.image_bytes()
+        if host is None:
+            host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+        if host.device.type != "cpu" or not host.is_contiguous():
+            raise ValueError("host image must be a contiguous CPU tensor")
+        st = _load().csa2_group_save(ctypes.byref(self.c), host.data_ptr(), host.numel() * host.element_size(),
+                                     _stream(stream))
+        _check(st, "csa2_group_save")
+        return host
+
+    def restore(self, host: torch.Tensor, stream=None):
+        """Copy a host image back into the group's device buffers; asynchronous."""
+        if host.device.type != "cpu" or not host.is_contiguous():
+            raise ValueError("host image must be a contiguous CPU tensor")
+        st = _load().csa2_group_restore(ctypes.byref(self.c), host.data_ptr(),
+                                        host.numel() * host.element_size(), _stream(stream))
+        _check(st, "csa2_group_restore")
 
     def step_status(self, mode: str, **kw) -> int:
         """Like layer_step but returns the status code instead of raising."""

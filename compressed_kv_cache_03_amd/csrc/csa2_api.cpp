@@ -122,6 +122,40 @@ bool valid_index_width(csa2_idx_dtype dt, int32_t H, int32_t d) {
     return K <= 4096 && K % 16 == 0 && (dt == CSA2_IDX_BF16 || dt == CSA2_IDX_FP8_E4M3);
 }
 
+
+// Host-tier image of a group: for entries 0 .. n_valid_max-1 of every
+// sequence, codes, then scales, then index keys, then the selection when the
+// group holds one (B * sel_qs rows of k).
+struct ImageParts {
+    int64_t n = 0;
+    size_t code_row = 0, scale_row = 0, key_row = 0;  // bytes per entry
+    size_t codes = 0, scales = 0, keys = 0, sel = 0, total = 0;
+};
+
+bool image_parts(const csa2_group* g, ImageParts* p) {
+    if (!g || g->B < 1 || g->N_cap < 1 || !valid_dim(g->D) || g->k < 1 ||
+        !valid_index_width(g->idx_dtype, g->H_I, g->d_I) || g->n_valid_max < 0 || g->n_valid_max > g->N_cap)
+        return false;
+    if (g->has_selection && (g->sel_qs < 1 || (int64_t)g->B * g->sel_qs > g->sel_rows)) return false;
+    p->n = g->n_valid_max;
+    p->code_row = (size_t)g->D / 2;
+    p->scale_row = (size_t)g->D / 32 * 4;
+    p->key_row = (size_t)g->H_I * g->d_I * idx_elem_bytes(g->idx_dtype);
+    p->codes = (size_t)g->B * p->n * p->code_row;
+    p->scales = (size_t)g->B * p->n * p->scale_row;
+    p->keys = (size_t)g->B * p->n * p->key_row;
+    p->sel = g->has_selection ? (size_t)g->B * g->sel_qs * g->k * 4 : 0;
+    p->total = p->codes + p->scales + p->keys + p->sel;
+    return true;
+}
+
+// One strided array between the group (row pitch N_cap entries) and the packed image.
+hipError_t copy_rows(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t rows,
+                     hipMemcpyKind kind, hipStream_t s) {
+    if (width == 0 || rows == 0) return hipSuccess;
+    return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, rows, kind, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -457,6 +491,56 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         g->has_selection = 1;
         g->sel_qs = Qs;
     }
+    return CSA2_OK;
+}
+
+size_t csa2_group_image_bytes(const csa2_group* g) {
+    ImageParts p;
+    return image_parts(g, &p) ? p.total : 0;
+}
+
+csa2_status csa2_group_save(const csa2_group* g, void* host, size_t bytes, void* stream) {
+    ImageParts p;
+    if (!image_parts(g, &p) || !host || !g->codes || !g->scales || !g->ikeys || (p.sel && !g->sel))
+        return CSA2_ERR_INVALID_ARG;
+    if (!g->has_entries) return CSA2_ERR_STATE;
+    if (bytes < p.total) return CSA2_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* h = static_cast<char*>(host);
+    const size_t B = (size_t)g->B, N = (size_t)g->N_cap, n = (size_t)p.n;
+    hipError_t e = copy_rows(h, n * p.code_row, g->codes, N * p.code_row, n * p.code_row, B,
+                             hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = copy_rows(h + p.codes, n * p.scale_row, g->scales, N * p.scale_row, n * p.scale_row, B,
+                      hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = copy_rows(h + p.codes + p.scales, n * p.key_row, g->ikeys, N * p.key_row, n * p.key_row, B,
+                      hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && p.sel)
+        e = hipMemcpyAsync(h + p.codes + p.scales + p.keys, g->sel, p.sel, hipMemcpyDeviceToHost, s);
+    return hip_status(e);
+}
+
+csa2_status csa2_group_restore(csa2_group* g, const void* host, size_t bytes, void* stream) {
+    ImageParts p;
+    if (!image_parts(g, &p) || !host || !g->codes || !g->scales || !g->ikeys || (p.sel && !g->sel))
+        return CSA2_ERR_INVALID_ARG;
+    if (bytes < p.total) return CSA2_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const char* h = static_cast<const char*>(host);
+    const size_t B = (size_t)g->B, N = (size_t)g->N_cap, n = (size_t)p.n;
+    hipError_t e = copy_rows(g->codes, N * p.code_row, h, n * p.code_row, n * p.code_row, B,
+                             hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = copy_rows(g->scales, N * p.scale_row, h + p.codes, n * p.scale_row, n * p.scale_row, B,
+                      hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = copy_rows(g->ikeys, N * p.key_row, h + p.codes + p.scales, n * p.key_row, n * p.key_row, B,
+                      hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && p.sel)
+        e = hipMemcpyAsync(g->sel, h + p.codes + p.scales + p.keys, p.sel, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return CSA2_ERR_HIP;
+    g->has_entries = 1;
     return CSA2_OK;
 }
 

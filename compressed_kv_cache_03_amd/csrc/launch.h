@@ -38,6 +38,9 @@ struct ScoreArgs {
     float* scores;        // [R][ld]
     int64_t ld;
     uint32_t* hist;       // [R][4096] or null
+    // filled by launch_score_exact: with several query rows per sequence the
+    // blocks of one entry block and all its rows run together on one XCD
+    int64_t n_eblk = 0, blocks = 0, per_xcd = 0;
 };
 hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t stream);
 

@@ -157,10 +157,22 @@ template <int DT, int CPL>
 __global__ __launch_bounds__(kScoreThreads) void score_exact_kernel(ScoreArgs a) {
     constexpr int EPC = DT == 0 ? 8 : 16;  // elements per 16-byte chunk
     constexpr int EB = 128 * CPL;         // bytes per entry
-    const int64_t r = blockIdx.y;
+    int64_t r, e_block;
+    if (a.Qs == 1) {
+        r = blockIdx.y;
+        e_block = (int64_t)blockIdx.x * kScoreEntriesPerBlock;
+    } else {
+        // block w takes t = (w % 8) * per_xcd + w / 8: the Qs rows of a sequence
+        // for one entry block are consecutive t on one XCD and share its L2
+        const int64_t w = blockIdx.x;
+        const int64_t t = (w & 7) * a.per_xcd + (w >> 3);
+        if (t >= a.blocks) return;
+        const int64_t rest = t / a.Qs;
+        r = (rest / a.n_eblk) * a.Qs + t % a.Qs;
+        e_block = (rest % a.n_eblk) * kScoreEntriesPerBlock;
+    }
     const int64_t b = r / a.Qs;
     const int64_t nv = row_valid(a, r);
-    const int64_t e_block = (int64_t)blockIdx.x * kScoreEntriesPerBlock;
     if (e_block >= nv) return;
 
     __shared__ uint32_t lhist[kHistBins];
@@ -357,14 +369,18 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
     if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
 }
 
-hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t stream) {
+hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
+    ScoreArgs a = args;
     const int64_t R = (int64_t)a.B * a.Qs;
     if (R == 0 || a.N == 0) return hipSuccess;
     const int eb = a.K * (a.dtype == 0 ? 2 : 1);
     const int cpl = eb / 128;
     const bool fast = eb % 128 == 0 && (cpl == 1 || cpl == 2 || cpl == 4 || cpl == 8);
     if (fast) {
-        dim3 grid((unsigned)((a.N + kScoreEntriesPerBlock - 1) / kScoreEntriesPerBlock), (unsigned)R);
+        a.n_eblk = (a.N + kScoreEntriesPerBlock - 1) / kScoreEntriesPerBlock;
+        a.blocks = a.n_eblk * R;
+        a.per_xcd = (a.blocks + 7) / 8;
+        const dim3 grid = a.Qs == 1 ? dim3((unsigned)a.n_eblk, (unsigned)R) : dim3((unsigned)(8 * a.per_xcd));
         if (a.dtype == 0) {
             if (cpl == 1) hipLaunchKernelGGL((score_exact_kernel<0, 1>), grid, dim3(kScoreThreads), 0, stream, a);
             if (cpl == 2) hipLaunchKernelGGL((score_exact_kernel<0, 2>), grid, dim3(kScoreThreads), 0, stream, a);

@@ -184,6 +184,28 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
  * overflows int64. */
 int64_t csa2_cache_bytes(int64_t entries, int64_t numbers, int64_t copies, int64_t bits);
 
+/* Persistent tier ("DeepSeek-V4.1-Flash", "Fast memory, persistent storage
+ * and recomputation": the FP4 main entries are what a slower storage tier keeps
+ * and brings back; "Why Is DeepSeek V4.1 Flash So Fast?", section 7).
+ *
+ * A group image is a packed byte copy of what a group holds for entries
+ * 0 .. n_valid_max-1 of every sequence, in this order:
+ *   codes  [B][n_valid_max][D/2]     u8
+ *   scales [B][n_valid_max][D/32]    f32
+ *   ikeys  [B][n_valid_max][H_I][d_I] in idx_dtype
+ *   sel    [B*sel_qs][k]             i32, only when has_selection is set.
+ * csa2_group_image_bytes returns its size (0 for an invalid group).
+ * csa2_group_save copies the group into `host` (bytes >= the image size;
+ * CSA2_ERR_STATE if the group holds no entries).  csa2_group_restore copies an
+ * image back into a group of the same geometry, n_valid_max, has_selection and
+ * sel_qs, and sets has_entries.  Both are asynchronous on `stream`: the host
+ * buffer must stay alive until the stream reaches them, and it should be
+ * pinned (page-locked) for the copies to run at full rate.  Copy failures
+ * return CSA2_ERR_HIP; nothing is validated against the image's contents. */
+size_t csa2_group_image_bytes(const csa2_group* group);
+csa2_status csa2_group_save(const csa2_group* group, void* host, size_t bytes, void* stream);
+csa2_status csa2_group_restore(csa2_group* group, const void* host, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

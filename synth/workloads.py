@@ -6,6 +6,8 @@ Shapes follow the workload list this implementation is measured on:
   w3  long-context decode, batch 8, 262,144 entries, one Full layer, 4x64 fp8 e4m3, k=2048
   w4  prefill chunk, 4,096 queries against a causal 131,072-entry cache, 4x64 fp8, k=2048
   w5  16-layer decode stack, batch 64, 131,072 entries, (F,Ri,Ru,Ru) x 4, 4x64 bf16, k=2048
+  w6  speculative verify: w2 with a draft block of 5 queries per sequence, causal among
+      the drafts (query i of the block sees the entries up to its own)
 Every layer: 16 bf16 query heads of dim 128, scale 1/sqrt(128), a 128-row bf16 window,
 entries of dim 128 stored as FP4 e2m1 with an fp32 scale per 32 elements.
 
@@ -76,4 +78,7 @@ W4 = Workload(4, "prefill_q4096_n131072_causal_fp8idx", B=1, N=131072, H_I=4, d_
 W5 = Workload(5, "decode_b64_n131072_16layer_stack", B=64, N=131072, H_I=4, d_I=64,
               idx_dtype="bf16", k=2048, pattern=("F", "Ri", "Ru", "Ru"), groups=4)
 
-ALL = {1: W1, 2: W2, 3: W3, 4: W4, 5: W5}
+W6 = Workload(6, "verify5_b32_n65536_group_F_Ri_Ru_Ru", B=32, N=65536, H_I=4, d_I=64,
+              idx_dtype="bf16", k=2048, pattern=("F", "Ri", "Ru", "Ru"), Qs=5)
+
+ALL = {1: W1, 2: W2, 3: W3, 4: W4, 5: W5, 6: W6}

@@ -132,3 +132,22 @@ def test_layer_step_argument_errors():
     assert _step(0, _group(), _args(Hq=0)) == csa2.ERR_INVALID_ARG
     assert _step(0, _group(), _args(), ws_bytes=100) == csa2.ERR_WORKSPACE
     assert _step(0, _group(B=70000), _args()) == csa2.ERR_UNSUPPORTED
+
+
+def test_group_image_bytes_and_save_restore_validation():
+    L = csa2.lib()
+    g = _group()  # B=2, N_cap=1000, D=128, 4x64 bf16, k=64, n_valid_max=1000, no selection
+    per_entry = 128 // 2 + 128 // 32 * 4 + 4 * 64 * 2  # codes + scales + bf16 keys
+    assert L.csa2_group_image_bytes(ctypes.byref(g)) == 2 * 1000 * per_entry
+    gs = _group(has_selection=1, sel_qs=1, n_valid_max=300, idx_dtype=1)
+    per_entry8 = 128 // 2 + 128 // 32 * 4 + 4 * 64
+    assert L.csa2_group_image_bytes(ctypes.byref(gs)) == 2 * 300 * per_entry8 + 2 * 1 * 64 * 4
+    assert L.csa2_group_image_bytes(ctypes.byref(_group(D=100))) == 0
+    assert L.csa2_group_image_bytes(ctypes.byref(_group(has_selection=1, sel_qs=2))) == 0  # sel_rows 2 < B*2
+    need = L.csa2_group_image_bytes(ctypes.byref(g))
+    # every error is found before a copy is queued
+    assert L.csa2_group_save(ctypes.byref(g), None, need, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_group_save(ctypes.byref(g), FAKE, need - 1, None) == csa2.ERR_WORKSPACE
+    assert L.csa2_group_save(ctypes.byref(_group(has_entries=0)), FAKE, need, None) == csa2.ERR_STATE
+    assert L.csa2_group_restore(ctypes.byref(g), FAKE, need - 1, None) == csa2.ERR_WORKSPACE
+    assert L.csa2_group_restore(ctypes.byref(_group(codes=None)), FAKE, need, None) == csa2.ERR_INVALID_ARG

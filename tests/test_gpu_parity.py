@@ -11,7 +11,7 @@ import compressed_kv_cache_03_amd as csa2
 import oracle
 import synth
 from cases import make_inputs, rel_err
-from synth.workloads import W1, W2, W3, W4, W5
+from synth.workloads import W1, W2, W3, W4, W5, W6
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -268,6 +268,47 @@ def test_group_w2_scaled_ragged():
 
 def test_w3_scaled_fp8():
     Run(W3.scaled(B=2, N=9000), n_valid=[9000, 5000]).check_all()
+
+
+def test_group_save_restore_resumes_bitwise():
+    # Full and Reindex, then the group goes to a pinned host image, its device
+    # buffers are overwritten, the image comes back, and the two Reuse layers
+    # give the same bits as an uninterrupted run
+    wl = W2.scaled(B=3, N=6000, k=500)
+    nv = [5000, 6000, 4321]  # n_valid_max below N_cap: strided copies
+    ref = Run(wl, n_valid=nv)
+    ref_out = [ref.layer(li)[4:] for li in range(4)]
+    run = Run(wl, n_valid=nv)
+    for li in range(2):
+        run.layer(li)
+    g = run.g_gpu[0]
+    n = int(max(nv))
+    before = [host(t).copy() for t in (g.codes[:, :n], g.scales[:, :n], g.ikeys[:, :n], g.sel)]
+    image = g.save()
+    torch.cuda.synchronize()
+    assert image.numel() == g.image_bytes()
+    g.codes.fill_(0x5A)
+    g.scales.fill_(float("nan"))
+    g.ikeys.fill_(0x7FC1)
+    g.sel.fill_(-7)
+    g.restore(image)
+    torch.cuda.synchronize()
+    after = [host(t) for t in (g.codes[:, :n], g.scales[:, :n], g.ikeys[:, :n], g.sel)]
+    for a, b in zip(before, after):
+        assert bits_eq(a, b)
+    for li in range(2, 4):
+        mode, _, _, _, go, gl = run.layer(li)
+        assert mode == "Ru"
+        assert bits_eq(go, ref_out[li][0]) and bits_eq(gl, ref_out[li][1]), li
+
+
+def test_verify5_w6_scaled():
+    # a draft block of 5 queries per sequence through Full/Reindex/Reuse/Reuse
+    Run(W6.scaled(B=3, N=5000, k=700)).check_all()
+
+
+def test_verify5_w6_ragged_n_valid():
+    Run(W6.scaled(B=4, N=3000, k=256), n_valid=[3000, 2048, 300, 5]).check_all()
 
 
 def test_prefill_w4_scaled():
