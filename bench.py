@@ -66,12 +66,16 @@ def _dev(a, device):
 def algorithmic_bytes(wl):
     """Bytes the method must move per step (measurement section)."""
     B, N, D, K, k, W, Hq, Qs = wl.B, wl.N, wl.D, wl.H_I * wl.d_I, wl.k, wl.W, wl.Hq, wl.Qs
-    eb = 2 if wl.idx_dtype == "bf16" else 1
+    if wl.idx_dtype == "fp4":
+        key_b, q_b, new_key_b = K // 2 + K // 32 * 4, K * 2, K * 4 + K // 2 + K // 32 * 4
+    else:
+        eb = 2 if wl.idx_dtype == "bf16" else 1
+        key_b, q_b, new_key_b = K * eb, K * eb, K * eb * 2
     per_layer_attend = B * Qs * (k * (D // 2 + D // 32 * 4) + 2 * (Qs + W - 1) * D * 2 // Qs
                                  + Hq * D * 2 + Hq * D * 4 + Hq * 4)
-    scan = B * (N * K * eb + Qs * K * eb + Qs * N * 4)  # keys + index query + score write
-    select = B * Qs * k * 4                            # selection written
-    full_write = B * Qs * (D * 4 + D // 2 + D // 32 * 4 + K * eb * 2)
+    scan = B * (N * key_b + Qs * q_b + Qs * N * 4)  # keys + index query + score write
+    select = B * Qs * k * 4                         # selection written
+    full_write = B * Qs * (D * 4 + D // 2 + D // 32 * 4 + new_key_b)
     total = 0
     for mode in wl.pattern * wl.groups:
         total += per_layer_attend + B * Qs * k * 4  # every mode reads its selection
@@ -94,8 +98,13 @@ def run_gpu(wl, steps, warmup, device, scan_loop=True):
     groups = []
     for g in range(wl.groups):
         gc, gs = csa2.fp4_pack(_dev(inp.cache_x[g], device))
-        groups.append(csa2.Group(gc, gs, _dev(inp.ikeys[g], device), _dev(inp.n_valid, device),
-                                 wl.idx_dtype, wl.k, sel_rows=B * wl.Qs))
+        keys, kscales = _dev(inp.ikeys[g], device), None
+        if wl.idx_dtype == "fp4":
+            K = wl.H_I * wl.d_I
+            kc, kscales = csa2.fp4_pack(keys.reshape(B * N, K))
+            keys, kscales = kc.reshape(B, N, wl.H_I, wl.d_I // 2), kscales.reshape(B, N, K // 32)
+        groups.append(csa2.Group(gc, gs, keys, _dev(inp.n_valid, device), wl.idx_dtype, wl.k,
+                                 sel_rows=B * wl.Qs, ikey_scales=kscales))
     layers = []
     for L in inp.layers:
         d = {k: (_dev(v, device) if isinstance(v, np.ndarray) else v) for k, v in L.items()}
@@ -140,11 +149,11 @@ def run_gpu(wl, steps, warmup, device, scan_loop=True):
     scores = torch.empty(B, wl.Qs, N, dtype=torch.float32, device=device)
     reps = max(steps, 5)
     for _ in range(2):
-        csa2.index_score(first["iq"], grp.ikeys, wl.idx_dtype, out=scores)
+        csa2.index_score(first["iq"], grp.ikeys, wl.idx_dtype, out=scores, ik_scales=grp.ikey_scales)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(reps):
-        csa2.index_score(first["iq"], grp.ikeys, wl.idx_dtype, out=scores)
+        csa2.index_score(first["iq"], grp.ikeys, wl.idx_dtype, out=scores, ik_scales=grp.ikey_scales)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_scan = e0.elapsed_time(e1) / reps
@@ -287,6 +296,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-fp4-index", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -344,6 +354,17 @@ def main():
             "tokens_per_s": round(vw.B * vw.Qs / (ms_v * 1e-3), 1),
             "note": "draft block of 5 queries per sequence through the same 4-layer group; tokens/s "
                     "counts the 5 verified positions of each of the 32 sequences per step"}
+    if not args.no_fp4_index:
+        fw = ALL[7]
+        ms_f, ms_fscan, _, _ = run_gpu(fw, max(args.steps // 2, 3), 2, device)
+        _, f_scan_bytes = algorithmic_bytes(fw)
+        res["fp4_index"] = {
+            "workload": fw.name, "ms_per_step": round(ms_f, 4),
+            "tokens_per_s": round(fw.B * fw.Qs / (ms_f * 1e-3), 1),
+            "score_us": round(ms_fscan * 1e3, 2),
+            "score_GBps": round(f_scan_bytes / (ms_fscan * 1e-3) / 1e9, 1),
+            "note": "the w2 step with FP4 e2m1 index keys (fp32 block-32 scales, bf16 index queries); "
+                    "scores still exact"}
     if not args.no_prefill:
         pw = ALL[4]
         ms_chunk = run_prefill(pw, 5, 2, device)

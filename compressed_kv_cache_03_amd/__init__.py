@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_STATE, ERR_HIP = range(6)
 MODE = {"F": 0, "Ri": 1, "Ru": 2, "full": 0, "reindex": 1, "reuse": 2}
-IDX_DTYPE = {"bf16": 0, "e4m3": 1}
+IDX_DTYPE = {"bf16": 0, "e4m3": 1, "fp4": 2}
 
 vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
@@ -26,7 +26,8 @@ class CGroup(ctypes.Structure):
     _fields_ = [("B", i32), ("N_cap", i64), ("D", i32), ("H_I", i32), ("d_I", i32),
                 ("idx_dtype", ctypes.c_int), ("k", i32), ("codes", vp), ("scales", vp),
                 ("ikeys", vp), ("n_valid", vp), ("n_valid_max", i64), ("sel", vp),
-                ("sel_rows", i32), ("has_entries", i32), ("has_selection", i32), ("sel_qs", i32)]
+                ("sel_rows", i32), ("has_entries", i32), ("has_selection", i32), ("sel_qs", i32),
+                ("ikey_scales", vp)]
 
 
 class CLayerArgs(ctypes.Structure):
@@ -57,7 +58,7 @@ def _load():
     lib.csa2_version.argtypes = []
     lib.csa2_version.restype = ctypes.c_char_p
     lib.csa2_fp4_pack.argtypes = [vp, i64, i32, vp, vp, vp]
-    lib.csa2_index_score.argtypes = [vp, vp, ctypes.c_int, i32, i32, i64, i32, i32, vp, vp]
+    lib.csa2_index_score.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i64, i32, i32, vp, vp]
     lib.csa2_topk_workspace_bytes.argtypes = [i64, i64, i32]
     lib.csa2_topk_workspace_bytes.restype = sz
     lib.csa2_topk.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, sz, vp]
@@ -134,17 +135,22 @@ def fp4_pack(x: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.T
 
 
 def index_score(iq: torch.Tensor, ik: torch.Tensor, dtype: str, out: torch.Tensor | None = None,
-                stream=None) -> torch.Tensor:
+                stream=None, ik_scales: torch.Tensor | None = None) -> torch.Tensor:
     """iq [B, Qs, H, d] and ik [B, N, H, d] (uint8 for e4m3, int16/bf16/uint16 bits for bf16)
-    -> exact fp32 scores [B, Qs, N]."""
+    -> exact fp32 scores [B, Qs, N].  dtype 'fp4': iq bf16 bits, ik the e2m1 codes
+    [B, N, H, d/2] and ik_scales fp32 [B, N, H*d/32]."""
     _dev(iq, "iq")
     _dev(ik, "ik")
     B, Qs, H, d = iq.shape
     N = ik.shape[1]
+    if dtype == "fp4":
+        if ik_scales is None:
+            raise ValueError("fp4 index keys need ik_scales")
+        _dev(ik_scales, "ik_scales")
     if out is None:
         out = torch.empty(B, Qs, N, dtype=torch.float32, device=iq.device)
-    _check(_load().csa2_index_score(iq.data_ptr(), ik.data_ptr(), IDX_DTYPE[dtype], B, Qs, N, H, d,
-                                    out.data_ptr(), _stream(stream)), "csa2_index_score")
+    _check(_load().csa2_index_score(iq.data_ptr(), ik.data_ptr(), _ptr(ik_scales), IDX_DTYPE[dtype], B, Qs,
+                                    N, H, d, out.data_ptr(), _stream(stream)), "csa2_index_score")
     return out
 
 
@@ -198,17 +204,26 @@ class Group:
 
     def __init__(self, codes: torch.Tensor, scales: torch.Tensor, ikeys: torch.Tensor,
                  n_valid: torch.Tensor, idx_dtype: str, k: int, sel_rows: int,
-                 n_valid_max: int | None = None, has_entries: bool = True):
+                 n_valid_max: int | None = None, has_entries: bool = True,
+                 ikey_scales: torch.Tensor | None = None):
+        """ikeys [B, N_cap, H_I, d_I] in idx_dtype; for 'fp4' the e2m1 codes
+        [B, N_cap, H_I, d_I/2] and ikey_scales fp32 [B, N_cap, H_I*d_I/32]."""
         for name, t in (("codes", codes), ("scales", scales), ("ikeys", ikeys), ("n_valid", n_valid)):
             _dev(t, name)
         B, N_cap, H_I, d_I = ikeys.shape
+        if idx_dtype == "fp4":
+            if ikey_scales is None:
+                raise ValueError("fp4 index keys need ikey_scales")
+            _dev(ikey_scales, "ikey_scales")
+            d_I *= 2
+        self.ikey_scales = ikey_scales
         self.codes, self.scales, self.ikeys = codes, scales, ikeys
         self.n_valid = n_valid.to(torch.int32)
         self.sel = torch.full((sel_rows, k), -1, dtype=torch.int32, device=codes.device)
         nvm = int(self.n_valid.max().item()) if n_valid_max is None else int(n_valid_max)
         self.c = CGroup(B, N_cap, codes.shape[-1] * 2, H_I, d_I, IDX_DTYPE[idx_dtype], k,
                         codes.data_ptr(), scales.data_ptr(), ikeys.data_ptr(), self.n_valid.data_ptr(),
-                        nvm, self.sel.data_ptr(), sel_rows, int(has_entries), 0, 0)
+                        nvm, self.sel.data_ptr(), sel_rows, int(has_entries), 0, 0, _ptr(ikey_scales))
         self._ws = None
 
     @property

@@ -24,7 +24,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int idx_elem_bytes(csa2_idx_dtype dt) { return dt == CSA2_IDX_BF16 ? 2 : 1; }
+// bytes per stored index-key element row of K elements (FP4: codes only)
+size_t key_row_bytes(csa2_idx_dtype dt, int K) {
+    return dt == CSA2_IDX_BF16 ? (size_t)K * 2 : dt == CSA2_IDX_FP8_E4M3 ? (size_t)K : (size_t)K / 2;
+}
+int query_elem_bytes(csa2_idx_dtype dt) { return dt == CSA2_IDX_FP8_E4M3 ? 1 : 2; }
+int score_dtype(csa2_idx_dtype dt) { return dt == CSA2_IDX_BF16 ? 0 : dt == CSA2_IDX_FP8_E4M3 ? 1 : 2; }
 
 // Workspace carve-up shared by all entry points.  Offsets are 256-byte aligned.
 struct Layout {
@@ -119,6 +124,7 @@ bool valid_dim(int32_t D) { return D >= 32 && D <= 256 && D % 32 == 0; }
 bool valid_index_width(csa2_idx_dtype dt, int32_t H, int32_t d) {
     if (H < 1 || d < 1) return false;
     const int64_t K = (int64_t)H * d;
+    if (dt == CSA2_IDX_FP4_E2M1) return K <= 4096 && K % 32 == 0;
     return K <= 4096 && K % 16 == 0 && (dt == CSA2_IDX_BF16 || dt == CSA2_IDX_FP8_E4M3);
 }
 
@@ -129,7 +135,8 @@ bool valid_index_width(csa2_idx_dtype dt, int32_t H, int32_t d) {
 struct ImageParts {
     int64_t n = 0;
     size_t code_row = 0, scale_row = 0, key_row = 0;  // bytes per entry
-    size_t codes = 0, scales = 0, keys = 0, sel = 0, total = 0;
+    size_t kscale_row = 0;                            // FP4 index keys only
+    size_t codes = 0, scales = 0, keys = 0, kscales = 0, sel = 0, total = 0;
 };
 
 bool image_parts(const csa2_group* g, ImageParts* p) {
@@ -140,12 +147,14 @@ bool image_parts(const csa2_group* g, ImageParts* p) {
     p->n = g->n_valid_max;
     p->code_row = (size_t)g->D / 2;
     p->scale_row = (size_t)g->D / 32 * 4;
-    p->key_row = (size_t)g->H_I * g->d_I * idx_elem_bytes(g->idx_dtype);
+    p->key_row = key_row_bytes(g->idx_dtype, g->H_I * g->d_I);
+    p->kscale_row = g->idx_dtype == CSA2_IDX_FP4_E2M1 ? (size_t)g->H_I * g->d_I / 32 * 4 : 0;
+    p->kscales = (size_t)g->B * p->n * p->kscale_row;
     p->codes = (size_t)g->B * p->n * p->code_row;
     p->scales = (size_t)g->B * p->n * p->scale_row;
     p->keys = (size_t)g->B * p->n * p->key_row;
     p->sel = g->has_selection ? (size_t)g->B * g->sel_qs * g->k * 4 : 0;
-    p->total = p->codes + p->scales + p->keys + p->sel;
+    p->total = p->codes + p->scales + p->keys + p->kscales + p->sel;
     return true;
 }
 
@@ -194,20 +203,23 @@ csa2_status csa2_fp4_pack(const float* x, int64_t rows, int32_t dim, uint8_t* co
                                       static_cast<hipStream_t>(stream)));
 }
 
-csa2_status csa2_index_score(const void* iq, const void* ik, csa2_idx_dtype dtype, int32_t B,
-                             int32_t Qs, int64_t N, int32_t H, int32_t d, float* scores,
-                             void* stream) {
+csa2_status csa2_index_score(const void* iq, const void* ik, const float* ik_scales,
+                             csa2_idx_dtype dtype, int32_t B, int32_t Qs, int64_t N, int32_t H,
+                             int32_t d, float* scores, void* stream) {
     if (B < 0 || Qs < 1 || N < 0) return CSA2_ERR_INVALID_ARG;
     if (!valid_index_width(dtype, H, d)) return CSA2_ERR_INVALID_ARG;
     if (N >= (int64_t)1 << 31) return CSA2_ERR_UNSUPPORTED;
     if (B == 0 || N == 0) return CSA2_OK;
-    if (!iq || !ik || !scores) return CSA2_ERR_INVALID_ARG;
-    if (!aligned(iq, 16) || !aligned(ik, 16) || !aligned(scores, 4)) return CSA2_ERR_INVALID_ARG;
+    if (!iq || !ik || !scores || (dtype == CSA2_IDX_FP4_E2M1 && !ik_scales)) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(iq, 16) || !aligned(ik, 16) || !aligned(scores, 4) ||
+        (dtype == CSA2_IDX_FP4_E2M1 && !aligned(ik_scales, 4)))
+        return CSA2_ERR_INVALID_ARG;
     if ((int64_t)B * Qs > 65535) return CSA2_ERR_UNSUPPORTED;  // grid.y
     ScoreArgs a{};
     a.iq = iq;
     a.ik = ik;
-    a.dtype = dtype == CSA2_IDX_BF16 ? 0 : 1;
+    a.ik_scales = dtype == CSA2_IDX_FP4_E2M1 ? ik_scales : nullptr;
+    a.dtype = score_dtype(dtype);
     a.K = H * d;
     a.B = B;
     a.Qs = Qs;
@@ -332,6 +344,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
     if (!aligned(g->codes, 16) || !aligned(g->scales, 16) || !aligned(g->ikeys, 16) ||
         !aligned(g->sel, 4) || !aligned(g->n_valid, 4))
         return CSA2_ERR_INVALID_ARG;
+    if (g->idx_dtype == CSA2_IDX_FP4_E2M1 && (!g->ikey_scales || !aligned(g->ikey_scales, 16)))
+        return CSA2_ERR_INVALID_ARG;
     // layer arguments
     const int Qs = a->Qs;
     if (Qs < 1 || a->Hq < 1 || a->Hq > 32 || a->W < 0 || a->W > 1024 || !std::isfinite(a->sm_scale))
@@ -346,7 +360,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
     const bool selects = mode != CSA2_MODE_REUSE;
     if (selects && (!a->iq || !aligned(a->iq, 16))) return CSA2_ERR_INVALID_ARG;
     if (mode == CSA2_MODE_FULL &&
-        (!a->new_entry || !a->new_ikey || !aligned(a->new_entry, 16) || !aligned(a->new_ikey, 4)))
+        (!a->new_entry || !a->new_ikey || !aligned(a->new_entry, 16) ||
+         !aligned(a->new_ikey, g->idx_dtype == CSA2_IDX_FP4_E2M1 ? 16 : 4)))
         return CSA2_ERR_INVALID_ARG;
     // group state
     if (mode == CSA2_MODE_REINDEX && !g->has_entries) return CSA2_ERR_STATE;
@@ -364,8 +379,12 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         // S1: the step's new rows go to slots n_valid-Qs .. n_valid-1
         e = launch_fp4_pack(a->new_entry, R, g->D, g->codes, g->scales, g->n_valid, Qs, g->N_cap, s);
         if (e == hipSuccess)
-            e = launch_store_rows(a->new_ikey, R, K * idx_elem_bytes(g->idx_dtype), g->ikeys,
-                                  g->n_valid, Qs, g->N_cap, s);
+            e = g->idx_dtype == CSA2_IDX_FP4_E2M1
+                    ? launch_fp4_pack(static_cast<const float*>(a->new_ikey), R, K,
+                                      static_cast<uint8_t*>(g->ikeys), g->ikey_scales, g->n_valid, Qs,
+                                      g->N_cap, s)
+                    : launch_store_rows(a->new_ikey, R, (int)key_row_bytes(g->idx_dtype, K), g->ikeys,
+                                        g->n_valid, Qs, g->N_cap, s);
     }
     if (e == hipSuccess && selects && mfma_prefill(g, Qs)) {
         // S2 + S3 for a prefill chunk: sampled thresholds, MFMA score GEMM with a
@@ -448,7 +467,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         ScoreArgs sa{};
         sa.iq = a->iq;
         sa.ik = g->ikeys;
-        sa.dtype = g->idx_dtype == CSA2_IDX_BF16 ? 0 : 1;
+        sa.dtype = score_dtype(g->idx_dtype);
+        sa.ik_scales = g->ikey_scales;
         sa.K = K;
         sa.B = g->B;
         sa.Qs = Qs;
@@ -501,7 +521,8 @@ size_t csa2_group_image_bytes(const csa2_group* g) {
 
 csa2_status csa2_group_save(const csa2_group* g, void* host, size_t bytes, void* stream) {
     ImageParts p;
-    if (!image_parts(g, &p) || !host || !g->codes || !g->scales || !g->ikeys || (p.sel && !g->sel))
+    if (!image_parts(g, &p) || !host || !g->codes || !g->scales || !g->ikeys || (p.sel && !g->sel) ||
+        (p.kscales && !g->ikey_scales))
         return CSA2_ERR_INVALID_ARG;
     if (!g->has_entries) return CSA2_ERR_STATE;
     if (bytes < p.total) return CSA2_ERR_WORKSPACE;
@@ -516,14 +537,18 @@ csa2_status csa2_group_save(const csa2_group* g, void* host, size_t bytes, void*
     if (e == hipSuccess)
         e = copy_rows(h + p.codes + p.scales, n * p.key_row, g->ikeys, N * p.key_row, n * p.key_row, B,
                       hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && p.kscales)
+        e = copy_rows(h + p.codes + p.scales + p.keys, n * p.kscale_row, g->ikey_scales, N * p.kscale_row,
+                      n * p.kscale_row, B, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess && p.sel)
-        e = hipMemcpyAsync(h + p.codes + p.scales + p.keys, g->sel, p.sel, hipMemcpyDeviceToHost, s);
+        e = hipMemcpyAsync(h + p.codes + p.scales + p.keys + p.kscales, g->sel, p.sel, hipMemcpyDeviceToHost, s);
     return hip_status(e);
 }
 
 csa2_status csa2_group_restore(csa2_group* g, const void* host, size_t bytes, void* stream) {
     ImageParts p;
-    if (!image_parts(g, &p) || !host || !g->codes || !g->scales || !g->ikeys || (p.sel && !g->sel))
+    if (!image_parts(g, &p) || !host || !g->codes || !g->scales || !g->ikeys || (p.sel && !g->sel) ||
+        (p.kscales && !g->ikey_scales))
         return CSA2_ERR_INVALID_ARG;
     if (bytes < p.total) return CSA2_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -537,8 +562,11 @@ csa2_status csa2_group_restore(csa2_group* g, const void* host, size_t bytes, vo
     if (e == hipSuccess)
         e = copy_rows(g->ikeys, N * p.key_row, h + p.codes + p.scales, n * p.key_row, n * p.key_row, B,
                       hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && p.kscales)
+        e = copy_rows(g->ikey_scales, N * p.kscale_row, h + p.codes + p.scales + p.keys, n * p.kscale_row,
+                      n * p.kscale_row, B, hipMemcpyHostToDevice, s);
     if (e == hipSuccess && p.sel)
-        e = hipMemcpyAsync(g->sel, h + p.codes + p.scales + p.keys, p.sel, hipMemcpyHostToDevice, s);
+        e = hipMemcpyAsync(g->sel, h + p.codes + p.scales + p.keys + p.kscales, p.sel, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return CSA2_ERR_HIP;
     g->has_entries = 1;
     return CSA2_OK;

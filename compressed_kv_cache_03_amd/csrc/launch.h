@@ -28,8 +28,9 @@ hipError_t launch_store_rows(const void* src, int64_t rows, int row_bytes, void*
 // every written score into hist[r*4096 + digit].
 struct ScoreArgs {
     const void* iq;       // [R][K]
-    const void* ik;       // [B][N_cap][K]
-    int dtype;            // 0 bf16, 1 e4m3
+    const void* ik;       // [B][N_cap][K] (dtype 2: e2m1 codes [B][N_cap][K/2])
+    const float* ik_scales;  // dtype 2: [B][N_cap][K/32]
+    int dtype;            // 0 bf16, 1 e4m3, 2 FP4 e2m1 keys with bf16 queries
     int K;                // H*d
     int B, Qs;
     int64_t N;            // entries to consider per sequence (<= N_cap)

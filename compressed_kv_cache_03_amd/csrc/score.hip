@@ -31,7 +31,18 @@
 //     certificate (error <= gamma_(K-1) sum|p| for any order; both ends of
 //     [s - bound, s + bound] must round to the same fp32), and when both fail
 //     (a tie together with a > 53-bit exponent spread) the entry is recomputed
-//     with exact_bf16_dot, an integer long accumulator.
+//     with an integer long accumulator.
+//   * FP4 keys (e2m1 code times an fp32 scale per 32-element block, bf16
+//     queries): each lane sums its block's 32 products q * e2m1 in fp64, exact
+//     whenever the query block's exponent spread allows (a per-row property
+//     decided once per lane, else bounded by gamma_32 * 6 * sum|q|), then adds
+//     block sum * scale with one fma.  The rounding of those fmas and of the
+//     butterfly is bounded by (CPL + 3) * 2^-53 * sum |block sum * scale|, and
+//     both ends of the resulting interval must round to the same fp32.
+//   * The rare entries the certificate cannot decide are recomputed by the
+//     whole wave at once: each lane accumulates K/64 exact products into its
+//     own 640-bit integer accumulator, the accumulators are summed across the
+//     wave, and the total is rounded once.
 #include "common.h"
 #include "launch.h"
 
@@ -62,6 +73,8 @@ CSA2_DEV int64_t row_valid(const ScoreArgs& a, int64_t r) {
 // Exponent of the least significant bit of any bf16 value whose magnitude is at
 // least x (x given as fp32): a bf16 value is M * 2^(E-134), M an integer, E the
 // exponent field (taken as 1 for zero and subnormals).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 CSA2_DEV int bf16_lsb_exp(float x) {
     const int e = (int)(__float_as_uint(x) >> 23) & 0xff;
     return (e > 0 ? e : 1) - 134;
@@ -85,25 +98,9 @@ CSA2_DEV bool sum_is_exact(double sumabs, int L) {
 // routine lives in registers and the streaming kernel needs no scratch memory.
 constexpr int kFixDigits = 20;  // 640 bits: products reach bit 522, sums add 12
 
-CSA2_DEV float exact_bf16_dot(const uint16_t* q, const uint16_t* k, int K) {
-    int64_t d[kFixDigits];
-#pragma unroll
-    for (int j = 0; j < kFixDigits; ++j) d[j] = 0;
-    for (int i = 0; i < K; ++i) {
-        const uint32_t x = q[i], y = k[i];
-        const uint32_t ex = (x >> 7) & 0xff, ey = (y >> 7) & 0xff;
-        const uint32_t mx = (x & 0x7f) | (ex ? 0x80u : 0u), my = (y & 0x7f) | (ey ? 0x80u : 0u);
-        const int pos = (int)(ex ? ex : 1) + (int)(ey ? ey : 1) - 2;
-        const uint64_t v = (uint64_t)(mx * my) << (pos & 31);
-        const int li = pos >> 5;
-        int64_t lo = (int64_t)(v & 0xffffffffu), hi = (int64_t)(v >> 32);
-        if ((x ^ y) & 0x8000u) {
-            lo = -lo;
-            hi = -hi;
-        }
-#pragma unroll
-        for (int j = 0; j < kFixDigits; ++j) d[j] += (j == li ? lo : 0) + (j == li + 1 ? hi : 0);
-    }
+// Settle the carries of a digit accumulator whose bit 0 weighs 2^lsb0 and
+// round its value to fp32 (nearest even; an exact zero is +0).
+CSA2_DEV float fix_to_f32(int64_t (&d)[kFixDigits], int lsb0) {
     // settle carries (arithmetic shift = floor division by 2^32); the top digit
     // then carries the sign
 #pragma unroll
@@ -138,7 +135,7 @@ CSA2_DEV float exact_bf16_dot(const uint16_t* q, const uint16_t* k, int K) {
     }
     // X holds digits ti and ti-1; its bit 0 weighs 2^base
     const uint64_t X = (top << 32) | mid;
-    const int base = 32 * (ti - 1) - 266;
+    const int base = 32 * (ti - 1) + lsb0;
     const int qbit = 63 - __builtin_clzll(X);  // >= 32: digit ti is nonzero
     int lsb_exp = qbit + base - 23;              // fp32 keeps 24 bits ...
     if (lsb_exp < -149) lsb_exp = -149;          // ... none below 2^-149
@@ -151,11 +148,135 @@ CSA2_DEV float exact_bf16_dot(const uint16_t* q, const uint16_t* k, int K) {
     return neg ? -res : res;
 }
 
-// DT: 0 = bf16, 1 = e4m3.  CPL: 16-byte chunks per lane per entry, so an entry
-// is 128*CPL bytes (bf16: K = 64*CPL, e4m3: K = 128*CPL).
+// Adds the exact product of bf16 values x and y to the digit accumulator.
+CSA2_DEV void bf16_accum(int64_t (&d)[kFixDigits], uint32_t x, uint32_t y) {
+    const uint32_t ex = (x >> 7) & 0xff, ey = (y >> 7) & 0xff;
+    const uint32_t mx = (x & 0x7f) | (ex ? 0x80u : 0u), my = (y & 0x7f) | (ey ? 0x80u : 0u);
+    const int pos = (int)(ex ? ex : 1) + (int)(ey ? ey : 1) - 2;
+    const uint64_t v = (uint64_t)(mx * my) << (pos & 31);
+    const int li = pos >> 5;
+    int64_t lo = (int64_t)(v & 0xffffffffu), hi = (int64_t)(v >> 32);
+    if ((x ^ y) & 0x8000u) {
+        lo = -lo;
+        hi = -hi;
+    }
+#pragma unroll
+    for (int j = 0; j < kFixDigits; ++j) d[j] += (j == li ? lo : 0) + (j == li + 1 ? hi : 0);
+}
+
+// Sums every lane's digit accumulator into all lanes of the wave.  Each lane's
+// digits stay below 2^32 * (K/64 + 3) in magnitude, so the sum of 64 of them
+// fits an int64 digit.
+CSA2_DEV void wave_sum_digits(int64_t (&d)[kFixDigits]) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+#pragma unroll
+        for (int j = 0; j < kFixDigits; ++j) d[j] += __shfl_xor((long)d[j], m);
+    }
+}
+
+CSA2_DEV float exact_bf16_dot(const uint16_t* q, const uint16_t* k, int K) {
+    int64_t d[kFixDigits];
+#pragma unroll
+    for (int j = 0; j < kFixDigits; ++j) d[j] = 0;
+    for (int i = 0; i < K; ++i) bf16_accum(d, q[i], k[i]);
+    return fix_to_f32(d, -266);
+}
+
+// exact_bf16_dot computed by a whole wave (all 64 lanes active, same arguments
+// in every lane): lane l takes elements l, l+64, ...; every lane returns the
+// result.
+CSA2_DEV float wave_exact_bf16_dot(const uint16_t* q, const uint16_t* k, int K, int lane) {
+    int64_t d[kFixDigits];
+#pragma unroll
+    for (int j = 0; j < kFixDigits; ++j) d[j] = 0;
+    for (int i = lane; i < K; i += 64) bf16_accum(d, q[i], k[i]);
+    wave_sum_digits(d);
+    return fix_to_f32(d, -266);
+}
+
+// Exact fp32 (RNE) of sum_i q[i] * v[i] for bf16 q and FP4 keys, v[i] = the e2m1
+// value of code i times the fp32 scale of its 32-element block.  With
+// q = Mq 2^(Eq-134), |e2m1| = Mc 2^Ec (Mc in {0, 1, 3}, Ec in -1..2) and
+// scale = Ms 2^(Es-150), a product is Mq*Mc*Ms 2^(Eq+Ec+Es-284) with
+// Mq*Mc*Ms < 2^34: an integer multiple of 2^-288 placed at bit Eq+Ec+Es+4.  Same
+// 640-bit accumulator and final rounding as exact_bf16_dot.
+// Adds the exact product of bf16 x, e2m1 code nib and fp32 scale bits sb.
+CSA2_DEV void fp4_accum(int64_t (&d)[kFixDigits], uint32_t x, uint32_t nib, uint32_t sb) {
+    const uint32_t ex = (x >> 7) & 0xff, es = (sb >> 23) & 0xff, cm = nib & 7u;
+    const uint32_t mx = (x & 0x7f) | (ex ? 0x80u : 0u);
+    const uint32_t ms = (sb & 0x7fffffu) | (es ? 0x800000u : 0u);
+    // e2m1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 as Mc * 2^Ec (Ec + 1 stored)
+    const uint32_t mc = cm == 0 ? 0u : ((cm & 1u) && cm > 1 ? 3u : 1u);
+    const int ec1 = cm < 2 ? 0 : (int)(cm >> 1) - (int)(cm & 1u);  // Ec + 1
+    const uint64_t M = (uint64_t)(mx * mc) * ms;
+    if (M == 0) return;
+    const int pos = (int)(ex ? ex : 1) + ec1 + (int)(es ? es : 1) + 3;
+    const unsigned __int128 v = (unsigned __int128)M << (pos & 31);
+    int64_t d0 = (int64_t)(uint64_t)(v & 0xffffffffu), d1 = (int64_t)(uint64_t)((v >> 32) & 0xffffffffu),
+            d2 = (int64_t)(uint64_t)(v >> 64);
+    if (((x >> 15) ^ (nib >> 3) ^ (sb >> 31)) & 1u) {
+        d0 = -d0;
+        d1 = -d1;
+        d2 = -d2;
+    }
+    const int li = pos >> 5;
+#pragma unroll
+    for (int j = 0; j < kFixDigits; ++j)
+        d[j] += (j == li ? d0 : 0) + (j == li + 1 ? d1 : 0) + (j == li + 2 ? d2 : 0);
+}
+
+CSA2_DEV float exact_fp4_dot(const uint16_t* q, const uint8_t* codes, const float* scales, int K) {
+    int64_t d[kFixDigits];
+#pragma unroll
+    for (int j = 0; j < kFixDigits; ++j) d[j] = 0;
+    for (int i = 0; i < K; ++i)
+        fp4_accum(d, q[i], (codes[i >> 1] >> (4 * (i & 1))) & 15u, __float_as_uint(scales[i >> 5]));
+    return fix_to_f32(d, -288);
+}
+
+// exact_fp4_dot computed by a whole wave, as wave_exact_bf16_dot.
+CSA2_DEV float wave_exact_fp4_dot(const uint16_t* q, const uint8_t* codes, const float* scales, int K,
+                                  int lane) {
+    int64_t d[kFixDigits];
+#pragma unroll
+    for (int j = 0; j < kFixDigits; ++j) d[j] = 0;
+    for (int i = lane; i < K; i += 64)
+        fp4_accum(d, q[i], (codes[i >> 1] >> (4 * (i & 1))) & 15u, __float_as_uint(scales[i >> 5]));
+    wave_sum_digits(d);
+    return fix_to_f32(d, -288);
+}
+
+// Bound on the error of a block sum of 32 products q * e2m1 accumulated with fp64
+// FMAs: zero when the sum is provably exact, else gamma_32 * 6 * sum|q|.  Every
+// product is a multiple of 2^(emin - 135) (bf16 lsb 2^(E-134), e2m1 lsb 2^-1), so
+// if 6 * sum|q| < 2^(emin - 135 + 53) each partial sum is representable.  emin is
+// the smallest exponent field (1 for subnormals) over the block's nonzero q;
+// emin > 255 means every q is zero.
+CSA2_DEV double fp4_block_err(double qn1, int emin) {
+    if (emin > 255 || 6.0 * qn1 * (1.0 + 0x1p-40) < ldexp(1.0, emin - 135 + 53)) return 0.0;
+    return 32.0 * 0x1p-53 * 1.001 * 6.0 * qn1;
+}
+
+// Smallest exponent field of the nonzero bf16 values packed in w (1 for
+// subnormals, 1 << 20 when both are zero).
+CSA2_DEV int bf16_pair_emin(uint32_t w) {
+    const uint32_t lo = w & 0xffffu, hi = w >> 16;
+    const int elo = (lo & 0x7fffu) ? max((int)((lo >> 7) & 0xff), 1) : (1 << 20);
+    const int ehi = (hi & 0x7fffu) ? max((int)((hi >> 7) & 0xff), 1) : (1 << 20);
+    return min(elo, ehi);
+}
+
+
+// DT: 0 = bf16, 1 = e4m3, 2 = FP4 e2m1 codes with fp32 block-32 scales (bf16
+// queries).  CPL: 16-byte chunks per lane per entry, so an entry is 128*CPL
+// bytes (bf16: K = 64*CPL, e4m3: K = 128*CPL, FP4: K = 256*CPL, one scale block
+// per chunk).
+// FP4 keys with K = 256 are held to 128 registers (4 waves per SIMD); only the
+// rare exact-recompute path spills.
 template <int DT, int CPL>
-__global__ __launch_bounds__(kScoreThreads) void score_exact_kernel(ScoreArgs a) {
-    constexpr int EPC = DT == 0 ? 8 : 16;  // elements per 16-byte chunk
+__global__ __launch_bounds__(kScoreThreads, DT == 2 && CPL == 1 ? 4 : 1) void score_exact_kernel(ScoreArgs a) {
+    constexpr int EPC = DT == 0 ? 8 : DT == 1 ? 16 : 32;  // key elements per 16-byte chunk
     constexpr int EB = 128 * CPL;         // bytes per entry
     int64_t r, e_block;
     if (a.Qs == 1) {
@@ -186,7 +307,29 @@ __global__ __launch_bounds__(kScoreThreads) void score_exact_kernel(ScoreArgs a)
 
     // this lane's slice of the index query, as fp64
     double qd[CPL * EPC];
-    {
+    double berr[DT == 2 ? CPL : 1];  // FP4 keys: error bound of each chunk's block sum
+    constexpr double kBlkRound = (CPL + 3) * 0x1p-53 * 1.001;
+    if constexpr (DT == 2) {
+        // bf16 queries against 32-element key chunks: 64 query bytes per chunk
+        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.iq) + r * (int64_t)(4 * EB);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            double qn1 = 0.0;
+            int emin = 1 << 20;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + c * 512 + sub * 64 + v * 16);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    qd[c * EPC + 8 * v + 2 * t] = bf16_lo(w[t]);
+                    qd[c * EPC + 8 * v + 2 * t + 1] = bf16_hi(w[t]);
+                    qn1 += fabs(qd[c * EPC + 8 * v + 2 * t]) + fabs(qd[c * EPC + 8 * v + 2 * t + 1]);
+                    emin = min(emin, bf16_pair_emin(w[t]));
+                }
+            }
+            berr[c] = fp4_block_err(qn1, emin);
+        }
+    } else {
         const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.iq) + r * (int64_t)EB;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
@@ -208,7 +351,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_exact_kernel(ScoreArgs a)
         }
     }
     // |s_fp64 - s| <= gamma_(K-1) * sum|p| (any summation order), and the fp64
-    // accumulation of sum|p| itself is low by at most a factor (1 - K*2^-53).
+    // accumulation of sum|p| itself is low by at most a factor (1 - K*2^-53)
     const double bound_scale = (double)a.K * 0x1p-53 * 1.001 * (1.0 + (double)a.K * 0x1p-52);
     // least significant bit exponent of the smallest |q| of the row (bf16 values are
     // M * 2^(E-134) with integer M; a zero or subnormal gives the floor E = 1)
@@ -231,23 +374,41 @@ __global__ __launch_bounds__(kScoreThreads) void score_exact_kernel(ScoreArgs a)
         if (e_wave >= nv) break;  // wave-uniform
         double keep = 0.0, keep_abs = 0.0;
         uint32_t keep_ex = 0;
-#pragma unroll 2
-        for (int t = 0; t < kScoreRounds; ++t) {
-            const int64_t e = e_wave + t * 8 + g;
-            u32x4 w[CPL];
-            if (e < nv) {
-                const uint8_t* src = kbase + e * EB + sub * 16;
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
-                    w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
-            } else {
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) w[c] = u32x4{0u, 0u, 0u, 0u};
-            }
-            double acc = 0.0, aacc = 0.0;
+        // one round: 8 entries, 8 lanes each; lane sub == t keeps entry e_wave + 8t + g
+        auto round_body = [&](int t, const u32x4(&w)[CPL], const float(&ksc)[DT == 2 ? CPL : 1])
+                              __attribute__((always_inline)) {
+            double acc = 0.0, aacc = 0.0;  // FP4 keys: aacc is the error bound of acc
             uint32_t kex = 0x7fff7fffu;  // packed minimum of the two bf16 exponent fields
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
+                if constexpr (DT == 2) {
+                    // the chunk is one scale block: exact e2m1 values (scale 1) into an
+                    // fp64 block sum, then one fma with the block scale
+                    double blk = 0.0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t cw = w[c][u];
+                        const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
+                        const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
+                        const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
+                        const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
+                        const double* qq = qd + c * EPC + 8 * u;
+                        blk = fma(qq[0], (double)v0[0], blk);
+                        blk = fma(qq[1], (double)v0[1], blk);
+                        blk = fma(qq[2], (double)v1[0], blk);
+                        blk = fma(qq[3], (double)v1[1], blk);
+                        blk = fma(qq[4], (double)v2[0], blk);
+                        blk = fma(qq[5], (double)v2[1], blk);
+                        blk = fma(qq[6], (double)v3[0], blk);
+                        blk = fma(qq[7], (double)v3[1], blk);
+                    }
+                    // CPL fmas here and 3 butterfly adds each round once, relative to
+                    // partial sums bounded by sum |blk * scale|
+                    const double sd = (double)ksc[c];
+                    acc = fma(blk, sd, acc);
+                    aacc = fma(fma(kBlkRound, fabs(blk), berr[c]), fabs(sd), aacc);
+                    continue;
+                }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     if (DT == 0) {
@@ -271,10 +432,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_exact_kernel(ScoreArgs a)
             acc += swz_xor<1>(acc);
             acc += swz_xor<2>(acc);
             acc += swz_xor<4>(acc);
-            if (DT == 0) {
+            if (DT != 1) {
                 aacc += swz_xor<1>(aacc);
                 aacc += swz_xor<2>(aacc);
                 aacc += swz_xor<4>(aacc);
+            }
+            if (DT == 0) {
                 kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (1 << 10) | 0x1f));
                 kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (2 << 10) | 0x1f));
                 kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (4 << 10) | 0x1f));
@@ -284,13 +447,57 @@ __global__ __launch_bounds__(kScoreThreads) void score_exact_kernel(ScoreArgs a)
                 keep_abs = aacc;
                 keep_ex = kex;
             }
+        };
+        if constexpr (DT == 2) {
+            // FP4 rows are short (128 bytes per 256 elements): keys are loaded kPD
+            // rounds ahead of their use from a ring of kPD + 1 round buffers, so
+            // enough bytes are in flight per wave.  Entries past nv load entry
+            // nv - 1 (in bounds) and are never stored.
+            constexpr int kPD = 2;
+            u32x4 wr[kPD + 1][CPL];
+            float kr[kPD + 1][CPL];
+            auto load_round = [&](int t, u32x4(&w)[CPL], float(&ks)[CPL]) __attribute__((always_inline)) {
+                int64_t e = e_wave + t * 8 + g;
+                e = e < nv ? e : nv - 1;
+                const uint8_t* src = kbase + e * EB + sub * 16;
+                const float* sp = a.ik_scales + (b * a.N_cap + e) * (int64_t)(a.K / 32) + sub;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
+                    ks[c] = __builtin_nontemporal_load(sp + 8 * c);
+                }
+            };
+#pragma unroll
+            for (int t = 0; t < kPD; ++t) load_round(t, wr[t], kr[t]);
+#pragma unroll
+            for (int t = 0; t < kScoreRounds; ++t) {
+                if (t + kPD < kScoreRounds) load_round(t + kPD, wr[(t + kPD) % (kPD + 1)], kr[(t + kPD) % (kPD + 1)]);
+                round_body(t, wr[t % (kPD + 1)], kr[t % (kPD + 1)]);
+            }
+        } else {
+#pragma unroll 2
+            for (int t = 0; t < kScoreRounds; ++t) {
+                const int64_t e = e_wave + t * 8 + g;
+                u32x4 w[CPL];
+                const float ksc[1] = {0.0f};
+                if (e < nv) {
+                    const uint8_t* src = kbase + e * EB + sub * 16;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c)
+                        w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) w[c] = u32x4{0u, 0u, 0u, 0u};
+                }
+                round_body(t, w, ksc);
+            }
         }
 
         // lane (g, sub) now owns entry e_wave + 8*sub + g
         const int64_t e = e_wave + 8 * sub + g;
+        float res = 0.0f;
+        bool ok = true;
         if (e < nv) {
-            float res;
-            bool ok = true;
             if (DT == 0) {
                 res = (float)keep;
                 // smallest exponent field among the entry's elements (0 = zero or subnormal)
@@ -302,12 +509,37 @@ __global__ __launch_bounds__(kScoreThreads) void score_exact_kernel(ScoreArgs a)
                     ok = __float_as_uint(lo) == __float_as_uint(hi);
                     res = lo;
                 }
+            } else if (DT == 2) {
+                // keep_abs bounds every rounding of the entry; |keep| * 2^-52 covers the
+                // two interval ends' own rounding
+                const double eb = (keep_abs + fabs(keep) * 0x1p-52) * (1.0 + 0x1p-40);
+                const float lo = (float)(keep - eb), hi = (float)(keep + eb);
+                ok = __float_as_uint(lo) == __float_as_uint(hi);
+                res = lo;
             } else {
                 res = (float)keep;
             }
-            if (!ok)
-                res = exact_bf16_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * a.K,
-                                     reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + e) * a.K, a.K);
+        }
+        if (DT != 1) {
+            // entries the certificate could not decide: the whole wave computes
+            // each one exactly with the integer accumulator
+            uint64_t pend = __ballot(!ok);
+            while (pend) {
+                const int L = __builtin_ctzll(pend);
+                pend &= pend - 1;
+                const int64_t eL = __builtin_amdgcn_readlane((int)e, L);
+                const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.iq) + r * a.K;
+                float x;
+                if (DT == 2)
+                    x = wave_exact_fp4_dot(qp, reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + eL) * (a.K / 2),
+                                           a.ik_scales + (b * a.N_cap + eL) * (a.K / 32), a.K, lane);
+                else
+                    x = wave_exact_bf16_dot(qp, reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + eL) * a.K,
+                                            a.K, lane);
+                if (lane == L) res = x;
+            }
+        }
+        if (e < nv) {
             a.scores[r * a.ld + e] = res;
             if (with_hist) atomicAdd(&lhist[sort_key(res) >> (32 - kHistBits)], 1u);
         }
@@ -343,6 +575,27 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
             qmin = fminf(qmin, fabsf(qf));
             kmin = fminf(kmin, fabsf(kf));
         }
+    } else if (a.dtype == 2) {
+        // FP4 keys: per 32-element block an fp64 sum of q * e2m1 with its error
+        // bound, then one fma with the block scale; aacc bounds every rounding
+        const uint16_t* q = reinterpret_cast<const uint16_t*>(a.iq) + r * K;
+        const uint8_t* k = reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * (K / 2);
+        const float* sc = a.ik_scales + (b * a.N_cap + e) * (K / 32);
+        for (int blk0 = 0; blk0 < K; blk0 += 32) {
+            double blk = 0.0, qn1 = 0.0;
+            int emin = 1 << 20;
+            for (int i = blk0; i < blk0 + 32; ++i) {
+                const uint32_t nib = (k[i >> 1] >> (4 * (i & 1))) & 15u;
+                const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, 1.0f, 0);
+                const double qv = (double)bf16_to_f32(q[i]);
+                blk = fma(qv, (double)v[0], blk);
+                qn1 += fabs(qv);
+                emin = min(emin, bf16_pair_emin(q[i]));
+            }
+            const double sd = (double)sc[blk0 >> 5];
+            acc = fma(blk, sd, acc);
+            aacc = fma(fma((double)(K / 32) * 0x1p-53 * 1.001, fabs(blk), fp4_block_err(qn1, emin)), fabs(sd), aacc);
+        }
     } else {
         const uint8_t* q = reinterpret_cast<const uint8_t*>(a.iq) + r * K;
         const uint8_t* k = reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * K;
@@ -359,12 +612,21 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
             ok = __float_as_uint(lo) == __float_as_uint(hi);
             res = lo;
         }
+    } else if (a.dtype == 2) {
+        const double eb = (aacc + fabs(acc) * 0x1p-52) * (1.0 + 0x1p-40);
+        const float lo = (float)(acc - eb), hi = (float)(acc + eb);
+        ok = __float_as_uint(lo) == __float_as_uint(hi);
+        res = lo;
     } else {
         res = (float)acc;
     }
     if (!ok)
-        res = exact_bf16_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * K,
-                             reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + e) * K, K);
+        res = a.dtype == 2
+                  ? exact_fp4_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * K,
+                                  reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * (K / 2),
+                                  a.ik_scales + (b * a.N_cap + e) * (K / 32), K)
+                  : exact_bf16_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * K,
+                                   reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + e) * K, K);
     a.scores[r * a.ld + e] = res;
     if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
 }
@@ -373,7 +635,7 @@ hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
     ScoreArgs a = args;
     const int64_t R = (int64_t)a.B * a.Qs;
     if (R == 0 || a.N == 0) return hipSuccess;
-    const int eb = a.K * (a.dtype == 0 ? 2 : 1);
+    const int eb = a.dtype == 0 ? a.K * 2 : a.dtype == 1 ? a.K : a.K / 2;  // key bytes per entry
     const int cpl = eb / 128;
     const bool fast = eb % 128 == 0 && (cpl == 1 || cpl == 2 || cpl == 4 || cpl == 8);
     if (fast) {
@@ -386,11 +648,16 @@ hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
             if (cpl == 2) hipLaunchKernelGGL((score_exact_kernel<0, 2>), grid, dim3(kScoreThreads), 0, stream, a);
             if (cpl == 4) hipLaunchKernelGGL((score_exact_kernel<0, 4>), grid, dim3(kScoreThreads), 0, stream, a);
             if (cpl == 8) hipLaunchKernelGGL((score_exact_kernel<0, 8>), grid, dim3(kScoreThreads), 0, stream, a);
-        } else {
+        } else if (a.dtype == 1) {
             if (cpl == 1) hipLaunchKernelGGL((score_exact_kernel<1, 1>), grid, dim3(kScoreThreads), 0, stream, a);
             if (cpl == 2) hipLaunchKernelGGL((score_exact_kernel<1, 2>), grid, dim3(kScoreThreads), 0, stream, a);
             if (cpl == 4) hipLaunchKernelGGL((score_exact_kernel<1, 4>), grid, dim3(kScoreThreads), 0, stream, a);
             if (cpl == 8) hipLaunchKernelGGL((score_exact_kernel<1, 8>), grid, dim3(kScoreThreads), 0, stream, a);
+        } else {
+            if (cpl == 1) hipLaunchKernelGGL((score_exact_kernel<2, 1>), grid, dim3(kScoreThreads), 0, stream, a);
+            if (cpl == 2) hipLaunchKernelGGL((score_exact_kernel<2, 2>), grid, dim3(kScoreThreads), 0, stream, a);
+            if (cpl == 4) hipLaunchKernelGGL((score_exact_kernel<2, 4>), grid, dim3(kScoreThreads), 0, stream, a);
+            if (cpl == 8) hipLaunchKernelGGL((score_exact_kernel<2, 8>), grid, dim3(kScoreThreads), 0, stream, a);
         }
     } else {
         dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)R);

@@ -66,7 +66,13 @@ typedef enum {
     CSA2_MODE_REUSE = 2    /* shares the group's entries and latest selection   */
 } csa2_mode;
 
-typedef enum { CSA2_IDX_BF16 = 0, CSA2_IDX_FP8_E4M3 = 1 } csa2_idx_dtype;
+/* Index-key storage.  BF16 and FP8_E4M3: keys and index queries in that dtype.
+ * FP4_E2M1 ("Why Is DeepSeek V4.1 Flash So Fast?", section 7: FP4 reaches the
+ * indexer too): keys are stored with the cache's codec, e2m1 codes
+ * [..][H*d/2] (element 2i in the low nibble) plus one fp32 scale per 32
+ * consecutive elements [..][H*d/32], each key value code*scale exactly; index
+ * queries are bf16 and H*d must be a multiple of 32. */
+typedef enum { CSA2_IDX_BF16 = 0, CSA2_IDX_FP8_E4M3 = 1, CSA2_IDX_FP4_E2M1 = 2 } csa2_idx_dtype;
 
 /* State of one sharing group ("DeepSeek-V4.1-Flash", "Sharing the cache
  * across layers": one stored copy of the entries per group, plus the
@@ -90,6 +96,8 @@ typedef struct csa2_group {
     int32_t has_entries;      /* caller sets it after filling the cache; Full sets it */
     int32_t has_selection;    /* set by Full and Reindex, required by Reuse        */
     int32_t sel_qs;           /* Qs of the stored selection                         */
+    float* ikey_scales;       /* FP4_E2M1 keys only: [B][N_cap][H_I*d_I/32] scales;
+                                 ikeys then holds the codes [B][N_cap][H_I*d_I/2] */
 } csa2_group;
 
 /* Per-layer inputs.  Every mode uses its own queries and window ("every layer
@@ -100,7 +108,8 @@ typedef struct csa2_layer_args {
                               sees entries j <= n_valid-Qs+i)                       */
     int32_t Hq;            /* query heads, 1..32                                      */
     const void* q;         /* bf16 [B][Qs][Hq][D]                                     */
-    const void* iq;        /* [B][Qs][H_I][d_I] in idx_dtype; Full and Reindex only   */
+    const void* iq;        /* [B][Qs][H_I][d_I] in idx_dtype (bf16 for FP4_E2M1 keys);
+                              Full and Reindex only                                   */
     const void* wk;        /* bf16 [B][Qs+W-1][D] window keys; row i..i+W-1 for row i */
     const void* wv;        /* bf16 [B][Qs+W-1][D] window values                       */
     int32_t W;             /* window rows per query (0..1024)                         */
@@ -108,7 +117,8 @@ typedef struct csa2_layer_args {
                               window buffer; NULL = all valid                         */
     const float* new_entry;/* fp32 [B][Qs][D]: Full writes these at slots
                               n_valid-Qs .. n_valid-1                                 */
-    const void* new_ikey;  /* [B][Qs][H_I][d_I] index keys stored with them (Full)    */
+    const void* new_ikey;  /* [B][Qs][H_I][d_I] index keys stored with them (Full); in
+                              idx_dtype, or fp32 for FP4_E2M1 (packed on write)       */
     float sm_scale;        /* softmax scale, e.g. 1/sqrt(D)                           */
     float* out;            /* fp32 [B][Qs][Hq][D]                                     */
     float* lse;            /* fp32 [B][Qs][Hq] natural-log sum-exp, or NULL           */
@@ -129,13 +139,15 @@ csa2_status csa2_fp4_pack(const float* x, int64_t rows, int32_t dim, uint8_t* co
 
 /* S2 - Index scores ("Why Is DeepSeek V4.1 Flash So Fast?", section 4: a
  * cheaper search scores positions before attention; "Inference-Efficient
- * LLMs", section 5).  iq: [B][Qs][H][d], ik: [B][N][H][d] in `dtype`;
- * scores: fp32 [B][Qs][N], each the exact sum rounded once to fp32 (see the
- * top of this file).  H*d must be a multiple of 64 (bf16) or 128 (fp8) for
- * the streaming kernel and at most 4096.  N == 0 is a no-op. */
-csa2_status csa2_index_score(const void* iq, const void* ik, csa2_idx_dtype dtype, int32_t B,
-                             int32_t Qs, int64_t N, int32_t H, int32_t d, float* scores,
-                             void* stream);
+ * LLMs", section 5).  iq: [B][Qs][H][d], ik: [B][N][H][d] in `dtype`
+ * (FP4_E2M1: iq bf16, ik the codes [B][N][H*d/2] and ik_scales [B][N][H*d/32];
+ * ik_scales is ignored for the other dtypes); scores: fp32 [B][Qs][N], each
+ * the exact sum rounded once to fp32 (see the top of this file).  H*d must be
+ * a multiple of 64 (bf16), 128 (fp8) or 256 (FP4) for the streaming kernel,
+ * and at most 4096.  N == 0 is a no-op. */
+csa2_status csa2_index_score(const void* iq, const void* ik, const float* ik_scales,
+                             csa2_idx_dtype dtype, int32_t B, int32_t Qs, int64_t N, int32_t H,
+                             int32_t d, float* scores, void* stream);
 
 /* S3 - Top-k selection ("Why Is DeepSeek V4.1 Flash So Fast?", sections 3 and
  * 4: select the useful compressed positions).  scores: fp32 [R][ld], row r
@@ -192,7 +204,8 @@ int64_t csa2_cache_bytes(int64_t entries, int64_t numbers, int64_t copies, int64
  * 0 .. n_valid_max-1 of every sequence, in this order:
  *   codes  [B][n_valid_max][D/2]     u8
  *   scales [B][n_valid_max][D/32]    f32
- *   ikeys  [B][n_valid_max][H_I][d_I] in idx_dtype
+ *   ikeys  [B][n_valid_max][H_I][d_I] in idx_dtype (FP4: codes [..][H_I*d_I/2])
+ *   ikey_scales [B][n_valid_max][H_I*d_I/32] f32, FP4 index keys only
  *   sel    [B*sel_qs][k]             i32, only when has_selection is set.
  * csa2_group_image_bytes returns its size (0 for an invalid group).
  * csa2_group_save copies the group into `host` (bytes >= the image size;

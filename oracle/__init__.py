@@ -8,7 +8,8 @@ csa2_oracle.c.
 
 Storage conventions (identical to the inputs the GPU path receives):
   bf16 tensors are uint16 bit patterns, fp8 e4m3fn tensors are uint8 bit patterns,
-  index dtype code 0 = bf16, 1 = e4m3.
+  index dtype code 0 = bf16, 1 = e4m3, 2 = FP4 keys (e2m1 codes [.., K/2] plus fp32
+  scales per 32 elements [.., K/32], the cache codec) with bf16 index queries.
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ _SRC = os.path.join(_HERE, "csa2_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-IDX_DTYPES = {"bf16": 0, "e4m3": 1}
+IDX_DTYPES = {"bf16": 0, "e4m3": 1, "fp4": 2}
 MODES = {"F": 0, "Ri": 1, "Ru": 2}
 
 
@@ -44,7 +45,7 @@ class _Group(ctypes.Structure):
     _fields_ = [("B", i32), ("N_cap", i64), ("D", i32), ("H_I", i32), ("d_I", i32),
                 ("idx_dtype", i32), ("k", i32), ("codes", vp), ("scales", vp), ("ikeys", vp),
                 ("n_valid", vp), ("sel", vp), ("has_entries", i32), ("has_selection", i32),
-                ("sel_qs", i32)]
+                ("sel_qs", i32), ("ikey_scales", vp)]
 
 
 class _Layer(ctypes.Structure):
@@ -72,7 +73,7 @@ def _load():
     lib.orc_exact_dot_f32.restype = ctypes.c_float
     lib.orc_exact_sum_f32.argtypes = [vp, ctypes.c_int]
     lib.orc_exact_sum_f32.restype = ctypes.c_float
-    lib.orc_index_score.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, ctypes.c_int,
+    lib.orc_index_score.argtypes = [ctypes.c_int, vp, vp, vp, i64, i64, i64, ctypes.c_int,
                                     ctypes.c_int, vp, vp]
     lib.orc_index_score.restype = None
     lib.orc_topk.argtypes = [vp, i64, i64, i64, vp, ctypes.c_int, vp]
@@ -144,17 +145,26 @@ def exact_sum_f32(t: np.ndarray) -> np.float32:
     return np.float32(_load().orc_exact_sum_f32(t.ctypes.data, t.size))
 
 
-def index_score(dtype: str, iq: np.ndarray, ik: np.ndarray, n_valid_row=None) -> np.ndarray:
-    """iq [B, Qs, H, d] and ik [B, N, H, d] stored bits -> exact fp32 scores [B, Qs, N]."""
+def index_score(dtype: str, iq: np.ndarray, ik: np.ndarray, n_valid_row=None, ik_scales=None) -> np.ndarray:
+    """iq [B, Qs, H, d] and ik [B, N, H, d] stored bits -> exact fp32 scores [B, Qs, N].
+    dtype 'fp4': iq bf16 bits, ik e2m1 codes [B, N, H, d/2], ik_scales float32 [B, N, H*d/32]."""
     B, Qs, H, d = iq.shape
     N = ik.shape[1]
-    assert ik.shape == (B, N, H, d)
-    st = np.uint16 if dtype == "bf16" else np.uint8
-    iq = _c(iq, st)
-    ik = _c(ik, st)
+    if dtype == "fp4":
+        assert ik.shape == (B, N, H, d // 2) and ik_scales is not None
+        iq = _c(iq, np.uint16)
+        ik = _c(ik, np.uint8)
+        ks = _c(ik_scales, np.float32)
+        assert ks.shape == (B, N, H * d // 32)
+    else:
+        assert ik.shape == (B, N, H, d)
+        st = np.uint16 if dtype == "bf16" else np.uint8
+        iq = _c(iq, st)
+        ik = _c(ik, st)
+        ks = None
     nv = None if n_valid_row is None else _c(n_valid_row, np.int64)
     out = np.empty((B, Qs, N), dtype=np.float32)
-    _load().orc_index_score(IDX_DTYPES[dtype], iq.ctypes.data, ik.ctypes.data, B, Qs, N, H, d,
+    _load().orc_index_score(IDX_DTYPES[dtype], iq.ctypes.data, ik.ctypes.data, _p(ks), B, Qs, N, H, d,
                             _p(nv), out.ctypes.data)
     return out
 
@@ -199,18 +209,25 @@ class Group:
     """One sharing group's state: FP4 entries, index keys, valid counts and the shared selection."""
 
     def __init__(self, codes, scales, ikeys, n_valid, idx_dtype: str, k: int, max_rows: int,
-                 has_entries: bool = True):
+                 has_entries: bool = True, ikey_scales=None):
+        """ikeys [B, N, H, d] stored bits; 'fp4': e2m1 codes [B, N, H, d/2] and
+        ikey_scales float32 [B, N, H*d/32]."""
         self.codes = _c(codes, np.uint8)
         self.scales = _c(scales, np.float32)
+        self.idx_dtype = idx_dtype
         st = np.uint16 if idx_dtype == "bf16" else np.uint8
         self.ikeys = _c(ikeys, st)
         self.B, self.N_cap, H_I, d_I = self.ikeys.shape
+        self.ikey_scales = None
+        if idx_dtype == "fp4":
+            d_I *= 2
+            self.ikey_scales = _c(ikey_scales, np.float32)
         self.n_valid = _c(n_valid, np.int64)
         self.sel = np.full((max_rows, k), -1, dtype=np.int32)
         self._g = _Group(self.B, self.N_cap, self.codes.shape[2] * 2, H_I, d_I,
                          IDX_DTYPES[idx_dtype], k, self.codes.ctypes.data, self.scales.ctypes.data,
                          self.ikeys.ctypes.data, self.n_valid.ctypes.data, self.sel.ctypes.data,
-                         int(has_entries), 0, 0)
+                         int(has_entries), 0, 0, _p(self.ikey_scales))
 
     @property
     def has_selection(self) -> bool:
@@ -222,11 +239,12 @@ class Group:
         q = _c(q, np.uint16)
         B, Qs, Hq, D = q.shape
         st = self.ikeys.dtype
-        iq = None if iq is None else _c(iq, st)
+        qt = np.uint16 if self.idx_dtype == "fp4" else st  # fp4 keys take bf16 queries
+        iq = None if iq is None else _c(iq, qt)
         wk = _c(wk, np.uint16)
         wv = _c(wv, np.uint16)
         ne = None if new_entry is None else _c(new_entry, np.float32)
-        nk = None if new_ikey is None else _c(new_ikey, st)
+        nk = None if new_ikey is None else _c(new_ikey, np.float32 if self.idx_dtype == "fp4" else st)
         wl = None if wlen is None else _c(wlen, np.int32)
         out = np.zeros((B, Qs, Hq, D), dtype=np.float32)
         lse = np.zeros((B, Qs, Hq), dtype=np.float32)

@@ -222,9 +222,12 @@ float orc_exact_sum_f32(const double* t, int n) {
 /* [P1 s4], [P3 s5]: index scores.  iq [B][Qs][H][d], ik [B][N][H][d] in the
    stored dtype; scores [B][Qs][N] = fp32 RNE of the exact
    sum_h sum_e iq[b,i,h,e] * ik[b,j,h,e].  Rows r=(b,i) score entries
-   j < n_valid_row[r] only (NULL: all N); the rest are set to -inf. */
-void orc_index_score(int dtype, const void* iq, const void* ik, int64_t B, int64_t Qs, int64_t N,
-                     int H, int d, const int64_t* n_valid_row, float* scores) {
+   j < n_valid_row[r] only (NULL: all N); the rest are set to -inf.
+   dtype 2 ([P1 s7]: the indexer itself in FP4): keys are e2m1 codes
+   [B][N][H*d/2] with fp32 scales [B][N][H*d/32] (the cache codec), each key
+   value code*scale exactly; the index queries are bf16. */
+void orc_index_score(int dtype, const void* iq, const void* ik, const float* ik_scales, int64_t B,
+                     int64_t Qs, int64_t N, int H, int d, const int64_t* n_valid_row, float* scores) {
     const int K = H * d;
 #pragma omp parallel for schedule(dynamic, 1) collapse(2)
     for (int64_t b = 0; b < B; ++b)
@@ -232,14 +235,18 @@ void orc_index_score(int dtype, const void* iq, const void* ik, int64_t B, int64
             int64_t r = b * Qs + i;
             double* qv = (double*)malloc(sizeof(double) * K);
             double* kv = (double*)malloc(sizeof(double) * K);
-            for (int e = 0; e < K; ++e) qv[e] = orc_idx_value(dtype, iq, r * K + e);
+            for (int e = 0; e < K; ++e) qv[e] = orc_idx_value(dtype == 2 ? 0 : dtype, iq, r * K + e);
             int64_t nv = n_valid_row ? n_valid_row[r] : N;
             for (int64_t j = 0; j < N; ++j) {
                 if (j >= nv) {
                     scores[r * N + j] = -INFINITY;
                     continue;
                 }
-                for (int e = 0; e < K; ++e) kv[e] = orc_idx_value(dtype, ik, (b * N + j) * K + e);
+                if (dtype == 2)
+                    orc_fp4_dequant((const uint8_t*)ik + (b * N + j) * (K / 2), ik_scales + (b * N + j) * (K / 32),
+                                    1, K, kv);
+                else
+                    for (int e = 0; e < K; ++e) kv[e] = orc_idx_value(dtype, ik, (b * N + j) * K + e);
                 scores[r * N + j] = orc_exact_dot_f32(qv, kv, K);
             }
             free(qv);
@@ -384,10 +391,11 @@ typedef struct {
     int32_t D, H_I, d_I, idx_dtype, k;
     uint8_t* codes;        /* [B][N_cap][D/2] */
     float* scales;         /* [B][N_cap][D/32] */
-    void* ikeys;           /* [B][N_cap][H_I][d_I] */
+    void* ikeys;           /* [B][N_cap][H_I][d_I]; dtype 2: e2m1 codes [B][N_cap][K/2] */
     const int64_t* n_valid;/* [B], counts the step's new rows */
     int32_t* sel;          /* [B*Qs][k] */
     int32_t has_entries, has_selection, sel_qs;
+    float* ikey_scales;    /* dtype 2: [B][N_cap][K/32] */
 } orc_group;
 
 typedef struct {
@@ -399,7 +407,7 @@ typedef struct {
     int32_t W;
     const int32_t* wlen;
     const float* new_entry; /* fp32 [B][Qs][D] */
-    const void* new_ikey;   /* [B][Qs][H_I][d_I] */
+    const void* new_ikey;   /* [B][Qs][H_I][d_I]; dtype 2: fp32, packed on write */
     float sm_scale;
     float* out;
     float* lse;
@@ -418,7 +426,7 @@ static void select_rows(const orc_layer* L, orc_group* G) {
             if (nv_row[b * Qs + i] > nmax) nmax = nv_row[b * Qs + i];
         }
     float* s = (float*)malloc(sizeof(float) * (size_t)(B * Qs * N));
-    orc_index_score(G->idx_dtype, L->iq, G->ikeys, B, Qs, N, G->H_I, G->d_I, nv_row, s);
+    orc_index_score(G->idx_dtype, L->iq, G->ikeys, G->ikey_scales, B, Qs, N, G->H_I, G->d_I, nv_row, s);
     orc_topk(s, B * Qs, N, N, nv_row, G->k, G->sel);
     free(s);
     free(nv_row);
@@ -441,8 +449,13 @@ int orc_layer_step(int mode, const orc_layer* L, orc_group* G) {
                 orc_fp4_pack(L->new_entry + (b * Qs + i) * G->D, 1, G->D,
                              G->codes + (b * G->N_cap + slot) * (G->D / 2),
                              G->scales + (b * G->N_cap + slot) * (G->D / 32));
-                memcpy((char*)G->ikeys + (size_t)((b * G->N_cap + slot) * K) * kb,
-                       (const char*)L->new_ikey + (size_t)((b * Qs + i) * K) * kb, (size_t)K * kb);
+                if (G->idx_dtype == 2)
+                    orc_fp4_pack((const float*)L->new_ikey + (b * Qs + i) * K, 1, (int)K,
+                                 (uint8_t*)G->ikeys + (b * G->N_cap + slot) * (K / 2),
+                                 G->ikey_scales + (b * G->N_cap + slot) * (K / 32));
+                else
+                    memcpy((char*)G->ikeys + (size_t)((b * G->N_cap + slot) * K) * kb,
+                           (const char*)L->new_ikey + (size_t)((b * Qs + i) * K) * kb, (size_t)K * kb);
             }
         G->has_entries = 1;
         select_rows(L, G);

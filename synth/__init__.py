@@ -116,7 +116,10 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def normal_idx(dtype: str, seed_: int, n: int, offset: int = 0) -> np.ndarray:
-    """Index-vector stream in the named storage dtype ('bf16' -> uint16 bits, 'e4m3' -> uint8 bits)."""
+    """Index-vector stream in the named storage dtype ('bf16' -> uint16 bits, 'e4m3' -> uint8 bits,
+    'fp4' -> the fp32 values, which each side packs with its own FP4 codec)."""
+    if dtype == "fp4":
+        return normal_f32(seed_, n, offset)
     if dtype == "bf16":
         return normal_bf16(seed_, n, offset)
     if dtype == "e4m3":

@@ -17,13 +17,18 @@ from .workloads import Workload
 class Inputs:
     wl: Workload
     cache_x: list      # per group: fp32 [B, N, D]
-    ikeys: list        # per group: bits [B, N, H, d]
+    ikeys: list        # per group: bits [B, N, H, d] (fp4 keys: fp32 values, packed by each side)
     layers: list       # per layer: dict(q, iq, wk, wv, new_entry, new_ikey)
     n_valid: np.ndarray  # int32 [B]
 
 
 def idx_np_dtype(wl: Workload):
     return np.uint16 if wl.idx_dtype == "bf16" else np.uint8
+
+
+def query_dtype(wl: Workload) -> str:
+    """Storage dtype of the index queries: bf16 queries go with FP4 keys."""
+    return "bf16" if wl.idx_dtype == "fp4" else wl.idx_dtype
 
 
 def make_inputs(wl: Workload, n_valid=None, groups=None) -> Inputs:
@@ -43,7 +48,7 @@ def make_inputs(wl: Workload, n_valid=None, groups=None) -> Inputs:
                 wv=normal_bf16(st(5), B * (Qs + W - 1) * D).reshape(B, Qs + W - 1, D),
                 iq=None, new_entry=None, new_ikey=None, group=g)
             if mode in ("F", "Ri"):
-                L["iq"] = normal_idx(wl.idx_dtype, st(2), B * Qs * H * d).reshape(B, Qs, H, d)
+                L["iq"] = normal_idx(query_dtype(wl), st(2), B * Qs * H * d).reshape(B, Qs, H, d)
             if mode == "F":
                 L["new_entry"] = normal_f32(st(6), B * Qs * D).reshape(B, Qs, D)
                 L["new_ikey"] = normal_idx(wl.idx_dtype, st(7), B * Qs * H * d).reshape(B, Qs, H, d)

@@ -8,6 +8,8 @@ Shapes follow the workload list this implementation is measured on:
   w5  16-layer decode stack, batch 64, 131,072 entries, (F,Ri,Ru,Ru) x 4, 4x64 bf16, k=2048
   w6  speculative verify: w2 with a draft block of 5 queries per sequence, causal among
       the drafts (query i of the block sees the entries up to its own)
+  w7  w2 with FP4 index keys: e2m1 codes with an fp32 scale per 32 elements (the cache
+      codec), bf16 index queries
 Every layer: 16 bf16 query heads of dim 128, scale 1/sqrt(128), a 128-row bf16 window,
 entries of dim 128 stored as FP4 e2m1 with an fp32 scale per 32 elements.
 
@@ -37,7 +39,7 @@ class Workload:
     N: int
     H_I: int
     d_I: int
-    idx_dtype: str  # 'bf16' or 'e4m3'
+    idx_dtype: str  # 'bf16', 'e4m3' or 'fp4' (keys; fp4 takes bf16 queries)
     k: int
     pattern: tuple  # modes of one sharing group, e.g. ('F','Ri','Ru','Ru')
     groups: int = 1
@@ -81,4 +83,7 @@ W5 = Workload(5, "decode_b64_n131072_16layer_stack", B=64, N=131072, H_I=4, d_I=
 W6 = Workload(6, "verify5_b32_n65536_group_F_Ri_Ru_Ru", B=32, N=65536, H_I=4, d_I=64,
               idx_dtype="bf16", k=2048, pattern=("F", "Ri", "Ru", "Ru"), Qs=5)
 
-ALL = {1: W1, 2: W2, 3: W3, 4: W4, 5: W5, 6: W6}
+W7 = Workload(7, "decode_b32_n65536_group_F_Ri_Ru_Ru_fp4idx", B=32, N=65536, H_I=4, d_I=64,
+              idx_dtype="fp4", k=2048, pattern=("F", "Ri", "Ru", "Ru"))
+
+ALL = {1: W1, 2: W2, 3: W3, 4: W4, 5: W5, 6: W6, 7: W7}

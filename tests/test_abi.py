@@ -54,12 +54,15 @@ def test_fp4_pack_validation():
 
 def test_index_score_validation():
     L = csa2.lib()
-    assert L.csa2_index_score(FAKE, FAKE, 0, 1, 1, 10, 64, 65, FAKE, None) == csa2.ERR_INVALID_ARG
-    assert L.csa2_index_score(FAKE, FAKE, 7, 1, 1, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
-    assert L.csa2_index_score(FAKE, FAKE, 0, 1, 0, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
-    assert L.csa2_index_score(None, FAKE, 0, 1, 1, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
-    assert L.csa2_index_score(FAKE, FAKE, 0, 1, 1, 1 << 31, 4, 64, FAKE, None) == csa2.ERR_UNSUPPORTED
-    assert L.csa2_index_score(FAKE, FAKE, 0, 1, 1, 0, 4, 64, FAKE, None) == csa2.OK
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 1, 10, 64, 65, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, None, 7, 1, 1, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 0, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(None, FAKE, None, 0, 1, 1, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 1, 1 << 31, 4, 64, FAKE, None) == csa2.ERR_UNSUPPORTED
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 1, 0, 4, 64, FAKE, None) == csa2.OK
+    # FP4 keys need their scales, and whole 32-element blocks
+    assert L.csa2_index_score(FAKE, FAKE, None, 2, 1, 1, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, FAKE, 2, 1, 1, 10, 1, 48, FAKE, None) == csa2.ERR_INVALID_ARG
 
 
 def test_topk_validation():
@@ -151,3 +154,13 @@ def test_group_image_bytes_and_save_restore_validation():
     assert L.csa2_group_save(ctypes.byref(_group(has_entries=0)), FAKE, need, None) == csa2.ERR_STATE
     assert L.csa2_group_restore(ctypes.byref(g), FAKE, need - 1, None) == csa2.ERR_WORKSPACE
     assert L.csa2_group_restore(ctypes.byref(_group(codes=None)), FAKE, need, None) == csa2.ERR_INVALID_ARG
+
+
+def test_fp4_index_keys_validation_and_image():
+    # FP4 keys: the group needs its key scales; the image carries them after the codes
+    assert _step(0, _group(idx_dtype=2), _args()) == csa2.ERR_INVALID_ARG
+    assert _step(0, _group(idx_dtype=2, H_I=1, d_I=48, ikey_scales=FAKE), _args()) == csa2.ERR_INVALID_ARG
+    L = csa2.lib()
+    g = _group(idx_dtype=2, ikey_scales=FAKE, n_valid_max=10)
+    per_entry = 128 // 2 + 128 // 32 * 4 + 4 * 64 // 2 + 4 * 64 // 32 * 4
+    assert L.csa2_group_image_bytes(ctypes.byref(g)) == 2 * 10 * per_entry

@@ -11,7 +11,7 @@ import compressed_kv_cache_03_amd as csa2
 import oracle
 import synth
 from cases import make_inputs, rel_err
-from synth.workloads import W1, W2, W3, W4, W5, W6
+from synth.workloads import W1, W2, W3, W4, W5, W6, W7
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -112,6 +112,46 @@ def test_index_score_bf16_rounding_ties_take_exact_path():
     got = csa2.index_score(dev(iq), dev(ik), "bf16")
     torch.cuda.synchronize()
     assert bits_eq(host(got), oracle.index_score("bf16", iq, ik))
+
+
+def _fp4_key_case(rng, B, N, H, d):
+    # wide-exponent bf16 queries; every code byte; block scales over many binades
+    K = H * d
+    iq = synth.to_bf16_bits(((rng.random((B, 2, H, d)) - 0.5) *
+                             np.exp2(rng.integers(-60, 60, (B, 2, H, d)))).astype(np.float32))
+    codes = rng.integers(0, 256, (B, N, H, d // 2)).astype(np.uint8)
+    sc = (rng.random((B, N, K // 32)) + 0.5) * np.exp2(rng.integers(-126, 100, (B, N, K // 32)))
+    sc[:, ::7, 0] = 0.0
+    return iq, codes, sc.astype(np.float32)
+
+
+@pytest.mark.parametrize("H,d", [(4, 64), (2, 256), (3, 32)])
+def test_index_score_fp4_keys_bit_exact(H, d):
+    # (4, 64) and (2, 256) run the streaming kernel, (3, 32) the generic one
+    rng = np.random.default_rng(H * 100 + d)
+    B, N = 2, 3000
+    iq, codes, scales = _fp4_key_case(rng, B, N, H, d)
+    got = csa2.index_score(dev(iq), dev(codes), "fp4", ik_scales=dev(scales))
+    torch.cuda.synchronize()
+    assert bits_eq(host(got), oracle.index_score("fp4", iq, codes, ik_scales=scales))
+
+
+def test_index_score_fp4_keys_rounding_ties_take_exact_path():
+    # two blocks whose values sum to an fp32 midpoint: the certificate cannot decide,
+    # the exact accumulator rounds to even
+    K = 256
+    iq = np.zeros((1, 1, 1, K), np.uint16)
+    iq[0, 0, 0, 0] = synth.to_bf16_bits(np.array([1.0], np.float32))[0]
+    iq[0, 0, 0, 32] = iq[0, 0, 0, 0]
+    N = 64
+    codes = np.zeros((1, N, 1, K // 2), np.uint8)
+    scales = np.ones((1, N, K // 32), np.float32)
+    for j in range(N):
+        codes[0, j, 0, 0], codes[0, j, 0, 16] = 0x2, (0x2, 0x5, 0xA, 0xD)[j % 4]  # 1 and +-1, +-3
+        scales[0, j, 1] = 2.0 ** -(24 + j % 16)
+    got = csa2.index_score(dev(iq), dev(codes), "fp4", ik_scales=dev(scales))
+    torch.cuda.synchronize()
+    assert bits_eq(host(got), oracle.index_score("fp4", iq, codes, ik_scales=scales))
 
 
 # ---------------------------------------------------------------- S3 top-k
@@ -221,12 +261,23 @@ class Run:
         for g in range(wl.groups):
             x = self.inp.cache_x[g]
             oc, os_ = oracle.fp4_pack(x.reshape(B * N, D))
-            self.g_orc.append(oracle.Group(oc.reshape(B, N, D // 2), os_.reshape(B, N, D // 32),
-                                           self.inp.ikeys[g].copy(), self.inp.n_valid.astype(np.int64),
-                                           wl.idx_dtype, wl.k, max_rows=B * wl.Qs))
             gc, gs = csa2.fp4_pack(dev(x))
-            self.g_gpu.append(csa2.Group(gc, gs, dev(self.inp.ikeys[g]), dev(self.inp.n_valid),
-                                         wl.idx_dtype, wl.k, sel_rows=B * wl.Qs))
+            if wl.idx_dtype == "fp4":
+                # FP4 index keys: each side packs the fp32 key values with its own codec
+                K = H * d
+                kx = self.inp.ikeys[g].reshape(B * N, K)
+                okc, oks = oracle.fp4_pack(kx)
+                gkc, gks = csa2.fp4_pack(dev(kx))
+                o_keys, o_ks = okc.reshape(B, N, H, d // 2), oks.reshape(B, N, K // 32)
+                g_keys, g_ks = gkc.reshape(B, N, H, d // 2), gks.reshape(B, N, K // 32)
+            else:
+                o_keys, o_ks = self.inp.ikeys[g].copy(), None
+                g_keys, g_ks = dev(self.inp.ikeys[g]), None
+            self.g_orc.append(oracle.Group(oc.reshape(B, N, D // 2), os_.reshape(B, N, D // 32), o_keys,
+                                           self.inp.n_valid.astype(np.int64), wl.idx_dtype, wl.k,
+                                           max_rows=B * wl.Qs, ikey_scales=o_ks))
+            self.g_gpu.append(csa2.Group(gc, gs, g_keys, dev(self.inp.n_valid), wl.idx_dtype, wl.k,
+                                         sel_rows=B * wl.Qs, ikey_scales=g_ks))
 
     def layer(self, li):
         L = self.inp.layers[li]
@@ -256,6 +307,8 @@ class Run:
                 assert bits_eq(host(self.g_gpu[g].codes), self.g_orc[g].codes)
                 assert bits_eq(host(self.g_gpu[g].scales), self.g_orc[g].scales)
                 assert bits_eq(host(self.g_gpu[g].ikeys), self.g_orc[g].ikeys)
+                if self.g_orc[g].ikey_scales is not None:
+                    assert bits_eq(host(self.g_gpu[g].ikey_scales), self.g_orc[g].ikey_scales)
 
 
 def test_layer_step_w1_full_size():
@@ -300,6 +353,10 @@ def test_group_save_restore_resumes_bitwise():
         mode, _, _, _, go, gl = run.layer(li)
         assert mode == "Ru"
         assert bits_eq(go, ref_out[li][0]) and bits_eq(gl, ref_out[li][1]), li
+
+
+def test_w7_scaled_fp4_index_keys():
+    Run(W7.scaled(B=3, N=6000, k=600), n_valid=[6000, 4097, 5555]).check_all()
 
 
 def test_verify5_w6_scaled():

@@ -139,3 +139,69 @@ def test_e4m3_decoder_matches_torch_all_codes():
     ref = _e4m3_vals(codes)
     assert np.array_equal(ours, ref) and np.array_equal(np.signbit(ours), np.signbit(ref))
     assert math.isnan(oracle.idx_values("e4m3", np.array([0x7F], np.uint8))[0])
+
+
+# FP4 index keys (the cache codec reused by the indexer): value = e2m1(code) * scale
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # OCP MX e2m1 magnitudes, codes 0..7
+
+
+def _fp4_key_values(codes, scales):
+    """codes uint8 [..., K/2] (element 2i in the low nibble), scales float32 [..., K/32]
+    -> exact Fractions [..., K] as nested lists, written out from the format."""
+    codes = np.asarray(codes)
+    scales = np.asarray(scales)
+    K = scales.shape[-1] * 32
+    flat_c = codes.reshape(-1, K // 2)
+    flat_s = scales.reshape(-1, K // 32)
+    out = []
+    for row_c, row_s in zip(flat_c, flat_s):
+        vals = []
+        for e in range(K):
+            nib = (int(row_c[e // 2]) >> (4 * (e % 2))) & 15
+            mag = Fraction(E2M1[nib & 7])
+            vals.append((-mag if nib & 8 else mag) * Fraction(float(row_s[e // 32])))
+        out.append(vals)
+    return out
+
+
+def test_index_score_fp4_keys_match_rational_brute_force():
+    rng = np.random.default_rng(21)
+    B, Qs, N, H, d = 1, 3, 25, 2, 64
+    K = H * d
+    iq = _wide_bf16(rng, B * Qs * K).reshape(B, Qs, H, d)
+    codes = rng.integers(0, 256, (B, N, H, d // 2)).astype(np.uint8)
+    # scales over many binades, some subnormal, some zero
+    sc = (rng.random((B, N, K // 32)) + 0.5) * np.exp2(rng.integers(-140, 100, (B, N, K // 32)))
+    sc[0, 3, 1] = 0.0
+    sc[0, 5, 0] = 2.0 ** -149
+    scales = sc.astype(np.float32)
+    s = oracle.index_score("fp4", iq, codes, ik_scales=scales)
+    qv = _bf16_vals(iq).reshape(B, Qs, K)
+    kv = _fp4_key_values(codes, scales)
+    for i in range(Qs):
+        for j in range(N):
+            want = round_f32(sum((Fraction(float(qv[0, i, e])) * kv[j][e] for e in range(K)), Fraction(0)))
+            assert s[0, i, j].view(np.uint32) == want.view(np.uint32), (i, j)
+
+
+def test_index_score_fp4_keys_planted_ties_and_cancellation():
+    # q = 1 on two elements whose key values sum to an fp32 midpoint or cancel exactly
+    K = 64
+    iq = synth.to_bf16_bits(np.zeros((1, 1, 1, K), np.float32))
+    iq[0, 0, 0, 0] = synth.to_bf16_bits(np.array([1.0], np.float32))[0]
+    iq[0, 0, 0, 32] = iq[0, 0, 0, 0]
+    codes = np.zeros((1, 3, 1, K // 2), np.uint8)
+    scales = np.ones((1, 3, K // 32), np.float32)
+    # entry 0: 1.0 + 2^-24 (a tie between 1 and 1+2^-23, rounds to even = 1.0)
+    codes[0, 0, 0, 0], codes[0, 0, 0, 16] = 0x2, 0x2          # e2m1 1.0 in both blocks
+    scales[0, 0] = [1.0, 2.0 ** -24]
+    # entry 1: 1.0 + 3*2^-24 (a tie between 1+2^-23 and 1+2^-22, rounds to even = 1+2^-22)
+    codes[0, 1, 0, 0], codes[0, 1, 0, 16] = 0x2, 0x5          # 1.0 and 3.0
+    scales[0, 1] = [1.0, 2.0 ** -24]
+    # entry 2: 6 * 2^100 - 6 * 2^100 = +0
+    codes[0, 2, 0, 0], codes[0, 2, 0, 16] = 0x7, 0xF          # +6 and -6
+    scales[0, 2] = [2.0 ** 100, 2.0 ** 100]
+    s = oracle.index_score("fp4", iq, codes, ik_scales=scales)[0, 0]
+    assert s[0] == np.float32(1.0)
+    assert s[1] == np.float32(1.0 + 2.0 ** -22)
+    assert s[2] == 0.0 and not np.signbit(s[2])
