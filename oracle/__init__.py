@@ -45,7 +45,8 @@ class _Group(ctypes.Structure):
     _fields_ = [("B", i32), ("N_cap", i64), ("D", i32), ("H_I", i32), ("d_I", i32),
                 ("idx_dtype", i32), ("k", i32), ("codes", vp), ("scales", vp), ("ikeys", vp),
                 ("n_valid", vp), ("sel", vp), ("has_entries", i32), ("has_selection", i32),
-                ("sel_qs", i32), ("ikey_scales", vp)]
+                ("sel_qs", i32), ("ikey_scales", vp), ("pool_blocks", i32), ("pool", vp),
+                ("has_pool", i32), ("pool_qs", i32)]
 
 
 class _Layer(ctypes.Structure):
@@ -78,6 +79,10 @@ def _load():
     lib.orc_index_score.restype = None
     lib.orc_topk.argtypes = [vp, i64, i64, i64, vp, ctypes.c_int, vp]
     lib.orc_topk.restype = None
+    lib.orc_pool_blocks.argtypes = [vp, i64, i64, vp, ctypes.c_int, vp]
+    lib.orc_pool_blocks.restype = None
+    lib.orc_pool_topk.argtypes = [vp, i64, i64, vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.orc_pool_topk.restype = None
     lib.orc_attend.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp,
                                ctypes.c_int, vp, vp, ctypes.c_int, vp, f32, vp, vp]
     lib.orc_attend.restype = None
@@ -179,6 +184,32 @@ def topk(scores: np.ndarray, k: int, n_valid=None) -> np.ndarray:
     return out
 
 
+POOL_BLOCK = 8
+
+
+def pool_blocks(scores: np.ndarray, P: int, n_valid) -> np.ndarray:
+    """Hierarchical pool: scores float32 [R, N], n_valid [R] -> int32 [R, P], the P blocks of 8
+    positions with the largest block score (max over the block's valid positions), ascending."""
+    s = _c(scores, np.float32)
+    R, N = s.shape
+    nv = _c(n_valid, np.int64)
+    out = np.empty((R, P), dtype=np.int32)
+    _load().orc_pool_blocks(s.ctypes.data, R, N, nv.ctypes.data, P, out.ctypes.data)
+    return out
+
+
+def pool_topk(scores: np.ndarray, pool: np.ndarray, k: int, n_valid) -> np.ndarray:
+    """Top-k over the valid positions of the pool's blocks only: int32 [R, k] ascending, -1 padded."""
+    s = _c(scores, np.float32)
+    R, N = s.shape
+    pl = _c(pool, np.int32)
+    nv = _c(n_valid, np.int64)
+    out = np.empty((R, k), dtype=np.int32)
+    _load().orc_pool_topk(s.ctypes.data, R, N, nv.ctypes.data, pl.ctypes.data, pl.shape[1], k,
+                          out.ctypes.data)
+    return out
+
+
 def attend(q, codes, scales, idx, wk, wv, W, sm_scale, wlen=None):
     """q bf16 bits [B, Qs, Hq, D]; codes [B, N, D/2]; scales [B, N, D/32]; idx [B*Qs, k];
     wk, wv bf16 bits [B, Qs+W-1, D] -> (out float32 [B, Qs, Hq, D], lse float32 [B, Qs, Hq])."""
@@ -209,9 +240,10 @@ class Group:
     """One sharing group's state: FP4 entries, index keys, valid counts and the shared selection."""
 
     def __init__(self, codes, scales, ikeys, n_valid, idx_dtype: str, k: int, max_rows: int,
-                 has_entries: bool = True, ikey_scales=None):
+                 has_entries: bool = True, ikey_scales=None, pool_blocks: int = 0):
         """ikeys [B, N, H, d] stored bits; 'fp4': e2m1 codes [B, N, H, d/2] and
-        ikey_scales float32 [B, N, H*d/32]."""
+        ikey_scales float32 [B, N, H*d/32].  pool_blocks > 0: hierarchical search (Full keeps a
+        pool of that many 8-position blocks per row, Reindex ranks only the pool)."""
         self.codes = _c(codes, np.uint8)
         self.scales = _c(scales, np.float32)
         self.idx_dtype = idx_dtype
@@ -224,10 +256,12 @@ class Group:
             self.ikey_scales = _c(ikey_scales, np.float32)
         self.n_valid = _c(n_valid, np.int64)
         self.sel = np.full((max_rows, k), -1, dtype=np.int32)
+        self.pool = np.full((max_rows, max(pool_blocks, 1)), -1, dtype=np.int32)
         self._g = _Group(self.B, self.N_cap, self.codes.shape[2] * 2, H_I, d_I,
                          IDX_DTYPES[idx_dtype], k, self.codes.ctypes.data, self.scales.ctypes.data,
                          self.ikeys.ctypes.data, self.n_valid.ctypes.data, self.sel.ctypes.data,
-                         int(has_entries), 0, 0, _p(self.ikey_scales))
+                         int(has_entries), 0, 0, _p(self.ikey_scales), pool_blocks,
+                         self.pool.ctypes.data, 0, 0)
 
     @property
     def has_selection(self) -> bool:

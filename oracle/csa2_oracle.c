@@ -301,6 +301,72 @@ void orc_topk(const float* scores, int64_t R, int64_t N, int64_t ld, const int64
 }
 
 /* ------------------------------------------------------------------------ */
+/* Hierarchical search [P3 s5 "Hierarchical Sparse Indexing"]: a Full layer  */
+/* searches every position and keeps a pool of P blocks of 8 consecutive     */
+/* positions (the report's example: 2,048 blocks x 8 = 16,384 candidates);   */
+/* Reindex layers then rank only the pool's positions.  The pages fix no     */
+/* block-score rule; here a block's score is the largest index score among   */
+/* its valid positions, blocks are ranked by (score descending, block index  */
+/* ascending) with the same top-k as the positions, and the pool is the P    */
+/* best blocks, ascending, -1 padded.                                        */
+/* ------------------------------------------------------------------------ */
+#define ORC_POOL_BLOCK 8
+
+void orc_pool_blocks(const float* scores, int64_t R, int64_t ld, const int64_t* n_valid, int P,
+                     int32_t* pool) {
+    int64_t nb_max = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t nb = (n_valid[r] + ORC_POOL_BLOCK - 1) / ORC_POOL_BLOCK;
+        if (nb > nb_max) nb_max = nb;
+    }
+    if (nb_max < 1) nb_max = 1;
+    float* bs = (float*)malloc(sizeof(float) * (size_t)(R * nb_max));
+    int64_t* nb_row = (int64_t*)malloc(sizeof(int64_t) * (size_t)R);
+    for (int64_t r = 0; r < R; ++r) {
+        const int64_t nv = n_valid[r];
+        nb_row[r] = (nv + ORC_POOL_BLOCK - 1) / ORC_POOL_BLOCK;
+        for (int64_t j = 0; j < nb_row[r]; ++j) {
+            float m = scores[r * ld + j * ORC_POOL_BLOCK];
+            for (int64_t t = 1; t < ORC_POOL_BLOCK && j * ORC_POOL_BLOCK + t < nv; ++t) {
+                const float x = scores[r * ld + j * ORC_POOL_BLOCK + t];
+                if (x > m) m = x;
+            }
+            bs[r * nb_max + j] = m;
+        }
+    }
+    orc_topk(bs, R, nb_max, nb_max, nb_row, P, pool);
+    free(nb_row);
+    free(bs);
+}
+
+void orc_pool_topk(const float* scores, int64_t R, int64_t ld, const int64_t* n_valid,
+                   const int32_t* pool, int P, int k, int32_t* idx) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < R; ++r) {
+        sj_t* v = (sj_t*)malloc(sizeof(sj_t) * (size_t)P * ORC_POOL_BLOCK);
+        int64_t n = 0;
+        for (int p = 0; p < P; ++p) {
+            const int32_t blk = pool[r * P + p];
+            if (blk < 0) continue;
+            for (int t = 0; t < ORC_POOL_BLOCK; ++t) {
+                const int64_t j = (int64_t)blk * ORC_POOL_BLOCK + t;
+                if (j >= n_valid[r]) continue;
+                v[n].s = scores[r * ld + j];
+                v[n].j = (int32_t)j;
+                ++n;
+            }
+        }
+        qsort(v, (size_t)n, sizeof(sj_t), cmp_score_desc_index_asc);
+        const int64_t take = n < k ? n : k;
+        int32_t* out = idx + r * k;
+        for (int64_t t = 0; t < take; ++t) out[t] = v[t].j;
+        qsort(out, (size_t)take, sizeof(int32_t), cmp_int_asc);
+        for (int64_t t = take; t < k; ++t) out[t] = -1;
+        free(v);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Attention [P1 s3, s4], [P2 "Sharing the cache across layers"]: for query  */
 /* row r = (b, i) and head h, one softmax over                              */
 /*   z_j = scale * q.c_j   for the selected entries j (c_j dequantised, used */
@@ -396,6 +462,9 @@ typedef struct {
     int32_t* sel;          /* [B*Qs][k] */
     int32_t has_entries, has_selection, sel_qs;
     float* ikey_scales;    /* dtype 2: [B][N_cap][K/32] */
+    int32_t pool_blocks;   /* 0: flat search; P > 0: hierarchical with a pool of P blocks */
+    int32_t* pool;         /* [B*Qs][P] block indices kept by the latest Full */
+    int32_t has_pool, pool_qs;
 } orc_group;
 
 typedef struct {
@@ -415,7 +484,7 @@ typedef struct {
 
 enum { ORC_FULL = 0, ORC_REINDEX = 1, ORC_REUSE = 2 };
 
-static void select_rows(const orc_layer* L, orc_group* G) {
+static void select_rows(int mode, const orc_layer* L, orc_group* G) {
     const int64_t B = G->B, Qs = L->Qs, N = G->N_cap;
     int64_t* nv_row = (int64_t*)malloc(sizeof(int64_t) * (size_t)(B * Qs));
     int64_t nmax = 0;
@@ -427,7 +496,15 @@ static void select_rows(const orc_layer* L, orc_group* G) {
         }
     float* s = (float*)malloc(sizeof(float) * (size_t)(B * Qs * N));
     orc_index_score(G->idx_dtype, L->iq, G->ikeys, G->ikey_scales, B, Qs, N, G->H_I, G->d_I, nv_row, s);
-    orc_topk(s, B * Qs, N, N, nv_row, G->k, G->sel);
+    if (mode == ORC_REINDEX && G->pool_blocks > 0)
+        orc_pool_topk(s, B * Qs, N, nv_row, G->pool, G->pool_blocks, G->k, G->sel);
+    else
+        orc_topk(s, B * Qs, N, N, nv_row, G->k, G->sel);
+    if (mode == ORC_FULL && G->pool_blocks > 0) {
+        orc_pool_blocks(s, B * Qs, N, nv_row, G->pool_blocks, G->pool);
+        G->has_pool = 1;
+        G->pool_qs = L->Qs;
+    }
     free(s);
     free(nv_row);
     G->has_selection = 1;
@@ -458,11 +535,12 @@ int orc_layer_step(int mode, const orc_layer* L, orc_group* G) {
                            (const char*)L->new_ikey + (size_t)((b * Qs + i) * K) * kb, (size_t)K * kb);
             }
         G->has_entries = 1;
-        select_rows(L, G);
+        select_rows(ORC_FULL, L, G);
     } else if (mode == ORC_REINDEX) {
         if (!G->has_entries) return 4;
+        if (G->pool_blocks > 0 && (!G->has_pool || G->pool_qs != L->Qs)) return 4;
         if (!L->iq) return 1;
-        select_rows(L, G);
+        select_rows(ORC_REINDEX, L, G);
     } else if (mode == ORC_REUSE) {
         if (!G->has_selection || G->sel_qs != L->Qs) return 4;
     } else {
