@@ -104,7 +104,7 @@ def run_gpu(wl, steps, warmup, device, scan_loop=True):
             kc, kscales = csa2.fp4_pack(keys.reshape(B * N, K))
             keys, kscales = kc.reshape(B, N, wl.H_I, wl.d_I // 2), kscales.reshape(B, N, K // 32)
         groups.append(csa2.Group(gc, gs, keys, _dev(inp.n_valid, device), wl.idx_dtype, wl.k,
-                                 sel_rows=B * wl.Qs, ikey_scales=kscales))
+                                 sel_rows=B * wl.Qs, ikey_scales=kscales, pool_blocks=wl.pool_blocks))
     layers = []
     for L in inp.layers:
         d = {k: (_dev(v, device) if isinstance(v, np.ndarray) else v) for k, v in L.items()}
@@ -297,6 +297,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-fp4-index", action="store_true")
+    ap.add_argument("--no-hier", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -365,6 +366,15 @@ def main():
             "score_GBps": round(f_scan_bytes / (ms_fscan * 1e-3) / 1e9, 1),
             "note": "the w2 step with FP4 e2m1 index keys (fp32 block-32 scales, bf16 index queries); "
                     "scores still exact"}
+    if not args.no_hier:
+        hw = ALL[8]
+        ms_h, _, _, _ = run_gpu(hw, max(args.steps // 2, 3), 2, device, scan_loop=False)
+        res["hierarchical"] = {
+            "workload": hw.name, "ms_per_step": round(ms_h, 4),
+            "tokens_per_s": round(hw.B * hw.Qs / (ms_h * 1e-3), 1),
+            "pool": f"{hw.pool_blocks} blocks x 8 = {hw.pool_blocks * 8} candidates per row",
+            "note": "the w2 step with hierarchical search: Full scores all entries and keeps the pool, "
+                    "Reindex scores and ranks only the pool's entries"}
     if not args.no_prefill:
         pw = ALL[4]
         ms_chunk = run_prefill(pw, 5, 2, device)

@@ -27,7 +27,10 @@ class CGroup(ctypes.Structure):
                 ("idx_dtype", ctypes.c_int), ("k", i32), ("codes", vp), ("scales", vp),
                 ("ikeys", vp), ("n_valid", vp), ("n_valid_max", i64), ("sel", vp),
                 ("sel_rows", i32), ("has_entries", i32), ("has_selection", i32), ("sel_qs", i32),
-                ("ikey_scales", vp)]
+                ("ikey_scales", vp), ("pool_blocks", i32), ("pool", vp), ("has_pool", i32),
+                ("pool_qs", i32)]
+
+POOL_BLOCK = 8  # entries per block of a hierarchical group's pool
 
 
 class CLayerArgs(ctypes.Structure):
@@ -205,9 +208,11 @@ class Group:
     def __init__(self, codes: torch.Tensor, scales: torch.Tensor, ikeys: torch.Tensor,
                  n_valid: torch.Tensor, idx_dtype: str, k: int, sel_rows: int,
                  n_valid_max: int | None = None, has_entries: bool = True,
-                 ikey_scales: torch.Tensor | None = None):
+                 ikey_scales: torch.Tensor | None = None, pool_blocks: int = 0):
         """ikeys [B, N_cap, H_I, d_I] in idx_dtype; for 'fp4' the e2m1 codes
-        [B, N_cap, H_I, d_I/2] and ikey_scales fp32 [B, N_cap, H_I*d_I/32]."""
+        [B, N_cap, H_I, d_I/2] and ikey_scales fp32 [B, N_cap, H_I*d_I/32].
+        pool_blocks > 0 makes the group hierarchical: Full keeps a pool of that many
+        blocks of POOL_BLOCK entries per query row, Reindex searches only the pool."""
         for name, t in (("codes", codes), ("scales", scales), ("ikeys", ikeys), ("n_valid", n_valid)):
             _dev(t, name)
         B, N_cap, H_I, d_I = ikeys.shape
@@ -220,10 +225,12 @@ class Group:
         self.codes, self.scales, self.ikeys = codes, scales, ikeys
         self.n_valid = n_valid.to(torch.int32)
         self.sel = torch.full((sel_rows, k), -1, dtype=torch.int32, device=codes.device)
+        self.pool = torch.full((sel_rows, max(pool_blocks, 1)), -1, dtype=torch.int32, device=codes.device)
         nvm = int(self.n_valid.max().item()) if n_valid_max is None else int(n_valid_max)
         self.c = CGroup(B, N_cap, codes.shape[-1] * 2, H_I, d_I, IDX_DTYPE[idx_dtype], k,
                         codes.data_ptr(), scales.data_ptr(), ikeys.data_ptr(), self.n_valid.data_ptr(),
-                        nvm, self.sel.data_ptr(), sel_rows, int(has_entries), 0, 0, _ptr(ikey_scales))
+                        nvm, self.sel.data_ptr(), sel_rows, int(has_entries), 0, 0, _ptr(ikey_scales),
+                        int(pool_blocks), self.pool.data_ptr(), 0, 0)
         self._ws = None
 
     @property
@@ -260,7 +267,7 @@ class Group:
         return out, lse
 
     def image_bytes(self) -> int:
-        """Size of the group's host-tier image (entries, keys and selection)."""
+        """Size of the group's host-tier image (entries, keys, selection and pool)."""
         return int(_load().csa2_group_image_bytes(ctypes.byref(self.c)))
 
     def save(self, host: torch.Tensor | None = None, stream=None) -> torch.Tensor:

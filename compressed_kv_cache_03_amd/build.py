@@ -12,7 +12,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcsa2.so")
 ARCH = os.environ.get("CSA2_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["pack.hip", "score.hip", "topk.hip", "attend.hip", "index_gemm.hip", "csa2_api.cpp"]
+SOURCES = ["pack.hip", "score.hip", "topk.hip", "attend.hip", "index_gemm.hip", "pool.hip", "csa2_api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
 # -amdgpu-mfma-vgpr-form: MFMA accumulators in ordinary VGPRs, so the softmax

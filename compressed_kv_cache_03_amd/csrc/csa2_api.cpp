@@ -42,17 +42,25 @@ struct Layout {
     size_t blk = 0, blkcnt = 0;
     int cap = 0, nblk = 0;
     size_t part = 0;                     // attention partials
+    // hierarchical search
+    size_t bmax = 0, blk_nv = 0, pool_nv = 0;
+    int64_t ld_scores = 0, ld_blk = 0;
     size_t total = 0;
 };
 
 constexpr int64_t kSampleCols = 2048;  // threshold samples per prefill row
 
-// Prefill chunks with e4m3 keys select through the MFMA candidate path.
+// Prefill chunks with e4m3 keys select through the MFMA candidate path, which
+// never holds every score; a hierarchical group needs them for its block
+// scores and takes the exact path.
 bool mfma_prefill(const csa2_group* g, int Qs) {
     const int K = g->H_I * g->d_I;
     return Qs > 1 && g->idx_dtype == CSA2_IDX_FP8_E4M3 && (K == 128 || K == 256) &&
-           g->k <= band_max_k();
+           g->k <= band_max_k() && g->pool_blocks == 0;
 }
+
+int64_t pool_slots(const csa2_group* g) { return (int64_t)g->pool_blocks * CSA2_POOL_BLOCK; }
+int64_t block_count(int64_t N) { return (N + CSA2_POOL_BLOCK - 1) / CSA2_POOL_BLOCK; }
 
 struct TopkShape {
     int64_t R, N, slices;
@@ -80,8 +88,19 @@ Layout layer_layout(const csa2_group* g, int Qs, int Hq, int W) {
     Layout L;
     const int64_t R = (int64_t)g->B * Qs, N = g->N_cap;
     size_t off = 0;
+    // a hierarchical group scores either every entry or the pool's slots
+    L.ld_scores = std::max<int64_t>(N, pool_slots(g));
     L.scores = off;
-    off = align_up(off + (size_t)R * N * 4);
+    off = align_up(off + (size_t)R * L.ld_scores * 4);
+    if (g->pool_blocks > 0) {
+        L.ld_blk = block_count(N);
+        L.bmax = off;
+        off = align_up(off + (size_t)R * L.ld_blk * 4);
+        L.blk_nv = off;
+        off = align_up(off + (size_t)R * 4);
+        L.pool_nv = off;
+        off = align_up(off + (size_t)R * 4);
+    }
     if (mfma_prefill(g, Qs)) {
         L.cap = (int)std::min<int64_t>(band_cap(g->k), N);
         L.nblk = (int)((N + 255) / 256);
@@ -104,7 +123,11 @@ Layout layer_layout(const csa2_group* g, int Qs, int Hq, int W) {
         L.blk = off;
         off = align_up(off + (size_t)R * filter_colblks(N) * filter_blk_cap() * 8);
     } else {
-        add_topk(L, off, TopkShape{R, N, (N + topk_slice_len(N) - 1) / topk_slice_len(N)});
+        // one shape for every top-k of the layer: entries, blocks and pool slots
+        int64_t slices = 0;
+        for (int64_t n : {N, block_count(N), pool_slots(g)})
+            if (n > 0) slices = std::max(slices, (n + topk_slice_len(n) - 1) / topk_slice_len(n));
+        add_topk(L, off, TopkShape{R, L.ld_scores, slices});
     }
     L.part = off;
     off = align_up(off + attend_part_bytes(R, Hq, g->D, g->k, W));
@@ -136,6 +159,7 @@ struct ImageParts {
     int64_t n = 0;
     size_t code_row = 0, scale_row = 0, key_row = 0;  // bytes per entry
     size_t kscale_row = 0;                            // FP4 index keys only
+    size_t pool = 0;                                  // hierarchical groups with a pool
     size_t codes = 0, scales = 0, keys = 0, kscales = 0, sel = 0, total = 0;
 };
 
@@ -154,7 +178,10 @@ bool image_parts(const csa2_group* g, ImageParts* p) {
     p->scales = (size_t)g->B * p->n * p->scale_row;
     p->keys = (size_t)g->B * p->n * p->key_row;
     p->sel = g->has_selection ? (size_t)g->B * g->sel_qs * g->k * 4 : 0;
-    p->total = p->codes + p->scales + p->keys + p->kscales + p->sel;
+    if (g->has_pool && (g->pool_blocks < 1 || g->pool_qs < 1 || (int64_t)g->B * g->pool_qs > g->sel_rows))
+        return false;
+    p->pool = g->has_pool ? (size_t)g->B * g->pool_qs * g->pool_blocks * 4 : 0;
+    p->total = p->codes + p->scales + p->keys + p->kscales + p->sel + p->pool;
     return true;
 }
 
@@ -346,6 +373,10 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         return CSA2_ERR_INVALID_ARG;
     if (g->idx_dtype == CSA2_IDX_FP4_E2M1 && (!g->ikey_scales || !aligned(g->ikey_scales, 16)))
         return CSA2_ERR_INVALID_ARG;
+    if (g->pool_blocks < 0 ||
+        (g->pool_blocks > 0 && (pool_slots(g) < g->k || g->pool_blocks > block_count(g->N_cap) || !g->pool ||
+                                !aligned(g->pool, 4))))
+        return CSA2_ERR_INVALID_ARG;
     // layer arguments
     const int Qs = a->Qs;
     if (Qs < 1 || a->Hq < 1 || a->Hq > 32 || a->W < 0 || a->W > 1024 || !std::isfinite(a->sm_scale))
@@ -365,6 +396,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         return CSA2_ERR_INVALID_ARG;
     // group state
     if (mode == CSA2_MODE_REINDEX && !g->has_entries) return CSA2_ERR_STATE;
+    if (mode == CSA2_MODE_REINDEX && g->pool_blocks > 0 && (!g->has_pool || g->pool_qs != Qs))
+        return CSA2_ERR_STATE;
     if (mode == CSA2_MODE_REUSE && (!g->has_selection || g->sel_qs != Qs)) return CSA2_ERR_STATE;
     // workspace
     const Layout L = layer_layout(g, Qs, a->Hq, a->W);
@@ -448,22 +481,20 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         }
         if (e == hipSuccess) e = launch_band_final(ba, s);
     } else if (e == hipSuccess && selects) {
-        // S2 + S3: exact scores of the valid entries, digit histogram, selection
+        // S2 + S3: exact scores of the valid entries (or, for Reindex in a
+        // hierarchical group, of the pool's entries), digit histogram, selection
+        const bool in_pool = mode == CSA2_MODE_REINDEX && g->pool_blocks > 0;
+        float* scores = at<float>(ws, L.scores);
         TopkArgs t{};
-        t.scores = at<float>(ws, L.scores);
+        t.scores = scores;
         t.R = R;
-        t.N = g->n_valid_max;
-        t.ld = g->N_cap;
-        t.nvb = g->n_valid;
-        t.Qs = Qs;
+        t.ld = L.ld_scores;
         t.k = g->k;
         t.idx = g->sel;
         t.hist = at<uint32_t>(ws, L.hist);
         t.cand_idx = at<int32_t>(ws, L.cand_idx);
         t.cand_key = at<uint32_t>(ws, L.cand_key);
         t.slice_cnt = at<uint32_t>(ws, L.slice_cnt);
-        t.slice_len = topk_slice_len(g->N_cap);
-        t.slices = (int)((g->n_valid_max + t.slice_len - 1) / t.slice_len);
         ScoreArgs sa{};
         sa.iq = a->iq;
         sa.ik = g->ikeys;
@@ -472,15 +503,54 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         sa.K = K;
         sa.B = g->B;
         sa.Qs = Qs;
-        sa.N = g->n_valid_max;
         sa.N_cap = g->N_cap;
         sa.nvb = g->n_valid;
-        sa.scores = at<float>(ws, L.scores);
-        sa.ld = g->N_cap;
+        sa.scores = scores;
+        sa.ld = L.ld_scores;
         sa.hist = t.hist;
-        e = launch_zero(t.hist, R * kHistBinsHost, s);
+        if (in_pool) {
+            int32_t* pool_nv = at<int32_t>(ws, L.pool_nv);
+            e = launch_pool_count(g->pool, R, g->pool_blocks, g->n_valid, Qs, pool_nv, s);
+            sa.pool = g->pool;
+            sa.pool_blocks = g->pool_blocks;
+            sa.pool_nv = pool_nv;
+            sa.N = pool_slots(g);
+            t.N = pool_slots(g);
+            t.nvb = pool_nv;
+            t.Qs = 1;
+            t.slice_len = topk_slice_len(pool_slots(g));
+        } else {
+            sa.N = g->n_valid_max;
+            t.N = g->n_valid_max;
+            t.nvb = g->n_valid;
+            t.Qs = Qs;
+            t.slice_len = topk_slice_len(g->N_cap);
+        }
+        t.slices = (int)((t.N + t.slice_len - 1) / t.slice_len);
+        if (e == hipSuccess) e = launch_zero(t.hist, R * kHistBinsHost, s);
         if (e == hipSuccess) e = launch_score_exact(sa, s);
         if (e == hipSuccess) e = launch_topk_select(t, s);
+        // the selection holds pool slots: turn them into entries
+        if (e == hipSuccess && in_pool) e = launch_pool_map(g->sel, R, g->k, g->pool, g->pool_blocks, s);
+        if (e == hipSuccess && mode == CSA2_MODE_FULL && g->pool_blocks > 0) {
+            // the pool: blocks of 8 entries ranked by their largest score
+            float* bmax = at<float>(ws, L.bmax);
+            int32_t* blk_nv = at<int32_t>(ws, L.blk_nv);
+            TopkArgs tb = t;
+            tb.scores = bmax;
+            tb.N = block_count(g->n_valid_max);
+            tb.ld = L.ld_blk;
+            tb.nvb = blk_nv;
+            tb.Qs = 1;
+            tb.k = g->pool_blocks;
+            tb.idx = g->pool;
+            tb.slice_len = topk_slice_len(L.ld_blk);
+            tb.slices = (int)((tb.N + tb.slice_len - 1) / tb.slice_len);
+            e = launch_block_max(scores, R, g->n_valid_max, L.ld_scores, g->n_valid, Qs, bmax, L.ld_blk, blk_nv, s);
+            if (e == hipSuccess) e = launch_zero(tb.hist, R * kHistBinsHost, s);
+            if (e == hipSuccess) e = launch_topk_hist(tb, s);
+            if (e == hipSuccess) e = launch_topk_select(tb, s);
+        }
     }
     if (e == hipSuccess) {
         // S5 + S6: gather, dequantise, attend over the selection and the window
@@ -511,6 +581,10 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         g->has_selection = 1;
         g->sel_qs = Qs;
     }
+    if (mode == CSA2_MODE_FULL && g->pool_blocks > 0) {
+        g->has_pool = 1;
+        g->pool_qs = Qs;
+    }
     return CSA2_OK;
 }
 
@@ -522,7 +596,7 @@ size_t csa2_group_image_bytes(const csa2_group* g) {
 csa2_status csa2_group_save(const csa2_group* g, void* host, size_t bytes, void* stream) {
     ImageParts p;
     if (!image_parts(g, &p) || !host || !g->codes || !g->scales || !g->ikeys || (p.sel && !g->sel) ||
-        (p.kscales && !g->ikey_scales))
+        (p.kscales && !g->ikey_scales) || (p.pool && !g->pool))
         return CSA2_ERR_INVALID_ARG;
     if (!g->has_entries) return CSA2_ERR_STATE;
     if (bytes < p.total) return CSA2_ERR_WORKSPACE;
@@ -542,13 +616,16 @@ csa2_status csa2_group_save(const csa2_group* g, void* host, size_t bytes, void*
                       n * p.kscale_row, B, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess && p.sel)
         e = hipMemcpyAsync(h + p.codes + p.scales + p.keys + p.kscales, g->sel, p.sel, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && p.pool)
+        e = hipMemcpyAsync(h + p.codes + p.scales + p.keys + p.kscales + p.sel, g->pool, p.pool,
+                           hipMemcpyDeviceToHost, s);
     return hip_status(e);
 }
 
 csa2_status csa2_group_restore(csa2_group* g, const void* host, size_t bytes, void* stream) {
     ImageParts p;
     if (!image_parts(g, &p) || !host || !g->codes || !g->scales || !g->ikeys || (p.sel && !g->sel) ||
-        (p.kscales && !g->ikey_scales))
+        (p.kscales && !g->ikey_scales) || (p.pool && !g->pool))
         return CSA2_ERR_INVALID_ARG;
     if (bytes < p.total) return CSA2_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -567,6 +644,9 @@ csa2_status csa2_group_restore(csa2_group* g, const void* host, size_t bytes, vo
                       n * p.kscale_row, B, hipMemcpyHostToDevice, s);
     if (e == hipSuccess && p.sel)
         e = hipMemcpyAsync(g->sel, h + p.codes + p.scales + p.keys + p.kscales, p.sel, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && p.pool)
+        e = hipMemcpyAsync(g->pool, h + p.codes + p.scales + p.keys + p.kscales + p.sel, p.pool,
+                           hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return CSA2_ERR_HIP;
     g->has_entries = 1;
     return CSA2_OK;

@@ -39,11 +39,31 @@ struct ScoreArgs {
     float* scores;        // [R][ld]
     int64_t ld;
     uint32_t* hist;       // [R][4096] or null
+    // hierarchical search: score the positions of a candidate pool instead of
+    // 0..N-1.  Slot s of row r is position 8 * pool[r][s / 8] + s % 8 (pool blocks
+    // ascending, -1 padded); N is then 8 * pool_blocks and the row's valid slots
+    // are the prefix 0 .. pool_nv[r] - 1.
+    const int32_t* pool = nullptr;
+    int pool_blocks = 0;
+    const int32_t* pool_nv = nullptr;
     // filled by launch_score_exact: with several query rows per sequence the
     // blocks of one entry block and all its rows run together on one XCD
     int64_t n_eblk = 0, blocks = 0, per_xcd = 0;
 };
 hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t stream);
+
+// Hierarchical search helpers (pool.hip), positions grouped in blocks of 8.
+constexpr int kPoolBlock = 8;
+// bmax[r][j] = largest score among the valid positions 8j .. 8j+7 of row r
+// (valid count as for TopkArgs: nvb and Qs, or N when nvb is null); blk_nv[r] =
+// number of blocks holding a valid position.
+hipError_t launch_block_max(const float* scores, int64_t R, int64_t N, int64_t ld, const int32_t* nvb,
+                            int Qs, float* bmax, int64_t ld_blk, int32_t* blk_nv, hipStream_t stream);
+// pool_nv[r] = number of leading slots of row r's pool whose position is valid.
+hipError_t launch_pool_count(const int32_t* pool, int64_t R, int P, const int32_t* nvb, int Qs,
+                             int32_t* pool_nv, hipStream_t stream);
+// idx[r][j] (a slot of row r's pool, or -1) becomes the position it stands for.
+hipError_t launch_pool_map(int32_t* idx, int64_t R, int k, const int32_t* pool, int P, hipStream_t stream);
 
 // S3: top-k over scores [R][ld] with per-row valid counts nv(r) as above (Qs,
 // nvb) and k.  hist must already hold the digit histogram of each row's valid

@@ -64,10 +64,20 @@ CSA2_DEV uint32_t pk_min_u16(uint32_t a, uint32_t b) {
 }
 
 CSA2_DEV int64_t row_valid(const ScoreArgs& a, int64_t r) {
+    if (a.pool) {
+        const int64_t v = a.pool_nv[r];
+        return v < 0 ? 0 : (v > a.N ? a.N : v);
+    }
     if (!a.nvb) return a.N;
     const int64_t b = r / a.Qs, i = r % a.Qs;
     int64_t nv = (int64_t)a.nvb[b] - a.Qs + i + 1;
     return nv < 0 ? 0 : (nv > a.N ? a.N : nv);
+}
+
+// Position scored at slot s of row r: s itself, or in pool mode position
+// 8 * pool[r][s / 8] + s % 8 (a round of 8 slots is one pool block).
+CSA2_DEV int64_t slot_entry(const ScoreArgs& a, int64_t r, int64_t s) {
+    return a.pool ? (int64_t)a.pool[r * a.pool_blocks + (s >> 3)] * kPoolBlock + (s & 7) : s;
 }
 
 // Exponent of the least significant bit of any bf16 value whose magnitude is at
@@ -274,7 +284,8 @@ CSA2_DEV int bf16_pair_emin(uint32_t w) {
 // per chunk).
 // FP4 keys with K = 256 are held to 128 registers (4 waves per SIMD); only the
 // rare exact-recompute path spills.
-template <int DT, int CPL>
+// POOL: the slots are a hierarchical pool's positions (a.pool set).
+template <int DT, int CPL, bool POOL>
 __global__ __launch_bounds__(kScoreThreads, DT == 2 && CPL == 1 ? 4 : 1) void score_exact_kernel(ScoreArgs a) {
     constexpr int EPC = DT == 0 ? 8 : DT == 1 ? 16 : 32;  // key elements per 16-byte chunk
     constexpr int EB = 128 * CPL;         // bytes per entry
@@ -459,8 +470,9 @@ __global__ __launch_bounds__(kScoreThreads, DT == 2 && CPL == 1 ? 4 : 1) void sc
             auto load_round = [&](int t, u32x4(&w)[CPL], float(&ks)[CPL]) __attribute__((always_inline)) {
                 int64_t e = e_wave + t * 8 + g;
                 e = e < nv ? e : nv - 1;
-                const uint8_t* src = kbase + e * EB + sub * 16;
-                const float* sp = a.ik_scales + (b * a.N_cap + e) * (int64_t)(a.K / 32) + sub;
+                const int64_t pe = POOL ? slot_entry(a, r, e) : e;
+                const uint8_t* src = kbase + pe * EB + sub * 16;
+                const float* sp = a.ik_scales + (b * a.N_cap + pe) * (int64_t)(a.K / 32) + sub;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
@@ -481,7 +493,7 @@ __global__ __launch_bounds__(kScoreThreads, DT == 2 && CPL == 1 ? 4 : 1) void sc
                 u32x4 w[CPL];
                 const float ksc[1] = {0.0f};
                 if (e < nv) {
-                    const uint8_t* src = kbase + e * EB + sub * 16;
+                    const uint8_t* src = kbase + (POOL ? slot_entry(a, r, e) : e) * EB + sub * 16;
 #pragma unroll
                     for (int c = 0; c < CPL; ++c)
                         w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
@@ -527,7 +539,8 @@ __global__ __launch_bounds__(kScoreThreads, DT == 2 && CPL == 1 ? 4 : 1) void sc
             while (pend) {
                 const int L = __builtin_ctzll(pend);
                 pend &= pend - 1;
-                const int64_t eL = __builtin_amdgcn_readlane((int)e, L);
+                const int64_t eS = __builtin_amdgcn_readlane((int)e, L);
+                const int64_t eL = POOL ? slot_entry(a, r, eS) : eS;
                 const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.iq) + r * a.K;
                 float x;
                 if (DT == 2)
@@ -562,12 +575,13 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
     const int64_t nv = row_valid(a, r);
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= nv) return;
+    const int64_t pe = slot_entry(a, r, e);
     const int K = a.K;
     double acc = 0.0, aacc = 0.0;
     float qmin = INFINITY, kmin = INFINITY;
     if (a.dtype == 0) {
         const uint16_t* q = reinterpret_cast<const uint16_t*>(a.iq) + r * K;
-        const uint16_t* k = reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + e) * K;
+        const uint16_t* k = reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + pe) * K;
         for (int i = 0; i < K; ++i) {
             const float qf = bf16_to_f32(q[i]), kf = bf16_to_f32(k[i]);
             acc = fma((double)qf, (double)kf, acc);
@@ -579,8 +593,8 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
         // FP4 keys: per 32-element block an fp64 sum of q * e2m1 with its error
         // bound, then one fma with the block scale; aacc bounds every rounding
         const uint16_t* q = reinterpret_cast<const uint16_t*>(a.iq) + r * K;
-        const uint8_t* k = reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * (K / 2);
-        const float* sc = a.ik_scales + (b * a.N_cap + e) * (K / 32);
+        const uint8_t* k = reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + pe) * (K / 2);
+        const float* sc = a.ik_scales + (b * a.N_cap + pe) * (K / 32);
         for (int blk0 = 0; blk0 < K; blk0 += 32) {
             double blk = 0.0, qn1 = 0.0;
             int emin = 1 << 20;
@@ -598,7 +612,7 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
         }
     } else {
         const uint8_t* q = reinterpret_cast<const uint8_t*>(a.iq) + r * K;
-        const uint8_t* k = reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * K;
+        const uint8_t* k = reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + pe) * K;
         for (int i = 0; i < K; ++i) acc = fma(e4m3_to_f64(q[i]), e4m3_to_f64(k[i]), acc);
     }
     float res;
@@ -623,10 +637,10 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
     if (!ok)
         res = a.dtype == 2
                   ? exact_fp4_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * K,
-                                  reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * (K / 2),
-                                  a.ik_scales + (b * a.N_cap + e) * (K / 32), K)
+                                  reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + pe) * (K / 2),
+                                  a.ik_scales + (b * a.N_cap + pe) * (K / 32), K)
                   : exact_bf16_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * K,
-                                   reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + e) * K, K);
+                                   reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + pe) * K, K);
     a.scores[r * a.ld + e] = res;
     if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
 }
@@ -643,22 +657,27 @@ hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
         a.blocks = a.n_eblk * R;
         a.per_xcd = (a.blocks + 7) / 8;
         const dim3 grid = a.Qs == 1 ? dim3((unsigned)a.n_eblk, (unsigned)R) : dim3((unsigned)(8 * a.per_xcd));
-        if (a.dtype == 0) {
-            if (cpl == 1) hipLaunchKernelGGL((score_exact_kernel<0, 1>), grid, dim3(kScoreThreads), 0, stream, a);
-            if (cpl == 2) hipLaunchKernelGGL((score_exact_kernel<0, 2>), grid, dim3(kScoreThreads), 0, stream, a);
-            if (cpl == 4) hipLaunchKernelGGL((score_exact_kernel<0, 4>), grid, dim3(kScoreThreads), 0, stream, a);
-            if (cpl == 8) hipLaunchKernelGGL((score_exact_kernel<0, 8>), grid, dim3(kScoreThreads), 0, stream, a);
-        } else if (a.dtype == 1) {
-            if (cpl == 1) hipLaunchKernelGGL((score_exact_kernel<1, 1>), grid, dim3(kScoreThreads), 0, stream, a);
-            if (cpl == 2) hipLaunchKernelGGL((score_exact_kernel<1, 2>), grid, dim3(kScoreThreads), 0, stream, a);
-            if (cpl == 4) hipLaunchKernelGGL((score_exact_kernel<1, 4>), grid, dim3(kScoreThreads), 0, stream, a);
-            if (cpl == 8) hipLaunchKernelGGL((score_exact_kernel<1, 8>), grid, dim3(kScoreThreads), 0, stream, a);
-        } else {
-            if (cpl == 1) hipLaunchKernelGGL((score_exact_kernel<2, 1>), grid, dim3(kScoreThreads), 0, stream, a);
-            if (cpl == 2) hipLaunchKernelGGL((score_exact_kernel<2, 2>), grid, dim3(kScoreThreads), 0, stream, a);
-            if (cpl == 4) hipLaunchKernelGGL((score_exact_kernel<2, 4>), grid, dim3(kScoreThreads), 0, stream, a);
-            if (cpl == 8) hipLaunchKernelGGL((score_exact_kernel<2, 8>), grid, dim3(kScoreThreads), 0, stream, a);
-        }
+        const bool pool = a.pool != nullptr;
+#define CSA2_SCORE_LAUNCH(DTV, CPLV)                                                                   \
+    if (a.dtype == DTV && cpl == CPLV) {                                                             \
+        if (pool)                                                                                    \
+            hipLaunchKernelGGL((score_exact_kernel<DTV, CPLV, true>), grid, dim3(kScoreThreads), 0, stream, a); \
+        else                                                                                         \
+            hipLaunchKernelGGL((score_exact_kernel<DTV, CPLV, false>), grid, dim3(kScoreThreads), 0, stream, a); \
+    }
+        CSA2_SCORE_LAUNCH(0, 1)
+        CSA2_SCORE_LAUNCH(0, 2)
+        CSA2_SCORE_LAUNCH(0, 4)
+        CSA2_SCORE_LAUNCH(0, 8)
+        CSA2_SCORE_LAUNCH(1, 1)
+        CSA2_SCORE_LAUNCH(1, 2)
+        CSA2_SCORE_LAUNCH(1, 4)
+        CSA2_SCORE_LAUNCH(1, 8)
+        CSA2_SCORE_LAUNCH(2, 1)
+        CSA2_SCORE_LAUNCH(2, 2)
+        CSA2_SCORE_LAUNCH(2, 4)
+        CSA2_SCORE_LAUNCH(2, 8)
+#undef CSA2_SCORE_LAUNCH
     } else {
         dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)R);
         hipLaunchKernelGGL(score_exact_generic_kernel, grid, dim3(256), 0, stream, a);

@@ -98,7 +98,19 @@ typedef struct csa2_group {
     int32_t sel_qs;           /* Qs of the stored selection                         */
     float* ikey_scales;       /* FP4_E2M1 keys only: [B][N_cap][H_I*d_I/32] scales;
                                  ikeys then holds the codes [B][N_cap][H_I*d_I/2] */
+    /* Hierarchical search ("Inference-Efficient LLMs", section 5): with
+     * pool_blocks = P > 0 a Full layer also keeps, per query row, the P blocks of
+     * CSA2_POOL_BLOCK consecutive entries whose largest index score ranks first
+     * (ties to the lower block; blocks ascending, -1 padded), and Reindex layers
+     * score and select only among the pool's valid entries.  P = 0: every
+     * selecting layer searches all entries.  Requires k <= P * CSA2_POOL_BLOCK. */
+    int32_t pool_blocks;
+    int32_t* pool;            /* [sel_rows][pool_blocks] block indices (library-written) */
+    int32_t has_pool;         /* set by Full when pool_blocks > 0                   */
+    int32_t pool_qs;          /* Qs of the stored pool                              */
 } csa2_group;
+
+#define CSA2_POOL_BLOCK 8
 
 /* Per-layer inputs.  Every mode uses its own queries and window ("every layer
  * keeps its own queries and its own local-window state"). */
@@ -179,8 +191,12 @@ csa2_status csa2_sparse_attend(const void* q, int32_t B, int32_t Qs, int32_t Hq,
  * cache across layers"; "Why Is DeepSeek V4.1 Flash So Fast?", section 5):
  *   FULL    packs new_entry/new_ikey into slots n_valid-Qs .. n_valid-1,
  *           scores the group's keys with iq, selects into g->sel, attends;
+ *           with pool_blocks > 0 it also writes the pool (g->pool);
  *   REINDEX scores the shared keys with its own iq, overwrites g->sel, attends;
  *           writes no entries (CSA2_ERR_STATE if g->has_entries == 0);
+ *           with pool_blocks > 0 it scores only the entries of the pool the
+ *           latest Full left and leaves the pool as it is (CSA2_ERR_STATE if
+ *           g->has_pool == 0 or g->pool_qs != Qs);
  *   REUSE   attends with g->sel as left by the latest Full/Reindex of the
  *           group; writes neither entries nor the selection (CSA2_ERR_STATE if
  *           g->has_selection == 0 or g->sel_qs != Qs).
@@ -206,12 +222,13 @@ int64_t csa2_cache_bytes(int64_t entries, int64_t numbers, int64_t copies, int64
  *   scales [B][n_valid_max][D/32]    f32
  *   ikeys  [B][n_valid_max][H_I][d_I] in idx_dtype (FP4: codes [..][H_I*d_I/2])
  *   ikey_scales [B][n_valid_max][H_I*d_I/32] f32, FP4 index keys only
- *   sel    [B*sel_qs][k]             i32, only when has_selection is set.
+ *   sel    [B*sel_qs][k]             i32, only when has_selection is set
+ *   pool   [B*pool_qs][pool_blocks]  i32, only when has_pool is set.
  * csa2_group_image_bytes returns its size (0 for an invalid group).
  * csa2_group_save copies the group into `host` (bytes >= the image size;
  * CSA2_ERR_STATE if the group holds no entries).  csa2_group_restore copies an
- * image back into a group of the same geometry, n_valid_max, has_selection and
- * sel_qs, and sets has_entries.  Both are asynchronous on `stream`: the host
+ * image back into a group of the same geometry, n_valid_max, has_selection,
+ * sel_qs, has_pool and pool_qs, and sets has_entries.  Both are asynchronous on `stream`: the host
  * buffer must stay alive until the stream reaches them, and it should be
  * pinned (page-locked) for the copies to run at full rate.  Copy failures
  * return CSA2_ERR_HIP; nothing is validated against the image's contents. */

@@ -10,6 +10,8 @@ Shapes follow the workload list this implementation is measured on:
       the drafts (query i of the block sees the entries up to its own)
   w7  w2 with FP4 index keys: e2m1 codes with an fp32 scale per 32 elements (the cache
       codec), bf16 index queries
+  w8  w2 with hierarchical search: Full keeps a pool of 2,048 blocks of 8 entries
+      (16,384 candidates) per query row, Reindex searches only the pool
 Every layer: 16 bf16 query heads of dim 128, scale 1/sqrt(128), a 128-row bf16 window,
 entries of dim 128 stored as FP4 e2m1 with an fp32 scale per 32 elements.
 
@@ -47,6 +49,7 @@ class Workload:
     Hq: int = 16
     D: int = 128
     W: int = 128
+    pool_blocks: int = 0  # > 0: hierarchical search with a pool of that many 8-entry blocks
 
     @property
     def sm_scale(self) -> float:
@@ -86,4 +89,6 @@ W6 = Workload(6, "verify5_b32_n65536_group_F_Ri_Ru_Ru", B=32, N=65536, H_I=4, d_
 W7 = Workload(7, "decode_b32_n65536_group_F_Ri_Ru_Ru_fp4idx", B=32, N=65536, H_I=4, d_I=64,
               idx_dtype="fp4", k=2048, pattern=("F", "Ri", "Ru", "Ru"))
 
-ALL = {1: W1, 2: W2, 3: W3, 4: W4, 5: W5, 6: W6, 7: W7}
+W8 = Workload(8, "decode_b32_n65536_group_F_Ri_Ru_Ru_hier", B=32, N=65536, H_I=4, d_I=64,
+              idx_dtype="bf16", k=2048, pattern=("F", "Ri", "Ru", "Ru"), pool_blocks=2048)
+ALL = {1: W1, 2: W2, 3: W3, 4: W4, 5: W5, 6: W6, 7: W7, 8: W8}

@@ -164,3 +164,20 @@ def test_fp4_index_keys_validation_and_image():
     g = _group(idx_dtype=2, ikey_scales=FAKE, n_valid_max=10)
     per_entry = 128 // 2 + 128 // 32 * 4 + 4 * 64 // 2 + 4 * 64 // 32 * 4
     assert L.csa2_group_image_bytes(ctypes.byref(g)) == 2 * 10 * per_entry
+
+
+def test_hierarchical_pool_validation_and_image():
+    # a pool needs room for k entries, at most one block per 8 cache slots, and a buffer
+    assert _step(0, _group(pool_blocks=-1), _args()) == csa2.ERR_INVALID_ARG
+    assert _step(0, _group(pool_blocks=7, pool=FAKE), _args()) == csa2.ERR_INVALID_ARG    # 56 < k = 64
+    assert _step(0, _group(pool_blocks=126, pool=FAKE), _args()) == csa2.ERR_INVALID_ARG  # > 1000/8 blocks
+    assert _step(0, _group(pool_blocks=8), _args()) == csa2.ERR_INVALID_ARG               # no pool buffer
+    # Reindex in a hierarchical group needs the pool of a Full layer with the same Qs
+    assert _step(1, _group(pool_blocks=8, pool=FAKE), _args()) == csa2.ERR_STATE
+    assert _step(1, _group(pool_blocks=8, pool=FAKE, has_pool=1, pool_qs=2), _args()) == csa2.ERR_STATE
+    L = csa2.lib()
+    g = _group(n_valid_max=10, has_selection=1, sel_qs=1, pool_blocks=8, pool=FAKE, has_pool=1, pool_qs=1)
+    per_entry = 128 // 2 + 128 // 32 * 4 + 4 * 64 * 2
+    assert L.csa2_group_image_bytes(ctypes.byref(g)) == 2 * 10 * per_entry + 2 * 64 * 4 + 2 * 8 * 4
+    assert L.csa2_group_save(ctypes.byref(_group(has_pool=1, pool_qs=1, pool_blocks=8)), FAKE, 10 ** 9,
+                             None) == csa2.ERR_INVALID_ARG  # image with a pool needs the buffer

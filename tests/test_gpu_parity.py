@@ -11,7 +11,7 @@ import compressed_kv_cache_03_amd as csa2
 import oracle
 import synth
 from cases import make_inputs, rel_err
-from synth.workloads import W1, W2, W3, W4, W5, W6, W7
+from synth.workloads import W1, W2, W3, W4, W5, W6, W7, W8
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -275,9 +275,10 @@ class Run:
                 g_keys, g_ks = dev(self.inp.ikeys[g]), None
             self.g_orc.append(oracle.Group(oc.reshape(B, N, D // 2), os_.reshape(B, N, D // 32), o_keys,
                                            self.inp.n_valid.astype(np.int64), wl.idx_dtype, wl.k,
-                                           max_rows=B * wl.Qs, ikey_scales=o_ks))
+                                           max_rows=B * wl.Qs, ikey_scales=o_ks,
+                                           pool_blocks=wl.pool_blocks))
             self.g_gpu.append(csa2.Group(gc, gs, g_keys, dev(self.inp.n_valid), wl.idx_dtype, wl.k,
-                                         sel_rows=B * wl.Qs, ikey_scales=g_ks))
+                                         sel_rows=B * wl.Qs, ikey_scales=g_ks, pool_blocks=wl.pool_blocks))
 
     def layer(self, li):
         L = self.inp.layers[li]
@@ -309,6 +310,9 @@ class Run:
                 assert bits_eq(host(self.g_gpu[g].ikeys), self.g_orc[g].ikeys)
                 if self.g_orc[g].ikey_scales is not None:
                     assert bits_eq(host(self.g_gpu[g].ikey_scales), self.g_orc[g].ikey_scales)
+                if self.wl.pool_blocks:
+                    R, P = self.wl.B * self.wl.Qs, self.wl.pool_blocks
+                    assert np.array_equal(host(self.g_gpu[g].pool)[:R, :P], self.g_orc[g].pool[:R, :P])
 
 
 def test_layer_step_w1_full_size():
@@ -355,8 +359,59 @@ def test_group_save_restore_resumes_bitwise():
         assert bits_eq(go, ref_out[li][0]) and bits_eq(gl, ref_out[li][1]), li
 
 
+def test_hierarchical_group_save_restore_keeps_the_pool():
+    # saved after Full: the image carries the pool, and the Reindex that follows
+    # the restore searches the same pool as an uninterrupted run
+    wl = W8.scaled(B=2, N=3000, k=200, pool_blocks=50)
+    nv = [3000, 2500]
+    ref = Run(wl, n_valid=nv)
+    ref_res = [ref.layer(li) for li in range(2)]
+    ref_sel = host(ref.g_gpu[0].sel).copy()
+    run = Run(wl, n_valid=nv)
+    run.layer(0)
+    g = run.g_gpu[0]
+    pool_before = host(g.pool).copy()
+    image = g.save()
+    torch.cuda.synchronize()
+    assert image.numel() == g.image_bytes()
+    g.pool.fill_(-3)
+    g.sel.fill_(-7)
+    g.restore(image)
+    torch.cuda.synchronize()
+    assert bits_eq(host(g.pool), pool_before)
+    mode, _, _, _, go, gl = run.layer(1)
+    assert mode == "Ri"
+    assert np.array_equal(host(g.sel), ref_sel)
+    assert bits_eq(go, ref_res[1][4]) and bits_eq(gl, ref_res[1][5])
+
+
 def test_w7_scaled_fp4_index_keys():
     Run(W7.scaled(B=3, N=6000, k=600), n_valid=[6000, 4097, 5555]).check_all()
+
+
+def test_w8_scaled_hierarchical_ragged():
+    # 125 blocks of 8 per row, 60 kept: Reindex ranks 480 candidates
+    Run(W8.scaled(B=3, N=1000, k=100, pool_blocks=60), n_valid=[1000, 411, 999]).check_all()
+
+
+def test_w8_hierarchical_pool_covers_every_block():
+    Run(W8.scaled(B=2, N=800, k=64, pool_blocks=100), n_valid=[800, 123]).check_all()
+
+
+def test_w8_hierarchical_all_scores_equal():
+    # equal keys: every block ties, the pool is the first blocks and Reindex the first entries
+    Run(W8.scaled(B=2, N=2000, k=50, pool_blocks=20), n_valid=[2000, 1501],
+        ikeys=lambda g, k: np.full_like(k, k.flat[0])).check_all()
+
+
+def test_w8_hierarchical_fp4_keys_and_draft_rows():
+    Run(W8.scaled(B=2, N=3000, k=120, pool_blocks=40, idx_dtype="fp4"), n_valid=[3000, 2222]).check_all()
+    Run(W8.scaled(B=2, N=3000, k=120, pool_blocks=40, Qs=5), n_valid=[3000, 1999]).check_all()
+
+
+def test_w8_pool_size_layer_step():
+    # the real pool (2,048 blocks = 16,384 candidates) over 20,000 entries
+    Run(W8.scaled(B=2, N=20000), n_valid=[20000, 17003]).check_all()
 
 
 def test_verify5_w6_scaled():
