@@ -6,7 +6,8 @@
 //   * block_max_kernel: the block scores a Full layer ranks (one thread per
 //     block, 32 bytes of scores each);
 //   * pool_count_kernel: the number of leading pool slots whose position is
-//     valid (one workgroup per row, a minimum over the first invalid slot);
+//     valid (one workgroup per row, a minimum over each block's first invalid
+//     slot);
 //   * pool_map_kernel: a selection of pool slots becomes a selection of
 //     positions.
 // The ranking itself is the ordinary top-k (topk.hip) on block scores or on the
@@ -52,12 +53,13 @@ __global__ __launch_bounds__(256) void pool_count_kernel(const int32_t* pool, in
     const int64_t r = blockIdx.x;
     const int64_t nv = causal_valid(nvb, Qs, INT64_MAX, r);
     const int32_t* row = pool + r * P;
-    const int S = P * kPoolBlock;
-    int first = S;  // first slot whose position is not valid
-    for (int s = threadIdx.x; s < S; s += 256) {
-        const int32_t blk = row[s / kPoolBlock];
-        const bool ok = blk >= 0 && (int64_t)blk * kPoolBlock + s % kPoolBlock < nv;
-        if (!ok) first = min(first, s);
+    int first = P * kPoolBlock;  // first slot whose position is not valid
+#pragma unroll 8
+    for (int j = threadIdx.x; j < P; j += 256) {
+        // block j's slots 8j .. 8j+7 hold positions 8*blk .. 8*blk+7
+        const int32_t blk = row[j];
+        const int64_t room = blk < 0 ? 0 : nv - (int64_t)blk * kPoolBlock;
+        if (room < kPoolBlock) first = min(first, j * kPoolBlock + (int)(room > 0 ? room : 0));
     }
     __shared__ int red[4];
 #pragma unroll

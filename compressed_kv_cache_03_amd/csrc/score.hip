@@ -290,12 +290,11 @@ __global__ __launch_bounds__(kScoreThreads, DT == 2 && CPL == 1 ? 4 : 1) void sc
     constexpr int EPC = DT == 0 ? 8 : DT == 1 ? 16 : 32;  // key elements per 16-byte chunk
     constexpr int EB = 128 * CPL;         // bytes per entry
     int64_t r, e_block;
-    if (a.Qs == 1) {
-        r = blockIdx.y;
-        e_block = (int64_t)blockIdx.x * kScoreEntriesPerBlock;
-    } else {
-        // block w takes t = (w % 8) * per_xcd + w / 8: the Qs rows of a sequence
-        // for one entry block are consecutive t on one XCD and share its L2
+    {
+        // block w takes t = (w % 8) * per_xcd + w / 8: each XCD gets a run of
+        // consecutive t, so the Qs rows of a sequence for one entry block share
+        // its L2, and with Qs = 1 a row's scores land in one XCD's L2, where its
+        // top-k workgroup reads them
         const int64_t w = blockIdx.x;
         const int64_t t = (w & 7) * a.per_xcd + (w >> 3);
         if (t >= a.blocks) return;
@@ -656,7 +655,7 @@ hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
         a.n_eblk = (a.N + kScoreEntriesPerBlock - 1) / kScoreEntriesPerBlock;
         a.blocks = a.n_eblk * R;
         a.per_xcd = (a.blocks + 7) / 8;
-        const dim3 grid = a.Qs == 1 ? dim3((unsigned)a.n_eblk, (unsigned)R) : dim3((unsigned)(8 * a.per_xcd));
+        const dim3 grid((unsigned)(8 * a.per_xcd));
         const bool pool = a.pool != nullptr;
 #define CSA2_SCORE_LAUNCH(DTV, CPLV)                                                                   \
     if (a.dtype == DTV && cpl == CPLV) {                                                             \
