@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     // so its latency overlaps the histogram's
     const int64_t nv4 = (reinterpret_cast<uintptr_t>(s) & 15) == 0 ? nv / 4 : 0;
     const float4* s4 = reinterpret_cast<const float4*>(s);
-    constexpr int U = 16;  // 16-byte loads per thread per batch: 64K entries
+    constexpr int U = 8;  // 16-byte loads per thread per batch: 32K entries
     float4 v[U];
     auto load_batch = [&](int64_t q0) {
 #pragma unroll
@@ -301,19 +301,61 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
             }
         }
     };
+    // The aligned part, one batch at a time, with no LDS atomics: a wave's 64
+    // lanes hold 256 consecutive entries, so each bitmap word of entries above
+    // bin b1 belongs to 8 lanes and is built with an OR across them and stored
+    // once; the threshold bin's entries are counted per thread and placed in
+    // the candidate list by a block scan.
+    const int lane = threadIdx.x & 63;
+    uint32_t cbase = 0;  // candidates placed by earlier batches
     for (int64_t q0 = 0; q0 < nv4; q0 += (int64_t)U * kRowThreads) {
         if (q0 > 0) load_batch(q0);
+        uint32_t cm[U / 8] = {};  // bit 4u + c (mod 32): component c of load u lies in bin b1
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t q = q0 + u * kRowThreads + threadIdx.x;
-            if (q < nv4) {
-                visit(sort_key(v[u].x), 4 * q);
-                visit(sort_key(v[u].y), 4 * q + 1);
-                visit(sort_key(v[u].z), 4 * q + 2);
-                visit(sort_key(v[u].w), 4 * q + 3);
+            const bool ok = q < nv4;
+            const float x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            uint32_t nib = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t d = sort_key(x4[c]) >> (32 - kHistBits);
+                nib |= (ok && d > b1) ? 1u << c : 0u;
+                cm[u / 8] |= (ok && in_lds && d == b1) ? 1u << (4 * (u % 8) + c) : 0u;
+            }
+            uint32_t word = nib << (4 * (lane & 7));
+            word |= (uint32_t)__builtin_amdgcn_ds_swizzle((int)word, (1 << 10) | 0x1f);
+            word |= (uint32_t)__builtin_amdgcn_ds_swizzle((int)word, (2 << 10) | 0x1f);
+            word |= (uint32_t)__builtin_amdgcn_ds_swizzle((int)word, (4 << 10) | 0x1f);
+            if (ok && (lane & 7) == 0) s_bits[(4 * q) >> 5] = word;
+        }
+        uint32_t mine = 0;
+#pragma unroll
+        for (int i = 0; i < U / 8; ++i) mine += __popc(cm[i]);
+        uint32_t batch_total;
+        uint32_t pos = cbase + block_exclusive_scan(mine, scan_lds, &batch_total);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t m4 = (cm[u / 8] >> (4 * (u % 8))) & 15u;
+            if (m4) {
+                const int64_t q = q0 + u * kRowThreads + threadIdx.x;
+                const float x4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if ((m4 >> c) & 1u) {
+                        if (pos < (uint32_t)kRowCand) {  // always, given the histogram of these scores
+                            s_ckey[pos] = sort_key(x4[c]);
+                            s_cidx[pos] = (int32_t)(4 * q + c);
+                        }
+                        ++pos;
+                    }
+                }
             }
         }
+        cbase += batch_total;
     }
+    if (threadIdx.x == 0) s_ncand = cbase;
+    __syncthreads();  // words stored whole above; the tail below ORs into them
     for (int64_t j = 4 * nv4 + threadIdx.x; j < nv; j += kRowThreads) visit(sort_key(s[j]), j);
     __syncthreads();
     const uint32_t C = min(s_ncand, (uint32_t)kRowCand);
