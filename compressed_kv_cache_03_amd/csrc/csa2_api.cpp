@@ -408,16 +408,28 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
     const int K = g->H_I * g->d_I;
     hipError_t e = hipSuccess;
 
+    const bool exact_select = selects && !mfma_prefill(g, Qs);
     if (mode == CSA2_MODE_FULL) {
-        // S1: the step's new rows go to slots n_valid-Qs .. n_valid-1
-        e = launch_fp4_pack(a->new_entry, R, g->D, g->codes, g->scales, g->n_valid, Qs, g->N_cap, s);
-        if (e == hipSuccess)
-            e = g->idx_dtype == CSA2_IDX_FP4_E2M1
-                    ? launch_fp4_pack(static_cast<const float*>(a->new_ikey), R, K,
-                                      static_cast<uint8_t*>(g->ikeys), g->ikey_scales, g->n_valid, Qs,
-                                      g->N_cap, s)
-                    : launch_store_rows(a->new_ikey, R, (int)key_row_bytes(g->idx_dtype, K), g->ikeys,
-                                        g->n_valid, Qs, g->N_cap, s);
+        // S1: the step's new rows go to slots n_valid-Qs .. n_valid-1, with their
+        // index keys; the same launch zeroes the digit histogram of the scoring
+        FullPrepArgs fp{};
+        fp.entry = a->new_entry;
+        fp.rows = R;
+        fp.D = g->D;
+        fp.codes = g->codes;
+        fp.scales = g->scales;
+        fp.key = a->new_ikey;
+        fp.key_fp4 = g->idx_dtype == CSA2_IDX_FP4_E2M1;
+        fp.K = K;
+        fp.key_words = (int)(key_row_bytes(g->idx_dtype, K) / 4);
+        fp.ikeys = g->ikeys;
+        fp.ikey_scales = g->ikey_scales;
+        fp.nvb = g->n_valid;
+        fp.Qs = Qs;
+        fp.N_cap = g->N_cap;
+        fp.zero = exact_select ? at<uint32_t>(ws, L.hist) : nullptr;
+        fp.zero_words = exact_select ? R * kHistBinsHost : 0;
+        e = launch_full_prep(fp, s);
     }
     if (e == hipSuccess && selects && mfma_prefill(g, Qs)) {
         // S2 + S3 for a prefill chunk: sampled thresholds, MFMA score GEMM with a
@@ -527,7 +539,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
             t.slice_len = topk_slice_len(g->N_cap);
         }
         t.slices = (int)((t.N + t.slice_len - 1) / t.slice_len);
-        if (e == hipSuccess) e = launch_zero(t.hist, R * kHistBinsHost, s);
+        if (e == hipSuccess && mode != CSA2_MODE_FULL) e = launch_zero(t.hist, R * kHistBinsHost, s);
         if (e == hipSuccess) e = launch_score_exact(sa, s);
         if (e == hipSuccess) e = launch_topk_select(t, s);
         // the selection holds pool slots: turn them into entries

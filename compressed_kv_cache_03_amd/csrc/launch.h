@@ -12,6 +12,27 @@ constexpr int kHistBitsHost = 12;
 constexpr int64_t kHistBinsHost = 1 << kHistBitsHost;  // first radix digit bins per row
 
 // Zero `words` uint32 words (a plain fill kernel, safe inside graph capture).
+// A Full layer's writes before scoring in one launch (pack.hip): entries,
+// their index keys and the zeroed digit histogram.
+struct FullPrepArgs {
+    const float* entry;    // fp32 [rows][D]
+    int64_t rows;
+    int D;
+    uint8_t* codes;
+    float* scales;
+    const void* key;       // [rows][K] stored as is (key_words u32 each) or fp32 to pack
+    int key_fp4;
+    int K, key_words;
+    void* ikeys;
+    float* ikey_scales;
+    const int32_t* nvb;
+    int Qs;
+    int64_t N_cap;
+    uint32_t* zero;
+    int64_t zero_words;
+    int64_t nb_pack = 0, nb_key = 0;  // filled by launch_full_prep
+};
+hipError_t launch_full_prep(const FullPrepArgs& a, hipStream_t stream);
 hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t stream);
 
 // S1: see pack.hip for the row -> slot mapping when nvb != nullptr.

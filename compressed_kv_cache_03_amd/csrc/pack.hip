@@ -32,13 +32,10 @@ CSA2_DEV uint32_t e2m1_mag_code(double a, double s) {
 //   dst = r                                  when nvb == nullptr,
 //   dst = b*N_cap + nvb[b] - Qs + i          with r = b*Qs + i otherwise
 // (the Full-mode write of a step's new rows at slots n_valid-Qs .. n_valid-1).
-__global__ __launch_bounds__(256) void fp4_pack_kernel(const float* __restrict__ x, int64_t rows,
-                                                       int dim, uint8_t* __restrict__ codes,
-                                                       float* __restrict__ scales,
-                                                       const int32_t* __restrict__ nvb, int Qs,
-                                                       int64_t N_cap) {
+CSA2_DEV void fp4_pack_lane(int64_t gid, const float* __restrict__ x, int64_t rows, int dim,
+                             uint8_t* __restrict__ codes, float* __restrict__ scales,
+                             const int32_t* __restrict__ nvb, int Qs, int64_t N_cap) {
     const int lanes_per_row = dim / 8;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = rows * lanes_per_row;
     // every lane of a 4-lane block group must take part in the swizzles
     const bool active = gid < total;
@@ -79,6 +76,14 @@ __global__ __launch_bounds__(256) void fp4_pack_kernel(const float* __restrict__
     if ((part & 3) == 0) scales[dst * (dim / 32) + part / 4] = scale;
 }
 
+__global__ __launch_bounds__(256) void fp4_pack_kernel(const float* __restrict__ x, int64_t rows,
+                                                       int dim, uint8_t* __restrict__ codes,
+                                                       float* __restrict__ scales,
+                                                       const int32_t* __restrict__ nvb, int Qs,
+                                                       int64_t N_cap) {
+    fp4_pack_lane((int64_t)blockIdx.x * blockDim.x + threadIdx.x, x, rows, dim, codes, scales, nvb, Qs, N_cap);
+}
+
 hipError_t launch_fp4_pack(const float* x, int64_t rows, int dim, uint8_t* codes, float* scales,
                            const int32_t* nvb, int Qs, int64_t N_cap, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
@@ -90,11 +95,9 @@ hipError_t launch_fp4_pack(const float* x, int64_t rows, int dim, uint8_t* codes
 }
 
 // Index keys of the new rows go next to their entries (same slot mapping).
-__global__ __launch_bounds__(256) void store_rows_kernel(const uint32_t* __restrict__ src, int64_t rows,
-                                                         int row_words, uint32_t* __restrict__ dst,
-                                                         const int32_t* __restrict__ nvb, int Qs,
-                                                         int64_t N_cap) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+CSA2_DEV void store_rows_lane(int64_t gid, const uint32_t* __restrict__ src, int64_t rows, int row_words,
+                               uint32_t* __restrict__ dst, const int32_t* __restrict__ nvb, int Qs,
+                               int64_t N_cap) {
     if (gid >= rows * row_words) return;
     const int64_t r = gid / row_words, w = gid % row_words;
     int64_t drow = r;
@@ -105,6 +108,13 @@ __global__ __launch_bounds__(256) void store_rows_kernel(const uint32_t* __restr
         drow = b * N_cap + slot;
     }
     dst[drow * row_words + w] = src[gid];
+}
+
+__global__ __launch_bounds__(256) void store_rows_kernel(const uint32_t* __restrict__ src, int64_t rows,
+                                                         int row_words, uint32_t* __restrict__ dst,
+                                                         const int32_t* __restrict__ nvb, int Qs,
+                                                         int64_t N_cap) {
+    store_rows_lane((int64_t)blockIdx.x * blockDim.x + threadIdx.x, src, rows, row_words, dst, nvb, Qs, N_cap);
 }
 
 hipError_t launch_store_rows(const void* src, int64_t rows, int row_bytes, void* dst,
@@ -122,6 +132,40 @@ __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
          i += (int64_t)gridDim.x * blockDim.x)
         p[i] = 0u;
+}
+
+// A Full layer's writes before scoring, in one launch: the new entries' FP4
+// records, their index keys (stored, or FP4-packed with their own scales) and
+// the zeroed digit histogram.  Blocks [0, nb_pack) pack entries, the next
+// nb_key blocks write keys, the rest zero the histogram.
+__global__ __launch_bounds__(256) void full_prep_kernel(FullPrepArgs a) {
+    const int64_t blk = blockIdx.x;
+    if (blk < a.nb_pack) {
+        fp4_pack_lane(blk * 256 + threadIdx.x, a.entry, a.rows, a.D, a.codes, a.scales, a.nvb, a.Qs, a.N_cap);
+    } else if (blk < a.nb_pack + a.nb_key) {
+        const int64_t gid = (blk - a.nb_pack) * 256 + threadIdx.x;
+        if (a.key_fp4)
+            fp4_pack_lane(gid, static_cast<const float*>(a.key), a.rows, a.K, static_cast<uint8_t*>(a.ikeys),
+                          a.ikey_scales, a.nvb, a.Qs, a.N_cap);
+        else
+            store_rows_lane(gid, static_cast<const uint32_t*>(a.key), a.rows, a.key_words,
+                            static_cast<uint32_t*>(a.ikeys), a.nvb, a.Qs, a.N_cap);
+    } else {
+        const int64_t first = blk - a.nb_pack - a.nb_key, nz = gridDim.x - a.nb_pack - a.nb_key;
+        for (int64_t i = first * 256 + threadIdx.x; i < a.zero_words; i += nz * 256) a.zero[i] = 0u;
+    }
+}
+
+hipError_t launch_full_prep(const FullPrepArgs& args, hipStream_t stream) {
+    FullPrepArgs a = args;
+    a.nb_pack = (a.rows * (a.D / 8) + 255) / 256;
+    a.nb_key = a.key_fp4 ? (a.rows * (a.K / 8) + 255) / 256 : (a.rows * a.key_words + 255) / 256;
+    int64_t nz = (a.zero_words + 255) / 256;
+    if (nz > 1024) nz = 1024;
+    if (nz < 1) nz = 1;
+    const int64_t blocks = a.nb_pack + a.nb_key + nz;
+    hipLaunchKernelGGL(full_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t stream) {
