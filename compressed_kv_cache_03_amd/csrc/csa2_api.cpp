@@ -33,7 +33,10 @@ int score_dtype(csa2_idx_dtype dt) { return dt == CSA2_IDX_BF16 ? 0 : dt == CSA2
 
 // Workspace carve-up shared by all entry points.  Offsets are 256-byte aligned.
 struct Layout {
-    size_t hist = 0, hist_bytes = 0;     // [R][4096] u32 (zeroed per selection)
+    size_t hist = 0, hist_bytes = 0;     // [R][4096] u32 (zeroed per selection), then the
+                                         // undecided-score counter (zeroed with it)
+    size_t fix_list = 0;                 // [R][N] (row, entry) queue of the draft-row scorer
+    bool rows_scorer = false;
     size_t scores = 0;                   // [R][N] f32
     size_t cand_idx = 0, cand_key = 0;   // [R][N]
     size_t slice_cnt = 0;                // [R][slices]
@@ -69,7 +72,7 @@ struct TopkShape {
 void add_topk(Layout& L, size_t& off, const TopkShape& t) {
     L.hist = off;
     L.hist_bytes = (size_t)t.R * kHistBinsHost * 4;
-    off = align_up(off + L.hist_bytes);
+    off = align_up(off + L.hist_bytes + 4);
     L.cand_idx = off;
     off = align_up(off + (size_t)t.R * t.N * 4);
     L.cand_key = off;
@@ -128,6 +131,13 @@ Layout layer_layout(const csa2_group* g, int Qs, int Hq, int W) {
         for (int64_t n : {N, block_count(N), pool_slots(g)})
             if (n > 0) slices = std::max(slices, (n + topk_slice_len(n) - 1) / topk_slice_len(n));
         add_topk(L, off, TopkShape{R, L.ld_scores, slices});
+        // several bf16 query rows per sequence share each key load (score.hip)
+        const int K = g->H_I * g->d_I;
+        L.rows_scorer = Qs >= 2 && g->idx_dtype == CSA2_IDX_BF16 && (K == 128 || K == 256);
+        if (L.rows_scorer) {
+            L.fix_list = off;
+            off = align_up(off + (size_t)R * N * 8);
+        }
     }
     L.part = off;
     off = align_up(off + attend_part_bytes(R, Hq, g->D, g->k, W));
@@ -428,7 +438,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         fp.Qs = Qs;
         fp.N_cap = g->N_cap;
         fp.zero = exact_select ? at<uint32_t>(ws, L.hist) : nullptr;
-        fp.zero_words = exact_select ? R * kHistBinsHost : 0;
+        fp.zero_words = exact_select ? R * kHistBinsHost + 1 : 0;  // histogram and queue counter
         e = launch_full_prep(fp, s);
     }
     if (e == hipSuccess && selects && mfma_prefill(g, Qs)) {
@@ -520,6 +530,10 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         sa.scores = scores;
         sa.ld = L.ld_scores;
         sa.hist = t.hist;
+        if (L.rows_scorer) {
+            sa.fix_cnt = t.hist + R * kHistBinsHost;
+            sa.fix_list = at<uint2>(ws, L.fix_list);
+        }
         if (in_pool) {
             int32_t* pool_nv = at<int32_t>(ws, L.pool_nv);
             e = launch_pool_count(g->pool, R, g->pool_blocks, g->n_valid, Qs, pool_nv, s);
@@ -539,7 +553,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
             t.slice_len = topk_slice_len(g->N_cap);
         }
         t.slices = (int)((t.N + t.slice_len - 1) / t.slice_len);
-        if (e == hipSuccess && mode != CSA2_MODE_FULL) e = launch_zero(t.hist, R * kHistBinsHost, s);
+        if (e == hipSuccess && mode != CSA2_MODE_FULL) e = launch_zero(t.hist, R * kHistBinsHost + 1, s);
         if (e == hipSuccess) e = launch_score_exact(sa, s);
         if (e == hipSuccess) e = launch_topk_select(t, s);
         // the selection holds pool slots: turn them into entries

@@ -67,6 +67,11 @@ struct ScoreArgs {
     const int32_t* pool = nullptr;
     int pool_blocks = 0;
     const int32_t* pool_nv = nullptr;
+    // several query rows per sequence (Qs >= 2, bf16 keys, K = 128 or 256):
+    // with a queue for undecided scores (counter zeroed beforehand, room for
+    // one (row, entry) per score) the rows share each key load
+    uint32_t* fix_cnt = nullptr;
+    uint2* fix_list = nullptr;
     // filled by launch_score_exact: with several query rows per sequence the
     // blocks of one entry block and all its rows run together on one XCD
     int64_t n_eblk = 0, blocks = 0, per_xcd = 0;

@@ -43,6 +43,8 @@
 //     whole wave at once: each lane accumulates K/64 exact products into its
 //     own 640-bit integer accumulator, the accumulators are summed across the
 //     wave, and the total is rounded once.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -566,6 +568,227 @@ __global__ __launch_bounds__(kScoreThreads, DT == 2 && CPL == 1 ? 4 : 1) void sc
     }
 }
 
+// Several query rows of one sequence against bf16 keys (a draft block being
+// verified, or a prefill chunk on the exact path): each key is loaded and
+// widened to fp64 once and multiplied into QR row accumulators, instead of
+// being streamed once per row.
+//
+//   * 16 lanes per entry, 4 entries per wave round; lane `sub` loads the
+//     16-byte chunks at byte offset sub*16 + c*256 of the entry, so every
+//     chunk round of a wave reads four 256-byte segments;
+//   * rows are taken in groups of QR; workgroup tiles (sequence, row group,
+//     256-entry block) are laid out XCD-contiguous like score_exact_kernel;
+//   * exactness as for one row: Sum|p| is bounded by Sum|q| * max|k| (the
+//     entry's largest exponent field), every product is a multiple of
+//     2^(lsb(min|q|) + lsb(min|k|)); the rare undecided score is queued
+//     (row, entry) for score_fixup_kernel, which recomputes it exactly with a
+//     whole wave and adds it to the histogram, so the integer accumulator's
+//     registers stay out of this kernel;
+//   * the digit-1 histograms of the QR rows share the workgroup's LDS as
+//     packed 16-bit counters (a workgroup adds at most 256 per bin).
+constexpr int kRowsLanes = 16;                     // lanes per entry
+constexpr int kRowsRounds = 16;                    // rounds of 4 entries per wave
+constexpr int kRowsEntriesPerBlock = 4 * 4 * kRowsRounds;  // 256 per workgroup
+constexpr int kRowsPD = 3;                         // rounds of loads in flight
+
+template <int CPL, int QR>
+__global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(ScoreArgs a) {
+    constexpr int CH = CPL / 2;   // 16-byte chunks per lane
+    constexpr int EL = CH * 8;    // bf16 elements per lane
+    constexpr int EB = 128 * CPL; // bytes per entry
+    const int64_t w = blockIdx.x;
+    const int64_t t = (w & 7) * a.per_xcd + (w >> 3);
+    if (t >= a.blocks) return;
+    const int64_t ngroups = (a.Qs + QR - 1) / QR;
+    const int64_t eblk = t % a.n_eblk, bg = t / a.n_eblk;
+    const int64_t b = bg / ngroups, i0 = (bg % ngroups) * QR;
+    const int nrows = (int)(a.Qs - i0 < QR ? a.Qs - i0 : QR);
+    const int64_t r0 = b * a.Qs + i0;
+    // the group's last row sees the most entries
+    const int64_t nv_last = row_valid(a, r0 + nrows - 1);
+    const int64_t e_block = eblk * kRowsEntriesPerBlock;
+    if (e_block >= nv_last) return;
+
+    __shared__ uint32_t lhist[QR][kHistBins / 2];
+    const bool with_hist = a.hist != nullptr;
+    if (with_hist) {
+        for (int i = threadIdx.x; i < QR * kHistBins / 2; i += kScoreThreads) (&lhist[0][0])[i] = 0;
+    }
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, sub = lane & 15;
+
+    // this lane's slice of every row's index query (bf16 values, exact in fp32,
+    // widened to fp64 where they are used); per row Sum|q| and the least
+    // significant bit exponent of the smallest |q|
+    float qd[QR][EL];
+    double qsum[QR];
+    int lq[QR];
+    int64_t nv[QR];
+#pragma unroll
+    for (int j = 0; j < QR; ++j) {
+        const int jj = j < nrows ? j : nrows - 1;  // rows past the group repeat its last row
+        nv[j] = j < nrows ? row_valid(a, r0 + j) : 0;
+        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.iq) + (r0 + jj) * (int64_t)EB;
+        float qmin = INFINITY;
+        double qs = 0.0;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const u32x4 qw = *reinterpret_cast<const u32x4*>(qrow + c * 256 + sub * 16);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                qd[j][c * 8 + 2 * u] = bf16_lo(qw[u]);
+                qd[j][c * 8 + 2 * u + 1] = bf16_hi(qw[u]);
+                qs += fabs((double)qd[j][c * 8 + 2 * u]) + fabs((double)qd[j][c * 8 + 2 * u + 1]);
+                qmin = fminf(qmin, fminf(fabsf(bf16_lo(qw[u])), fabsf(bf16_hi(qw[u]))));
+            }
+        }
+        qs += swz_xor<1>(qs);
+        qs += swz_xor<2>(qs);
+        qs += swz_xor<4>(qs);
+        qs += swz_xor<8>(qs);
+        qmin = fminf(qmin, swz_xor<1>(qmin));
+        qmin = fminf(qmin, swz_xor<2>(qmin));
+        qmin = fminf(qmin, swz_xor<4>(qmin));
+        qmin = fminf(qmin, swz_xor<8>(qmin));
+        qsum[j] = qs;
+        lq[j] = bf16_lsb_exp(qmin);
+    }
+    const double bound_scale = (double)a.K * 0x1p-53 * 1.001 * (1.0 + (double)a.K * 0x1p-52);
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.ik) + b * a.N_cap * (int64_t)EB;
+    if (with_hist) __syncthreads();
+
+    const int64_t e_wave = e_block + wave * (4 * kRowsRounds);
+    if (e_wave < nv_last) {
+        // keys are loaded kRowsPD rounds ahead of their use (ring of kRowsPD + 1)
+        u32x4 ring[kRowsPD + 1][CH];
+        auto load = [&](int64_t e, u32x4(&dst)[CH]) __attribute__((always_inline)) {
+            e = e < nv_last ? e : nv_last - 1;  // in bounds; results past nv are not stored
+            const uint8_t* src = kbase + e * EB + sub * 16;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) dst[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 256));
+        };
+#pragma unroll
+        for (int p = 0; p < kRowsPD; ++p) load(e_wave + 4 * p + g, ring[p]);
+#pragma unroll
+        for (int rd = 0; rd < kRowsRounds; ++rd) {
+            const int64_t e = e_wave + 4 * rd + g;
+            if (e_wave + 4 * rd >= nv_last) break;  // wave-uniform
+            if (rd + kRowsPD < kRowsRounds) load(e + 4 * kRowsPD, ring[(rd + kRowsPD) % (kRowsPD + 1)]);
+            const u32x4(&wk)[CH] = ring[rd % (kRowsPD + 1)];
+            double acc[QR];
+#pragma unroll
+            for (int j = 0; j < QR; ++j) acc[j] = 0.0;
+            uint32_t kex = 0x7fff7fffu, kmx = 0u;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t kw = wk[c][u];
+                    const double lo = bf16_lo(kw), hi = bf16_hi(kw);
+#pragma unroll
+                    for (int j = 0; j < QR; ++j) {
+                        acc[j] = fma((double)qd[j][c * 8 + 2 * u], lo, acc[j]);
+                        acc[j] = fma((double)qd[j][c * 8 + 2 * u + 1], hi, acc[j]);
+                    }
+                    const uint32_t ef = kw & 0x7f807f80u;
+                    kex = pk_min_u16(kex, ef);
+                    kmx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, kmx),
+                                                                                 __builtin_bit_cast(u16x2, ef)));
+                }
+            }
+            // 16-lane butterfly with swizzles (xor 1, 2, 4, 8 stay inside the entry's lanes)
+            auto fold = [&](auto xr) __attribute__((always_inline)) {
+                constexpr int X = decltype(xr)::value;
+#pragma unroll
+                for (int j = 0; j < QR; ++j) acc[j] += swz_xor<X>(acc[j]);
+                kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (X << 10) | 0x1f));
+                kmx = __builtin_bit_cast(
+                    uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, kmx),
+                                                        __builtin_bit_cast(u16x2, (uint32_t)__builtin_amdgcn_ds_swizzle(
+                                                                                      (int)kmx, (X << 10) | 0x1f))));
+            };
+            fold(std::integral_constant<int, 1>{});
+            fold(std::integral_constant<int, 2>{});
+            fold(std::integral_constant<int, 4>{});
+            fold(std::integral_constant<int, 8>{});
+            // lane sub (< QR) finishes row sub of entry e: pick that row's values
+            // first, so the certificate below runs once per lane
+            double sj = 0.0, qs = 0.0;
+            int lqj = 0;
+            int64_t nvj = 0;
+#pragma unroll
+            for (int j = 0; j < QR; ++j) {
+                if (sub == j) {
+                    sj = acc[j];
+                    qs = qsum[j];
+                    lqj = lq[j];
+                    nvj = nv[j];
+                }
+            }
+            const bool mine = e < nvj;  // nv is 0 for lanes and rows past the group
+            const int64_t rr = r0 + sub;
+            float res = (float)sj;
+            bool ok = true;
+            if (mine) {
+                const uint32_t exmin = min(kex & 0xffffu, kex >> 16) >> 7;
+                const uint32_t exmax = max(kmx & 0xffffu, kmx >> 16) >> 7;
+                const double bound = ldexp(qs, (int)max(exmax, 1u) - 126);  // >= Sum|q||k|
+                const int lk = (int)(exmin > 0 ? exmin : 1u) - 134;
+                if (!sum_is_exact(bound, lqj + lk)) {
+                    const double eb = bound_scale * bound + fabs(sj) * 0x1p-52;
+                    const float lo = (float)(sj - eb), hi = (float)(sj + eb);
+                    ok = __float_as_uint(lo) == __float_as_uint(hi);
+                    res = lo;
+                }
+            }
+            if (mine && !ok) {
+                const uint32_t slot = atomicAdd(a.fix_cnt, 1u);
+                a.fix_list[slot] = make_uint2((uint32_t)rr, (uint32_t)e);
+            }
+            if (mine && ok) {
+                a.scores[rr * a.ld + e] = res;
+                if (with_hist) {
+                    const uint32_t bin = sort_key(res) >> (32 - kHistBits);
+                    atomicAdd(&lhist[rr - r0][bin >> 1], 1u << (16 * (bin & 1u)));
+                }
+            }
+        }
+    }
+    if (with_hist) {
+        __syncthreads();
+        for (int j = 0; j < nrows; ++j) {
+            uint32_t* ghist = a.hist + (r0 + j) * kHistBins;
+            for (int i = threadIdx.x; i < kHistBins / 2; i += kScoreThreads) {
+                const uint32_t c = lhist[j][i];
+                if (c & 0xffffu) atomicAdd(&ghist[2 * i], c & 0xffffu);
+                if (c >> 16) atomicAdd(&ghist[2 * i + 1], c >> 16);
+            }
+        }
+    }
+}
+
+// The scores score_rows_kernel could not decide: one wave per queued (row,
+// entry) at a time, exact integer accumulation, result and histogram count.
+// The queue holds at most one item per (row, entry), so the loop is bounded.
+__global__ __launch_bounds__(kScoreThreads) void score_fixup_kernel(ScoreArgs a) {
+    const uint32_t n = *a.fix_cnt;
+    const int lane = threadIdx.x & 63;
+    const uint32_t wid = blockIdx.x * (kScoreThreads / 64) + (threadIdx.x >> 6);
+    const uint32_t nw = gridDim.x * (kScoreThreads / 64);
+    for (uint32_t i = wid; i < n; i += nw) {
+        const uint2 it = a.fix_list[i];
+        const int64_t r = it.x, e = it.y, b = r / a.Qs;
+        const float x = wave_exact_bf16_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * a.K,
+                                            reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + e) * a.K,
+                                            a.K, lane);
+        if (lane == 0) {
+            a.scores[r * a.ld + e] = x;
+            if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(x) >> (32 - kHistBits))], 1u);
+        }
+    }
+}
+
 // Fallback for index widths the streaming kernel does not tile: one thread per
 // entry, same arithmetic and the same certification.
 __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
@@ -651,7 +874,27 @@ hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
     const int eb = a.dtype == 0 ? a.K * 2 : a.dtype == 1 ? a.K : a.K / 2;  // key bytes per entry
     const int cpl = eb / 128;
     const bool fast = eb % 128 == 0 && (cpl == 1 || cpl == 2 || cpl == 4 || cpl == 8);
-    if (fast) {
+    if (a.dtype == 0 && a.Qs >= 2 && !a.pool && a.fix_cnt && eb % 128 == 0 && (cpl == 2 || cpl == 4)) {
+        // several rows of a sequence share every key load
+        const int QR = a.Qs <= 5 ? a.Qs : 4;
+        a.n_eblk = (a.N + kRowsEntriesPerBlock - 1) / kRowsEntriesPerBlock;
+        a.blocks = a.n_eblk * a.B * ((a.Qs + QR - 1) / QR);
+        a.per_xcd = (a.blocks + 7) / 8;
+        const dim3 grid((unsigned)(8 * a.per_xcd));
+#define CSA2_ROWS_LAUNCH(CPLV, QRV)                                                                      \
+    if (cpl == CPLV && QR == QRV)                                                                        \
+        hipLaunchKernelGGL((score_rows_kernel<CPLV, QRV>), grid, dim3(kScoreThreads), 0, stream, a);
+        CSA2_ROWS_LAUNCH(2, 2)
+        CSA2_ROWS_LAUNCH(2, 3)
+        CSA2_ROWS_LAUNCH(2, 4)
+        CSA2_ROWS_LAUNCH(2, 5)
+        CSA2_ROWS_LAUNCH(4, 2)
+        CSA2_ROWS_LAUNCH(4, 3)
+        CSA2_ROWS_LAUNCH(4, 4)
+        CSA2_ROWS_LAUNCH(4, 5)
+#undef CSA2_ROWS_LAUNCH
+        hipLaunchKernelGGL(score_fixup_kernel, dim3(256), dim3(kScoreThreads), 0, stream, a);
+    } else if (fast) {
         a.n_eblk = (a.N + kScoreEntriesPerBlock - 1) / kScoreEntriesPerBlock;
         a.blocks = a.n_eblk * R;
         a.per_xcd = (a.blocks + 7) / 8;

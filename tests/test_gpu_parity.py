@@ -423,6 +423,41 @@ def test_verify5_w6_ragged_n_valid():
     Run(W6.scaled(B=4, N=3000, k=256), n_valid=[3000, 2048, 300, 5]).check_all()
 
 
+def _tie_keys(g, k):
+    # the index keys of the bf16 tie cases: sums on (or a hair beside) fp32
+    # midpoints, extreme exponent spreads, cancellation
+    b = lambda v: int(synth.to_bf16_bits(np.array([v], np.float32))[0])  # noqa: E731
+    pats = [{0: 1.0, 1: 2.0 ** -24}, {0: 1.0, 1: 3 * 2.0 ** -24}, {0: 1.0, 1: 2.0 ** -24, 2: 2.0 ** -80},
+            {0: 2.0 ** 100, 1: 1.0, 2: -(2.0 ** 100)}, {0: 2.0 ** 60, 1: -(2.0 ** 60), 2: 3.0},
+            {0: 2.0 ** -126, 1: 2.0 ** -130}, {0: -(2.0 ** -120), 1: 2.0 ** -120}]
+    out = np.zeros_like(k)
+    B, N = k.shape[:2]
+    flat = out.reshape(B, N, -1)
+    for j in range(N):
+        for e, v in pats[j % len(pats)].items():
+            flat[:, j, e] = b(v)
+        flat[:, j, 10 + j % 50] = b(2.0 ** -(j % 90)) if j % 3 == 0 else 0
+    return out
+
+
+def _tie_queries(iq):
+    out = np.zeros_like(iq)
+    flat = out.reshape(iq.shape[0], iq.shape[1], -1)
+    flat[:, :, :3] = 0x3F80
+    flat[:, :, 10:60] = 0x3F80
+    flat[:, 1::2, 64:] = synth.to_bf16_bits(np.array([0.5], np.float32))[0]  # rows differ past 64
+    return out
+
+
+def test_draft_rows_share_key_loads_ties_and_groups():
+    # several query rows per sequence go through the shared-load scorer; undecided
+    # scores are queued and recomputed exactly (heavy ties make the selection
+    # depend on every bit)
+    Run(W6.scaled(B=2, N=999, k=100, H_I=2, d_I=64), ikeys=_tie_keys, iq=_tie_queries).check_all()
+    Run(W6.scaled(B=2, N=1500, k=200, Qs=3), n_valid=[1500, 1001]).check_all()
+    Run(W6.scaled(B=2, N=1500, k=200, Qs=7, H_I=2, d_I=64), n_valid=[1500, 777]).check_all()
+
+
 def test_prefill_w4_scaled():
     Run(W4.scaled(N=6000, Qs=96, k=512)).check_all()
 
