@@ -50,12 +50,15 @@
 
 namespace csa2 {
 
-constexpr int kScoreThreads = 256;
+constexpr int kScoreThreads = 256;  // workgroup of the multi-row scorer and the fixup
 constexpr int kScoreRounds = 8;                                   // rounds of 8 entries per wave
 constexpr int kScoreEntriesPerWave = 8 * kScoreRounds;            // 64
-constexpr int kScoreEntriesPerChunk = 4 * kScoreEntriesPerWave;   // 256 per pass of the workgroup
+// The single-row stream runs 8 waves per workgroup: 512 entries share one LDS
+// histogram, which halves the workgroups that flush one to global memory.
+constexpr int kStreamThreads = 512;
+constexpr int kScoreEntriesPerChunk = (kStreamThreads / 64) * kScoreEntriesPerWave;  // 512 per pass of the workgroup
 constexpr int kScoreChunks = 1;                                   // passes per workgroup
-constexpr int kScoreEntriesPerBlock = kScoreChunks * kScoreEntriesPerChunk;  // 256
+constexpr int kScoreEntriesPerBlock = kScoreChunks * kScoreEntriesPerChunk;  // 512
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -288,7 +291,7 @@ CSA2_DEV int bf16_pair_emin(uint32_t w) {
 // rare exact-recompute path spills.
 // POOL: the slots are a hierarchical pool's positions (a.pool set).
 template <int DT, int CPL, bool POOL>
-__global__ __launch_bounds__(kScoreThreads, DT == 2 && CPL == 1 ? 4 : 1) void score_exact_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void score_exact_kernel(ScoreArgs a) {
     constexpr int EPC = DT == 0 ? 8 : DT == 1 ? 16 : 32;  // key elements per 16-byte chunk
     constexpr int EB = 128 * CPL;         // bytes per entry
     int64_t r, e_block;
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(kScoreThreads, DT == 2 && CPL == 1 ? 4 : 1) void sc
     __shared__ uint32_t lhist[kHistBins];
     const bool with_hist = a.hist != nullptr;
     if (with_hist) {
-        for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) lhist[i] = 0;
+        for (int i = threadIdx.x; i < kHistBins; i += kStreamThreads) lhist[i] = 0;
     }
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(kScoreThreads, DT == 2 && CPL == 1 ? 4 : 1) void sc
     if (with_hist) {
         __syncthreads();
         uint32_t* ghist = a.hist + r * kHistBins;
-        for (int i = threadIdx.x; i < kHistBins; i += kScoreThreads) {
+        for (int i = threadIdx.x; i < kHistBins; i += kStreamThreads) {
             const uint32_t c = lhist[i];
             if (c) atomicAdd(&ghist[i], c);
         }
@@ -903,9 +906,9 @@ hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
 #define CSA2_SCORE_LAUNCH(DTV, CPLV)                                                                   \
     if (a.dtype == DTV && cpl == CPLV) {                                                             \
         if (pool)                                                                                    \
-            hipLaunchKernelGGL((score_exact_kernel<DTV, CPLV, true>), grid, dim3(kScoreThreads), 0, stream, a); \
+            hipLaunchKernelGGL((score_exact_kernel<DTV, CPLV, true>), grid, dim3(kStreamThreads), 0, stream, a); \
         else                                                                                         \
-            hipLaunchKernelGGL((score_exact_kernel<DTV, CPLV, false>), grid, dim3(kScoreThreads), 0, stream, a); \
+            hipLaunchKernelGGL((score_exact_kernel<DTV, CPLV, false>), grid, dim3(kStreamThreads), 0, stream, a); \
     }
         CSA2_SCORE_LAUNCH(0, 1)
         CSA2_SCORE_LAUNCH(0, 2)
