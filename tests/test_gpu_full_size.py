@@ -1,0 +1,91 @@
+"""Parity at the workloads' full sizes, in the launch configuration the bench times.
+
+The decode workloads (batch 32 x 65,536 entries, the draft-block, FP4-key and
+hierarchical variants, and batch 8 x 262,144 entries) are compared against the
+oracle in full: every selection bit-exact, every attention output within the
+stated tolerance.  The prefill chunk (4,096 queries against 131,072 causal
+entries) is too large for the oracle as a whole; its GPU selection is checked
+for validity on every row and against the oracle exactly on sampled rows,
+attention included.
+"""
+import numpy as np
+import pytest
+import torch
+
+import compressed_kv_cache_03_amd as csa2
+import oracle
+from cases import make_inputs, rel_err
+from synth.workloads import W2, W3, W4, W6, W7, W8
+from test_gpu_parity import TOL, Run, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def test_w2_full_size():
+    Run(W2).check_all()
+
+
+def test_w3_full_size_fp8():
+    Run(W3).check_all()
+
+
+def test_w6_full_size_draft_block():
+    Run(W6).check_all()
+
+
+def test_w7_full_size_fp4_index_keys():
+    Run(W7).check_all()
+
+
+def test_w8_full_size_hierarchical():
+    Run(W8).check_all()
+
+
+def test_w4_full_size_prefill_sampled_rows():
+    wl = W4
+    B, N, D, Qs, W, k = wl.B, wl.N, wl.D, wl.Qs, wl.W, wl.k
+    assert B == 1
+    inp = make_inputs(wl)
+    L = inp.layers[0]
+    x = inp.cache_x[0]
+
+    # GPU: the whole chunk, as the bench runs it
+    gc, gs = csa2.fp4_pack(dev(x))
+    grp = csa2.Group(gc, gs, dev(inp.ikeys[0]), dev(inp.n_valid), wl.idx_dtype, k, sel_rows=B * Qs)
+    out, _ = grp.layer_step("F", q=dev(L["q"]), iq=dev(L["iq"]), wk=dev(L["wk"]), wv=dev(L["wv"]), W=W,
+                            sm_scale=wl.sm_scale, new_entry=dev(L["new_entry"]), new_ikey=dev(L["new_ikey"]))
+    torch.cuda.synchronize()
+    sel = host(grp.sel)[:Qs]
+    out = host(out).reshape(Qs, wl.Hq, D)
+
+    # every row: ascending distinct valid indices, min(k, visible) of them, then -1
+    visible = N - Qs + 1 + np.arange(Qs)
+    take = np.minimum(k, visible)
+    pos = np.arange(k)[None, :]
+    assert np.all((sel >= 0) == (pos < take[:, None]))
+    d = np.diff(sel.astype(np.int64), axis=1)
+    assert np.all(d[pos[:, 1:] < take[:, None]] > 0)
+    assert np.all(sel < visible[:, None])
+
+    # oracle on sampled rows: the cache after the chunk's own write (rows N-Qs..N-1
+    # packed from the new entries; their index keys stored), then the row's exact
+    # causal scores, top-k and joint attention with its own window rows
+    codes, scales = oracle.fp4_pack(x.reshape(N, D))
+    ncodes, nscales = oracle.fp4_pack(L["new_entry"].reshape(Qs, D))
+    codes = codes.reshape(N, D // 2).copy()
+    scales = scales.reshape(N, D // 32).copy()
+    codes[N - Qs:] = ncodes.reshape(Qs, D // 2)
+    scales[N - Qs:] = nscales.reshape(Qs, D // 32)
+    ikeys = inp.ikeys[0].copy()
+    ikeys[0, N - Qs:] = L["new_ikey"][0]
+    rng = np.random.default_rng(4096)
+    rows = sorted({0, 1, 255, 256, 1023, 2048, Qs - 2, Qs - 1, *rng.integers(0, Qs, 8).tolist()})
+    for i in rows:
+        nv = np.array([visible[i]], np.int64)
+        sc = oracle.index_score(wl.idx_dtype, L["iq"][:, i:i + 1], ikeys, n_valid_row=nv)
+        ref_sel = oracle.topk(sc.reshape(1, N), k, n_valid=nv)
+        assert np.array_equal(sel[i], ref_sel[0]), i
+        ro, _ = oracle.attend(L["q"][:, i:i + 1], codes.reshape(1, N, D // 2), scales.reshape(1, N, D // 32),
+                              ref_sel, L["wk"][:, i:i + W], L["wv"][:, i:i + W], W, np.float32(wl.sm_scale))
+        err = rel_err(out[i], ro.reshape(wl.Hq, D))
+        assert err <= TOL, (i, err)
