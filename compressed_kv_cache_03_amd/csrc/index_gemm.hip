@@ -177,12 +177,13 @@ __global__ __launch_bounds__(kSThreads) void sample_gemm_kernel(GemmArgs a) {
 // group, four consecutive entries of one query row (a quad).  A quad whose
 // largest score reaches theta is appended to the wave's LDS list, compacted
 // with a ballot; the score bits carry tags in their low 8 bits (lane and group
-// in the first, the 16-entry group of the block in the second).  When the list
-// fills up the wave alone drains it: per quad it tests the four truncated keys,
+// in the first, the 16-entry group of the block in the second).  The wave
+// alone drains its list at the start of every key tile, and before any 16-entry
+// group whose quads might not fit: per quad it tests the four truncated keys,
 // takes positions from a per-row LDS counter and writes the survivors.  No
 // workgroup barrier, no global atomic unless a region overflows.
 template <int KB>
-__global__ __launch_bounds__(kFThreads) void filter_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kFThreads, 2) void filter_gemm_kernel(GemmArgs a) {
     constexpr int RB = KB * 128;
     constexpr int PITCH = RB + 16;
     __shared__ __attribute__((aligned(16))) uint8_t btile[kGCols * PITCH];
@@ -243,10 +244,11 @@ __global__ __launch_bounds__(kFThreads) void filter_gemm_kernel(GemmArgs a) {
     // the block's regions, one per row, consecutive from wg_blk
     uint2* const wg_blk = a.blk + (cb * a.B * a.Qs + (int64_t)b * a.Qs + row0) * kFBlkCap;
     constexpr uint32_t row_pitch = kFBlkCap;  // the block's rows are consecutive regions
-    // Drain: each lane takes four quads at a time, so that the LDS round trips
-    // (quad, row data, row counter) of the four overlap.
-    auto drain = [&](uint32_t cq) __attribute__((always_inline)) {
-        constexpr int U = 4;
+    // Drain: each lane takes U quads at a time, so that the LDS round trips
+    // (quad, row data, row counter) of the U overlap (U = 4 at tile starts; 1
+    // inside a tile, where few registers are free and drains are rare).
+    auto drain = [&](uint32_t cq, auto u_c) __attribute__((always_inline)) {
+        constexpr int U = decltype(u_c)::value;
         __builtin_amdgcn_wave_barrier();
         for (uint32_t j0 = 0; j0 < cq; j0 += 64 * U) {
             u32x4 v[U];
@@ -303,20 +305,6 @@ __global__ __launch_bounds__(kFThreads) void filter_gemm_kernel(GemmArgs a) {
         __builtin_amdgcn_wave_barrier();
     };
 
-    // A quad that finds the list full: its passing scores go straight to the
-    // row's overflow list (global atomics; only when candidates are dense).
-    auto spill = [&](const f32x4& v, int qg, uint32_t c0) __attribute__((always_inline)) {
-        const int64_t r = (int64_t)b * a.Qs + row0 + wave * 64 + qg * 16 + n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t key = __float_as_uint(v[i]) & 0xffffff00u;
-            if (c0 + (uint32_t)i < lim[qg] && __uint_as_float(key) >= th[qg]) {
-                const uint32_t o = atomicAdd(&a.cand_cnt[r], 1u);
-                if (o < (uint32_t)a.cap) a.cand[r * a.cap + o] = make_uint2(key, c0 + (uint32_t)i);
-            }
-        }
-    };
-
     // the key tile is kGCols consecutive entries, one contiguous run of bytes:
     // load c (16-byte chunk q * kFThreads + tid) lands at entry c / CPE, piece c % CPE
     constexpr int CPE = RB / 16;                   // chunks per entry
@@ -346,7 +334,7 @@ __global__ __launch_bounds__(kFThreads) void filter_gemm_kernel(GemmArgs a) {
         // drain here, before the next tile's loads are issued: the wait for those
         // loads (vmcnt counts stores too) then never waits for fresh stores
         if (wcnt) {
-            drain(wcnt);
+            drain(wcnt, std::integral_constant<int, 4>{});
             wcnt = 0;
         }
         if (sub + 1 < ntiles) load_tile(tc0 + kGCols);
@@ -372,6 +360,11 @@ __global__ __launch_bounds__(kFThreads) void filter_gemm_kernel(GemmArgs a) {
         // comparison of the float bits (no NaN handling, -0 below any theta).
         auto run_tile = [&](auto mask_c, auto ipre_c) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_c)::value, IPRE = decltype(ipre_c)::value;
+            // The four query groups' tests are independent; their list positions
+            // are wave-uniform prefix sums of the ballots plus the lane's rank, so
+            // the four compactions do not wait on each other.  The list has room
+            // for every quad of the group (checked before each group), so no
+            // write needs a capacity test.
             auto epilogue = [&](f32x4 (&acc)[kFQG], int eg) {
                 const uint32_t grp = __builtin_amdgcn_readfirstlane((uint32_t)(sub * (kGCols / 16) + eg));
                 const uint32_t c0 = (uint32_t)tc0 + eg * 16 + 4 * g;
@@ -394,20 +387,27 @@ __global__ __launch_bounds__(kFThreads) void filter_gemm_kernel(GemmArgs a) {
                     }
                     bal[qg] = __ballot(p[qg]);
                 }
+                uint32_t base[kFQG];
+#pragma unroll
+                for (int qg = 0; qg < kFQG; ++qg) {
+                    base[qg] = wcnt;
+                    wcnt += (uint32_t)__popcll(bal[qg]);
+                }
 #pragma unroll
                 for (int qg = 0; qg < kFQG; ++qg) {
                     const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[qg] >> 32),
                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal[qg], 0u));
-                    const uint32_t pos = wcnt + below;
-                    if (p[qg]) {
-                        if (pos < (uint32_t)kFList)
-                            wl[pos] = u32x4{(__float_as_uint(acc[qg][0]) & vmask) | ltag[qg],
-                                            (__float_as_uint(acc[qg][1]) & vmask) | grp, __float_as_uint(acc[qg][2]),
-                                            __float_as_uint(acc[qg][3])};
-                        else
-                            spill(acc[qg], qg, c0);  // the list is full (dense candidates)
-                    }
-                    wcnt = min(wcnt + (uint32_t)__popcll(bal[qg]), (uint32_t)kFList);
+                    if (p[qg])
+                        wl[base[qg] + below] = u32x4{(__float_as_uint(acc[qg][0]) & vmask) | ltag[qg],
+                                                     (__float_as_uint(acc[qg][1]) & vmask) | grp,
+                                                     __float_as_uint(acc[qg][2]), __float_as_uint(acc[qg][3])};
+                }
+            };
+            // a group adds at most kFQG * 64 quads: drain first if they might not fit
+            auto make_room = [&]() __attribute__((always_inline)) {
+                if (wcnt > (uint32_t)(kFList - kFQG * 64)) {
+                    drain(wcnt, std::integral_constant<int, 1>{});
+                    wcnt = 0;
                 }
             };
             // the key fragments of group e + 1 are read while group e computes
@@ -420,16 +420,18 @@ __global__ __launch_bounds__(kFThreads) void filter_gemm_kernel(GemmArgs a) {
             for (int eg = 0; eg < kGCols / 16; eg += 2) {
                 read_kf(kfB, eg + 1);
                 mma(kfA, acc);
+                make_room();
                 epilogue(acc, eg);
                 if (eg + 2 < kGCols / 16) read_kf(kfA, eg + 2);
                 mma(kfB, acc);
+                make_room();
                 epilogue(acc, eg + 1);
             }
         };
         if (all_visible && ipre) run_tile(std::false_type{}, std::true_type{});
         else run_tile(std::true_type{}, std::false_type{});
     }
-    if (wcnt) drain(wcnt);
+    if (wcnt) drain(wcnt, std::integral_constant<int, 4>{});
     {
         const int lr = wave * 64 + lane;  // the wave's own rows
         const int64_t qrow = row0 + lr;
