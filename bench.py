@@ -35,6 +35,9 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_exact_w2_hbm_traffic.md"
 SCORE_SOURCE = os.path.join(ROOT, "compressed_kv_cache_03_amd", "csrc", "score.hip")
 
 
+TRAFFIC_WORKLOAD = "decode_b32_n65536_group_F_Ri_Ru_Ru"  # the workload the summary's counters cover
+
+
 def measured_traffic():
     """Bytes per launch of the dominant kernel from the committed counter summary, or None
     when the summary is missing or was taken on another version of the kernel source."""
@@ -182,6 +185,28 @@ def host_tier(grp, reps=3):
             "restore_GBps": round(n / (ms_restore * 1e-3) / 1e9, 1),
             "note": "pinned host image of the w2 sharing group (FP4 codes, scales, bf16 index keys, "
                     "selection); device <-> host copies, restored bits checked by the GPU tests"}
+
+
+def cache_accounting(wl):
+    """Stored cache bytes of the workload's layers with entries and index keys shared inside each
+    group, against every layer keeping its own (entries x numbers x copies x bits / 8 per array,
+    computed by the library's accounting entry point)."""
+    import compressed_kv_cache_03_amd as csa2
+
+    entries = wl.B * wl.N
+    K = wl.H_I * wl.d_I
+    arrays = {"fp4_codes": (wl.D, 4), "fp4_scales": (wl.D // 32, 32)}
+    if wl.idx_dtype == "fp4":
+        arrays.update({"index_keys": (K, 4), "index_key_scales": (K // 32, 32)})
+    else:
+        arrays["index_keys"] = (K, 16 if wl.idx_dtype == "bf16" else 8)
+    layers = len(wl.pattern) * wl.groups
+    shared = {n: csa2.cache_bytes(entries, num, wl.groups, bits) for n, (num, bits) in arrays.items()}
+    unshared = {n: csa2.cache_bytes(entries, num, layers, bits) for n, (num, bits) in arrays.items()}
+    return {"layers": layers, "stored_copies": wl.groups, "shared_bytes": shared,
+            "unshared_bytes": unshared, "shared_total": sum(shared.values()),
+            "unshared_total": sum(unshared.values()),
+            "ratio": round(sum(unshared.values()) / sum(shared.values()), 3)}
 
 
 def traffic_probe(wl, device):
@@ -342,9 +367,11 @@ def main():
                      "frac": round(total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "roofline": {"kernel": "score_exact_kernel (exact index-score stream)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic() if wl.name == TRAFFIC_WORKLOAD else None,
                      "bytes_per_launch": scan_bytes, "avg_launch_us": round(ms_scan * 1e3, 2)},
     }
+    res["cache"] = cache_accounting(wl)
     res["host_tier"] = host_tier(groups[0])
     del groups
     if not args.no_verify:

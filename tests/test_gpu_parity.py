@@ -192,6 +192,19 @@ def test_topk_parity_unaligned_rows(k):
     assert np.array_equal(host(got), oracle.topk(s, k, n_valid=nv.astype(np.int64)))
 
 
+@pytest.mark.parametrize("R,N", [(4, 200003), (8, 262144), (4, (1 << 19) - 3)])
+def test_topk_parity_long_rows_sliced(R, N):
+    # a few rows longer than 2^17 entries take the sliced path (compaction spread
+    # over the chip, then one final workgroup per row); ties, signed zeros, -inf
+    # and short valid counts as in the row-kernel tests
+    for k in (1, 2048, 9000):
+        s = _topk_scores(R, N, 31 + k)
+        nv = np.array([N, N - 7, 131073, 9, N, 150000, 1, N][:R], np.int32)
+        got = csa2.topk(dev(s), k, n_valid=dev(nv))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(got), oracle.topk(s, k, n_valid=nv.astype(np.int64))), (R, N, k)
+
+
 def test_topk_parity_long_row_multi_pass_slices():
     # beyond 2^24 entries a slice spans several 4096-entry compaction passes
     N = (1 << 24) + 5000
