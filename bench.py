@@ -67,7 +67,10 @@ def _dev(a, device):
 
 
 def algorithmic_bytes(wl):
-    """Bytes the method must move per step (measurement section)."""
+    """Bytes the method must move per step: every layer reads its selection, the selected FP4
+    records, its window rows and query and writes its output; a selecting layer also streams every
+    index key, reads its index query, writes a score per entry and its selection; a Full layer
+    also packs and stores its new entry and index key.  Returns (total, bytes of one score launch)."""
     B, N, D, K, k, W, Hq, Qs = wl.B, wl.N, wl.D, wl.H_I * wl.d_I, wl.k, wl.W, wl.Hq, wl.Qs
     if wl.idx_dtype == "fp4":
         key_b, q_b, new_key_b = K // 2 + K // 32 * 4, K * 2, K * 4 + K // 2 + K // 32 * 4
@@ -327,7 +330,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this implementation runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path would shard by sequence with no exchange, see DESIGN.md)", file=sys.stderr)
+              "(sequences are independent, so the path would shard by sequence with no exchange)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
