@@ -186,8 +186,8 @@ def host_tier(grp, reps=3):
     ms_save, ms_restore = e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
     return {"image_bytes": n, "save_GBps": round(n / (ms_save * 1e-3) / 1e9, 1),
             "restore_GBps": round(n / (ms_restore * 1e-3) / 1e9, 1),
-            "note": "pinned host image of the w2 sharing group (FP4 codes, scales, bf16 index keys, "
-                    "selection); device <-> host copies, restored bits checked by the GPU tests"}
+            "note": "pinned host image of the workload's first sharing group (FP4 codes, scales, index "
+                    "keys, selection); device <-> host copies, restored bits checked by the GPU tests"}
 
 
 def cache_accounting(wl):
