@@ -297,9 +297,8 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
     int64_t r, e_block;
     {
         // block w takes t = (w % 8) * per_xcd + w / 8: each XCD gets a run of
-        // consecutive t, so the Qs rows of a sequence for one entry block share
-        // its L2, and with Qs = 1 a row's scores land in one XCD's L2, where its
-        // top-k workgroup reads them
+        // consecutive t, so the Qs rows of a sequence for one entry block read
+        // its keys through the same L2
         const int64_t w = blockIdx.x;
         const int64_t t = (w & 7) * a.per_xcd + (w >> 3);
         if (t >= a.blocks) return;
