@@ -89,3 +89,25 @@ def test_w4_full_size_prefill_sampled_rows():
                               ref_sel, L["wk"][:, i:i + W], L["wv"][:, i:i + W], W, np.float32(wl.sm_scale))
         err = rel_err(out[i], ro.reshape(wl.Hq, D))
         assert err <= TOL, (i, err)
+
+
+def test_w4_full_size_prefill_run_to_run_bitwise():
+    # candidate regions are filled through atomics, so their order varies between
+    # runs; the selection (sorted) and the attention over it must not
+    wl = W4
+    inp = make_inputs(wl)
+    L = inp.layers[0]
+    gc, gs = csa2.fp4_pack(dev(inp.cache_x[0]))
+    keys = dev(inp.ikeys[0])
+    kw = dict(q=dev(L["q"]), iq=dev(L["iq"]), wk=dev(L["wk"]), wv=dev(L["wv"]), W=wl.W, sm_scale=wl.sm_scale,
+              new_entry=dev(L["new_entry"]), new_ikey=dev(L["new_ikey"]))
+    runs = []
+    for _ in range(2):
+        grp = csa2.Group(gc.clone(), gs.clone(), keys.clone(), dev(inp.n_valid), wl.idx_dtype, wl.k,
+                         sel_rows=wl.B * wl.Qs)
+        out, lse = grp.layer_step("F", **kw)
+        torch.cuda.synchronize()
+        runs.append((host(grp.sel), host(out), host(lse)))
+    assert np.array_equal(runs[0][0], runs[1][0])
+    assert np.array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
+    assert np.array_equal(runs[0][2].view(np.uint32), runs[1][2].view(np.uint32))
