@@ -15,7 +15,7 @@ import torch
 import compressed_kv_cache_03_amd as csa2
 import oracle
 from cases import make_inputs, rel_err
-from synth.workloads import W2, W3, W4, W6, W7, W8
+from synth.workloads import W2, W3, W4, W5, W6, W7, W8
 from test_gpu_parity import TOL, Run, dev, host
 
 pytestmark = pytest.mark.gpu
@@ -39,6 +39,43 @@ def test_w7_full_size_fp4_index_keys():
 
 def test_w8_full_size_hierarchical():
     Run(W8).check_all()
+
+
+def test_w5_full_size_stack_two_sequences_against_the_oracle():
+    # the 16-layer stack (4 groups of Full/Reindex/Reuse/Reuse, batch 64 x 131,072 entries) runs
+    # whole on the GPU; sequences are independent, so the oracle follows the first and the last
+    wl = W5
+    B, N, D = wl.B, wl.N, wl.D
+    seqs = np.array([0, B - 1])
+    inp = make_inputs(wl)
+    g_gpu, g_orc = [], []
+    for g in range(wl.groups):
+        x = dev(inp.cache_x[g])
+        gc, gs = csa2.fp4_pack(x)
+        del x
+        g_gpu.append(csa2.Group(gc, gs, dev(inp.ikeys[g]), dev(inp.n_valid), wl.idx_dtype, wl.k, sel_rows=B))
+        oc, os_ = oracle.fp4_pack(np.ascontiguousarray(inp.cache_x[g][seqs]).reshape(-1, D))
+        g_orc.append(oracle.Group(oc.reshape(2, N, D // 2), os_.reshape(2, N, D // 32),
+                                  np.ascontiguousarray(inp.ikeys[g][seqs]), inp.n_valid[seqs].astype(np.int64),
+                                  wl.idx_dtype, wl.k, max_rows=2))
+        inp.cache_x[g] = inp.ikeys[g] = None  # the host copies are no longer needed
+    torch.cuda.synchronize()
+    for li, L in enumerate(inp.layers):
+        g, mode = L["group"], L["mode"]
+        kw = dict(q=L["q"], wk=L["wk"], wv=L["wv"], W=wl.W, sm_scale=np.float32(wl.sm_scale))
+        if L["iq"] is not None:
+            kw["iq"] = L["iq"]
+        if L["new_entry"] is not None:
+            kw["new_entry"] = L["new_entry"]
+            kw["new_ikey"] = L["new_ikey"]
+        go, _ = g_gpu[g].layer_step(mode, **{k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in kw.items()})
+        rc, ro, _ = g_orc[g].layer_step(mode, **{k: (np.ascontiguousarray(v[seqs]) if isinstance(v, np.ndarray) else v)
+                                                 for k, v in kw.items()})
+        assert rc == 0
+        torch.cuda.synchronize()
+        assert np.array_equal(host(g_gpu[g].sel)[seqs], g_orc[g].sel[:2]), (li, mode)
+        err = rel_err(host(go)[seqs], ro)
+        assert err <= TOL, (li, mode, err)
 
 
 def test_w4_full_size_prefill_sampled_rows():
