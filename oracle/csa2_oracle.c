@@ -37,6 +37,14 @@
  *   - attention: one joint softmax over the selected entries and the window
  *     rows; an entry is one 128-vector used as both key and value and shared
  *     by all query heads; window keys and values are separate bf16 rows.
+ *
+ * Pins: every function below is checked, in the CPU tests, against something
+ * other than itself (the format's exhaustive code table, exact rational
+ * arithmetic, brute-force sorts, textbook dense attention at k = N, the
+ * pages' worked cache figure, mode invariants); none is parity unpinned.
+ * What no test can pin is the real model behind the pages (its score
+ * function, dimensions and scale rule, its bytes per token, the quality of
+ * its selections): these are readings, stated above, not reproductions.
  */
 #include <math.h>
 #include <stdint.h>
