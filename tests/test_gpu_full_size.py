@@ -148,3 +148,29 @@ def test_w4_full_size_prefill_run_to_run_bitwise():
     assert np.array_equal(runs[0][0], runs[1][0])
     assert np.array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
     assert np.array_equal(runs[0][2].view(np.uint32), runs[1][2].view(np.uint32))
+
+
+def test_w2_full_size_host_tier_round_trip_bitwise():
+    # the bench's host-tier leg at its size: the group after a Full layer goes to a
+    # pinned host image (about 1.24 GB), its device buffers are overwritten, the
+    # image comes back, and every stored byte and the selection are as before
+    wl = W2
+    inp = make_inputs(wl)
+    L = inp.layers[0]
+    gc, gs = csa2.fp4_pack(dev(inp.cache_x[0]))
+    g = csa2.Group(gc, gs, dev(inp.ikeys[0]), dev(inp.n_valid), wl.idx_dtype, wl.k, sel_rows=wl.B)
+    g.layer_step("F", q=dev(L["q"]), iq=dev(L["iq"]), wk=dev(L["wk"]), wv=dev(L["wv"]), W=wl.W,
+                 sm_scale=wl.sm_scale, new_entry=dev(L["new_entry"]), new_ikey=dev(L["new_ikey"]))
+    torch.cuda.synchronize()
+    before = [t.clone() for t in (g.codes, g.scales, g.ikeys, g.sel)]
+    image = g.save()
+    torch.cuda.synchronize()
+    assert image.numel() == g.image_bytes()
+    g.codes.fill_(0x5A)
+    g.scales.fill_(float("nan"))
+    g.ikeys.fill_(0x7FC1)
+    g.sel.fill_(-7)
+    g.restore(image)
+    torch.cuda.synchronize()
+    for a, b in zip(before, (g.codes, g.scales, g.ikeys, g.sel)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
