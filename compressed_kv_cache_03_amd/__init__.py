@@ -61,7 +61,7 @@ def _load():
     lib.csa2_version.argtypes = []
     lib.csa2_version.restype = ctypes.c_char_p
     lib.csa2_fp4_pack.argtypes = [vp, i64, i32, vp, vp, vp]
-    lib.csa2_index_score.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i64, i32, i32, vp, vp]
+    lib.csa2_index_score.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i64, i32, i32, i64, i32, vp, vp]
     lib.csa2_topk_workspace_bytes.argtypes = [i64, i64, i32]
     lib.csa2_topk_workspace_bytes.restype = sz
     lib.csa2_topk.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, sz, vp]
@@ -138,10 +138,12 @@ def fp4_pack(x: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.T
 
 
 def index_score(iq: torch.Tensor, ik: torch.Tensor, dtype: str, out: torch.Tensor | None = None,
-                stream=None, ik_scales: torch.Tensor | None = None) -> torch.Tensor:
+                stream=None, ik_scales: torch.Tensor | None = None, causal_offset: int = -1,
+                exact: bool = True) -> torch.Tensor:
     """iq [B, Qs, H, d] and ik [B, N, H, d] (uint8 for e4m3, int16/bf16/uint16 bits for bf16)
     -> exact fp32 scores [B, Qs, N].  dtype 'fp4': iq bf16 bits, ik the e2m1 codes
-    [B, N, H, d/2] and ik_scales fp32 [B, N, H*d/32]."""
+    [B, N, H, d/2] and ik_scales fp32 [B, N, H*d/32].  causal_offset c >= 0: row i scores
+    entries j <= c + i and gets -inf for the rest."""
     _dev(iq, "iq")
     _dev(ik, "ik")
     B, Qs, H, d = iq.shape
@@ -153,7 +155,8 @@ def index_score(iq: torch.Tensor, ik: torch.Tensor, dtype: str, out: torch.Tenso
     if out is None:
         out = torch.empty(B, Qs, N, dtype=torch.float32, device=iq.device)
     _check(_load().csa2_index_score(iq.data_ptr(), ik.data_ptr(), _ptr(ik_scales), IDX_DTYPE[dtype], B, Qs,
-                                    N, H, d, out.data_ptr(), _stream(stream)), "csa2_index_score")
+                                    N, H, d, int(causal_offset), int(bool(exact)), out.data_ptr(),
+                                    _stream(stream)), "csa2_index_score")
     return out
 
 

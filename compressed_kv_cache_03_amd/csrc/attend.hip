@@ -253,9 +253,12 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a, int chunk, int
                     for (int c = 0; c < NB; ++c)
                         *reinterpret_cast<uint2*>(dst + 2 * c) = uint2{cw[2 * c], cw[2 * c + 1]};
                 }
+                // an empty slot's scale is staged as 0, so its p = 0 meets finite data
+                // even where the record it was clamped to holds a non-finite scale
                 if (lane < kStep) {
+                    const bool live = (vmask >> lane) & 1u;
 #pragma unroll
-                    for (int blk = 0; blk < NB; ++blk) lscale[lane * NB + blk] = sw[blk];
+                    for (int blk = 0; blk < NB; ++blk) lscale[lane * NB + blk] = live ? sw[blk] : 0.0f;
                 }
             }
             load_rec(v + kStep, j_nxt);
@@ -334,6 +337,13 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a, int chunk, int
 #pragma unroll
                 for (int blk = 0; blk < NB; ++blk)
                     wvv[e][blk] = *reinterpret_cast<const uint32_t*>(a.wv + wrow(kslot_key(g, e)) * D + 32 * blk + 2 * m);
+            // value rows outside the valid tail (or past W) are zeroed: the caller may
+            // leave anything there, and p = 0 times a NaN or Inf would poison the sum
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (!((vmask >> kslot_key(g, e)) & 1u))
+#pragma unroll
+                    for (int blk = 0; blk < NB; ++blk) wvv[e][blk] = 0u;
             float z[8];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {

@@ -62,6 +62,13 @@ bool mfma_prefill(const csa2_group* g, int Qs) {
            g->k <= band_max_k() && g->pool_blocks == 0;
 }
 
+// Several bf16 query rows per sequence share each key load (score.hip), with a
+// queue of undecided scores in the workspace.
+bool rows_scorer(const csa2_group* g, int Qs) {
+    const int K = g->H_I * g->d_I;
+    return Qs >= 2 && g->idx_dtype == CSA2_IDX_BF16 && (K == 128 || K == 256);
+}
+
 int64_t pool_slots(const csa2_group* g) { return (int64_t)g->pool_blocks * CSA2_POOL_BLOCK; }
 int64_t block_count(int64_t N) { return (N + CSA2_POOL_BLOCK - 1) / CSA2_POOL_BLOCK; }
 
@@ -131,9 +138,7 @@ Layout layer_layout(const csa2_group* g, int Qs, int Hq, int W) {
         for (int64_t n : {N, block_count(N), pool_slots(g)})
             if (n > 0) slices = std::max(slices, (n + topk_slice_len(n) - 1) / topk_slice_len(n));
         add_topk(L, off, TopkShape{R, L.ld_scores, slices});
-        // several bf16 query rows per sequence share each key load (score.hip)
-        const int K = g->H_I * g->d_I;
-        L.rows_scorer = Qs >= 2 && g->idx_dtype == CSA2_IDX_BF16 && (K == 128 || K == 256);
+        L.rows_scorer = rows_scorer(g, Qs);
         if (L.rows_scorer) {
             L.fix_list = off;
             off = align_up(off + (size_t)R * N * 8);
@@ -202,6 +207,81 @@ hipError_t copy_rows(void* dst, size_t dpitch, const void* src, size_t spitch, s
     return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, rows, kind, s);
 }
 
+// Every check of csa2_layer_step except the workspace: arguments, group
+// geometry and state, and the launch sizes.  Touches no device.
+csa2_status check_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_group* g) {
+    if (!a || !g) return CSA2_ERR_INVALID_ARG;
+    if (mode != CSA2_MODE_FULL && mode != CSA2_MODE_REINDEX && mode != CSA2_MODE_REUSE)
+        return CSA2_ERR_INVALID_ARG;
+    // group geometry
+    if (g->B < 1 || g->N_cap < 1 || !valid_dim(g->D) || g->k < 1 || g->k > g->N_cap ||
+        !valid_index_width(g->idx_dtype, g->H_I, g->d_I))
+        return CSA2_ERR_INVALID_ARG;
+    if (g->N_cap >= (int64_t)1 << 31) return CSA2_ERR_UNSUPPORTED;
+    if (!g->codes || !g->scales || !g->ikeys || !g->n_valid || !g->sel) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(g->codes, 16) || !aligned(g->scales, 16) || !aligned(g->ikeys, 16) ||
+        !aligned(g->sel, 4) || !aligned(g->n_valid, 4))
+        return CSA2_ERR_INVALID_ARG;
+    if (g->idx_dtype == CSA2_IDX_FP4_E2M1 && (!g->ikey_scales || !aligned(g->ikey_scales, 16)))
+        return CSA2_ERR_INVALID_ARG;
+    if (g->pool_blocks < 0 ||
+        (g->pool_blocks > 0 && (pool_slots(g) < g->k || g->pool_blocks > block_count(g->N_cap) || !g->pool ||
+                                !aligned(g->pool, 4))))
+        return CSA2_ERR_INVALID_ARG;
+    // layer arguments
+    const int Qs = a->Qs;
+    if (Qs < 1 || a->Hq < 1 || a->Hq > 32 || a->W < 0 || a->W > 1024 || !std::isfinite(a->sm_scale))
+        return CSA2_ERR_INVALID_ARG;
+    if (g->n_valid_max < Qs || g->n_valid_max > g->N_cap) return CSA2_ERR_INVALID_ARG;
+    if ((int64_t)g->B * Qs > 65535) return CSA2_ERR_UNSUPPORTED;
+    if (g->sel_rows < (int64_t)g->B * Qs) return CSA2_ERR_INVALID_ARG;
+    if (!a->q || !a->out || (a->W > 0 && (!a->wk || !a->wv))) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(a->q, 16) || !aligned(a->out, 16) || (a->wk && !aligned(a->wk, 16)) ||
+        (a->wv && !aligned(a->wv, 16)))
+        return CSA2_ERR_INVALID_ARG;
+    const bool selects = mode != CSA2_MODE_REUSE;
+    if (selects && (!a->iq || !aligned(a->iq, 16))) return CSA2_ERR_INVALID_ARG;
+    if (mode == CSA2_MODE_FULL &&
+        (!a->new_entry || !a->new_ikey || !aligned(a->new_entry, 16) ||
+         !aligned(a->new_ikey, g->idx_dtype == CSA2_IDX_FP4_E2M1 ? 16 : 4)))
+        return CSA2_ERR_INVALID_ARG;
+    // group state
+    if (mode == CSA2_MODE_REINDEX && !g->has_entries) return CSA2_ERR_STATE;
+    if (mode == CSA2_MODE_REINDEX && g->pool_blocks > 0 && (!g->has_pool || g->pool_qs != Qs))
+        return CSA2_ERR_STATE;
+    if (mode == CSA2_MODE_REUSE && (!g->has_selection || g->sel_qs != Qs)) return CSA2_ERR_STATE;
+    const int K = g->H_I * g->d_I;
+    // launch sizes: HIP caps a grid at 2^32 - 1 work-items along x, which long
+    // rows times many query rows can exceed; refuse before anything is enqueued
+    if (selects && mfma_prefill(g, Qs)) {
+        GemmArgs ga{};
+        ga.K = K;
+        ga.B = g->B;
+        ga.Qs = Qs;
+        ga.N = g->n_valid_max;
+        ga.stride = (ga.N + kSampleCols - 1) / kSampleCols;
+        ga.ncols = (ga.N + ga.stride - 1) / ga.stride;
+        GemmArgs fa = ga;
+        fa.stride = 1;
+        fa.ncols = ga.N;
+        if (gemm_grid_threads(ga, 0) > kMaxGridThreads || gemm_grid_threads(fa, 1) > kMaxGridThreads)
+            return CSA2_ERR_UNSUPPORTED;
+    } else if (selects) {
+        const bool in_pool = mode == CSA2_MODE_REINDEX && g->pool_blocks > 0;
+        ScoreArgs sa{};
+        sa.dtype = score_dtype(g->idx_dtype);
+        sa.K = K;
+        sa.B = g->B;
+        sa.Qs = Qs;
+        sa.N = in_pool ? pool_slots(g) : g->n_valid_max;
+        sa.pool = in_pool ? g->pool : nullptr;
+        uint32_t queue_stand_in = 0;  // the plan only asks whether a queue exists
+        sa.fix_cnt = rows_scorer(g, Qs) ? &queue_stand_in : nullptr;
+        if (score_grid_threads(sa) > kMaxGridThreads) return CSA2_ERR_UNSUPPORTED;
+    }
+    return CSA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -234,6 +314,7 @@ csa2_status csa2_fp4_pack(const float* x, int64_t rows, int32_t dim, uint8_t* co
                           void* stream) {
     if (rows < 0 || dim <= 0 || dim % 32 != 0) return CSA2_ERR_INVALID_ARG;
     if (rows == 0) return CSA2_OK;
+    if (rows > kMaxGridThreads / (dim / 8)) return CSA2_ERR_UNSUPPORTED;  // one lane per 8 elements
     if (!x || !codes || !scales) return CSA2_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(codes, 4) || !aligned(scales, 4)) return CSA2_ERR_INVALID_ARG;
     return hip_status(launch_fp4_pack(x, rows, dim, codes, scales, nullptr, 1, rows,
@@ -242,8 +323,10 @@ csa2_status csa2_fp4_pack(const float* x, int64_t rows, int32_t dim, uint8_t* co
 
 csa2_status csa2_index_score(const void* iq, const void* ik, const float* ik_scales,
                              csa2_idx_dtype dtype, int32_t B, int32_t Qs, int64_t N, int32_t H,
-                             int32_t d, float* scores, void* stream) {
-    if (B < 0 || Qs < 1 || N < 0) return CSA2_ERR_INVALID_ARG;
+                             int32_t d, int64_t causal_offset, int32_t exact, float* scores,
+                             void* stream) {
+    (void)exact;  // every score is exact (see the header)
+    if (B < 0 || Qs < 1 || N < 0 || causal_offset < -1) return CSA2_ERR_INVALID_ARG;
     if (!valid_index_width(dtype, H, d)) return CSA2_ERR_INVALID_ARG;
     if (N >= (int64_t)1 << 31) return CSA2_ERR_UNSUPPORTED;
     if (B == 0 || N == 0) return CSA2_OK;
@@ -263,10 +346,15 @@ csa2_status csa2_index_score(const void* iq, const void* ik, const float* ik_sca
     a.N = N;
     a.N_cap = N;
     a.nvb = nullptr;
+    a.causal = causal_offset;
     a.scores = scores;
     a.ld = N;
     a.hist = nullptr;
-    return hip_status(launch_score_exact(a, static_cast<hipStream_t>(stream)));
+    if (score_grid_threads(a) > kMaxGridThreads) return CSA2_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_score_exact(a, s);
+    if (e == hipSuccess) e = launch_score_tail(a, s);
+    return hip_status(e);
 }
 
 size_t csa2_topk_workspace_bytes(int64_t R, int64_t N, int32_t k) {
@@ -369,46 +457,10 @@ size_t csa2_layer_workspace_bytes(const csa2_group* g, int32_t Qs, int32_t Hq, i
 
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group* g, void* ws,
                             size_t ws_bytes, void* stream) {
-    if (!a || !g) return CSA2_ERR_INVALID_ARG;
-    if (mode != CSA2_MODE_FULL && mode != CSA2_MODE_REINDEX && mode != CSA2_MODE_REUSE)
-        return CSA2_ERR_INVALID_ARG;
-    // group geometry
-    if (g->B < 1 || g->N_cap < 1 || !valid_dim(g->D) || g->k < 1 || g->k > g->N_cap ||
-        !valid_index_width(g->idx_dtype, g->H_I, g->d_I))
-        return CSA2_ERR_INVALID_ARG;
-    if (g->N_cap >= (int64_t)1 << 31) return CSA2_ERR_UNSUPPORTED;
-    if (!g->codes || !g->scales || !g->ikeys || !g->n_valid || !g->sel) return CSA2_ERR_INVALID_ARG;
-    if (!aligned(g->codes, 16) || !aligned(g->scales, 16) || !aligned(g->ikeys, 16) ||
-        !aligned(g->sel, 4) || !aligned(g->n_valid, 4))
-        return CSA2_ERR_INVALID_ARG;
-    if (g->idx_dtype == CSA2_IDX_FP4_E2M1 && (!g->ikey_scales || !aligned(g->ikey_scales, 16)))
-        return CSA2_ERR_INVALID_ARG;
-    if (g->pool_blocks < 0 ||
-        (g->pool_blocks > 0 && (pool_slots(g) < g->k || g->pool_blocks > block_count(g->N_cap) || !g->pool ||
-                                !aligned(g->pool, 4))))
-        return CSA2_ERR_INVALID_ARG;
-    // layer arguments
+    const csa2_status st = check_layer(mode, a, g);
+    if (st != CSA2_OK) return st;
     const int Qs = a->Qs;
-    if (Qs < 1 || a->Hq < 1 || a->Hq > 32 || a->W < 0 || a->W > 1024 || !std::isfinite(a->sm_scale))
-        return CSA2_ERR_INVALID_ARG;
-    if (g->n_valid_max < Qs || g->n_valid_max > g->N_cap) return CSA2_ERR_INVALID_ARG;
-    if ((int64_t)g->B * Qs > 65535) return CSA2_ERR_UNSUPPORTED;
-    if (g->sel_rows < (int64_t)g->B * Qs) return CSA2_ERR_INVALID_ARG;
-    if (!a->q || !a->out || (a->W > 0 && (!a->wk || !a->wv))) return CSA2_ERR_INVALID_ARG;
-    if (!aligned(a->q, 16) || !aligned(a->out, 16) || (a->wk && !aligned(a->wk, 16)) ||
-        (a->wv && !aligned(a->wv, 16)))
-        return CSA2_ERR_INVALID_ARG;
     const bool selects = mode != CSA2_MODE_REUSE;
-    if (selects && (!a->iq || !aligned(a->iq, 16))) return CSA2_ERR_INVALID_ARG;
-    if (mode == CSA2_MODE_FULL &&
-        (!a->new_entry || !a->new_ikey || !aligned(a->new_entry, 16) ||
-         !aligned(a->new_ikey, g->idx_dtype == CSA2_IDX_FP4_E2M1 ? 16 : 4)))
-        return CSA2_ERR_INVALID_ARG;
-    // group state
-    if (mode == CSA2_MODE_REINDEX && !g->has_entries) return CSA2_ERR_STATE;
-    if (mode == CSA2_MODE_REINDEX && g->pool_blocks > 0 && (!g->has_pool || g->pool_qs != Qs))
-        return CSA2_ERR_STATE;
-    if (mode == CSA2_MODE_REUSE && (!g->has_selection || g->sel_qs != Qs)) return CSA2_ERR_STATE;
     // workspace
     const Layout L = layer_layout(g, Qs, a->Hq, a->W);
     if (!ws || ws_bytes < L.total || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;

@@ -460,6 +460,14 @@ hipError_t launch_gemm_fp8(GemmArgs a, int mode, hipStream_t stream) {
     return hipGetLastError();
 }
 
+int64_t gemm_grid_threads(const GemmArgs& a, int mode) {
+    if (a.Qs == 0 || a.B == 0 || a.ncols == 0) return 0;
+    const int rows = mode == 0 ? kSRows : kFRows;
+    const int64_t cols = mode == 0 ? kGCols : kFBlkCols;
+    const int64_t tiles = (int64_t)a.B * ((a.ncols + cols - 1) / cols) * ((a.Qs + rows - 1) / rows);
+    return 8 * ((tiles + 7) / 8) * (mode == 0 ? kSThreads : kFThreads);
+}
+
 int64_t filter_colblks(int64_t ncols) { return (ncols + kFBlkCols - 1) / kFBlkCols; }
 int filter_blk_cap() { return kFBlkCap; }
 

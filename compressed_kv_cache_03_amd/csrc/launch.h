@@ -42,9 +42,13 @@ hipError_t launch_fp4_pack(const float* x, int64_t rows, int dim, uint8_t* codes
 hipError_t launch_store_rows(const void* src, int64_t rows, int row_bytes, void* dst,
                              const int32_t* nvb, int Qs, int64_t N_cap, hipStream_t stream);
 
+// Largest global size (work-items along one grid dimension) a launch may have.
+constexpr int64_t kMaxGridThreads = 0xffffffffLL;
+
 // S2: exact index scores.  Row r = b*Qs + i scores entries j < nv(r) of
-// sequence b (ik row stride N_cap entries), where nv(r) = N when nvb is null and
-// nvb[b] - Qs + i + 1 otherwise (clamped to [0, N]).  Writes scores[r*ld + j].
+// sequence b (ik row stride N_cap entries), where nv(r) = nvb[b] - Qs + i + 1
+// when nvb is set, causal + i + 1 when causal >= 0, and N otherwise (clamped to
+// [0, N]).  Writes scores[r*ld + j].
 // When hist != nullptr, also accumulates the first radix digit histogram of
 // every written score into hist[r*4096 + digit].
 struct ScoreArgs {
@@ -57,6 +61,7 @@ struct ScoreArgs {
     int64_t N;            // entries to consider per sequence (<= N_cap)
     int64_t N_cap;        // entry row stride of ik
     const int32_t* nvb;   // [B] or null
+    int64_t causal = -1;  // with nvb null: row i sees j <= causal + i (-1: every entry)
     float* scores;        // [R][ld]
     int64_t ld;
     uint32_t* hist;       // [R][4096] or null
@@ -77,6 +82,10 @@ struct ScoreArgs {
     int64_t n_eblk = 0, blocks = 0, per_xcd = 0;
 };
 hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t stream);
+// Work-items along x of the launches launch_score_exact would make for a.
+int64_t score_grid_threads(const ScoreArgs& a);
+// scores[r*ld + j] = -inf for nv(r) <= j < N (a causal cut-off's hidden entries).
+hipError_t launch_score_tail(const ScoreArgs& a, hipStream_t stream);
 
 // Hierarchical search helpers (pool.hip), positions grouped in blocks of 8.
 constexpr int kPoolBlock = 8;
@@ -157,6 +166,7 @@ struct GemmArgs {
     int cap;
 };
 hipError_t launch_gemm_fp8(GemmArgs a, int mode, hipStream_t stream);
+int64_t gemm_grid_threads(const GemmArgs& a, int mode);  // work-items along x of that launch
 int64_t filter_colblks(int64_t ncols);  // column-block regions per row of the filter
 int filter_blk_cap();                   // candidates per region
 

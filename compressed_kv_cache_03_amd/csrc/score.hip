@@ -73,7 +73,11 @@ CSA2_DEV int64_t row_valid(const ScoreArgs& a, int64_t r) {
         const int64_t v = a.pool_nv[r];
         return v < 0 ? 0 : (v > a.N ? a.N : v);
     }
-    if (!a.nvb) return a.N;
+    if (!a.nvb) {
+        if (a.causal < 0) return a.N;
+        const int64_t nv = a.causal + r % a.Qs + 1;
+        return nv > a.N ? a.N : nv;
+    }
     const int64_t b = r / a.Qs, i = r % a.Qs;
     int64_t nv = (int64_t)a.nvb[b] - a.Qs + i + 1;
     return nv < 0 ? 0 : (nv > a.N ? a.N : nv);
@@ -869,19 +873,72 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
     if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
 }
 
+// Which scoring kernel a call takes, with its tiling (n_eblk, blocks, per_xcd
+// filled in a).  ROWS: several rows share key loads; STREAM: one row per
+// workgroup tile; GENERIC: one thread per entry.
+enum class ScorePath { ROWS, STREAM, GENERIC };
+
+static ScorePath plan_score(ScoreArgs& a, int* cpl_out, int* qr_out) {
+    const int64_t R = (int64_t)a.B * a.Qs;
+    const int eb = a.dtype == 0 ? a.K * 2 : a.dtype == 1 ? a.K : a.K / 2;  // key bytes per entry
+    const int cpl = eb / 128;
+    *cpl_out = cpl;
+    *qr_out = 1;
+    const bool fast = eb % 128 == 0 && (cpl == 1 || cpl == 2 || cpl == 4 || cpl == 8);
+    if (a.dtype == 0 && a.Qs >= 2 && !a.pool && a.fix_cnt && eb % 128 == 0 && (cpl == 2 || cpl == 4)) {
+        const int QR = a.Qs <= 5 ? a.Qs : 4;
+        *qr_out = QR;
+        a.n_eblk = (a.N + kRowsEntriesPerBlock - 1) / kRowsEntriesPerBlock;
+        a.blocks = a.n_eblk * a.B * ((a.Qs + QR - 1) / QR);
+        a.per_xcd = (a.blocks + 7) / 8;
+        return ScorePath::ROWS;
+    }
+    if (fast) {
+        a.n_eblk = (a.N + kScoreEntriesPerBlock - 1) / kScoreEntriesPerBlock;
+        a.blocks = a.n_eblk * R;
+        a.per_xcd = (a.blocks + 7) / 8;
+        return ScorePath::STREAM;
+    }
+    return ScorePath::GENERIC;
+}
+
+int64_t score_grid_threads(const ScoreArgs& args) {
+    ScoreArgs a = args;
+    if ((int64_t)a.B * a.Qs == 0 || a.N == 0) return 0;
+    int cpl, qr;
+    switch (plan_score(a, &cpl, &qr)) {
+        case ScorePath::ROWS: return 8 * a.per_xcd * kScoreThreads;
+        case ScorePath::STREAM: return 8 * a.per_xcd * kStreamThreads;
+        default: return (a.N + 255) / 256 * 256;
+    }
+}
+
+__global__ __launch_bounds__(256) void score_tail_kernel(ScoreArgs a, int64_t e0) {
+    const int64_t r = blockIdx.y;
+    const int64_t e = e0 + (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e < a.N && e >= row_valid(a, r)) a.scores[r * a.ld + e] = -INFINITY;
+}
+
+hipError_t launch_score_tail(const ScoreArgs& a, hipStream_t stream) {
+    const int64_t R = (int64_t)a.B * a.Qs;
+    if (R == 0 || a.N == 0 || a.pool || (!a.nvb && a.causal < 0)) return hipSuccess;
+    // row 0 sees the fewest entries; nothing before its cut is hidden in any row
+    int64_t first = a.nvb ? 0 : (a.causal + 1 < a.N ? a.causal + 1 : a.N);
+    first = first / 256 * 256;
+    if (first >= a.N) return hipSuccess;
+    const dim3 grid((unsigned)((a.N - first + 255) / 256), (unsigned)R);
+    hipLaunchKernelGGL(score_tail_kernel, grid, dim3(256), 0, stream, a, first);
+    return hipGetLastError();
+}
+
 hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
     ScoreArgs a = args;
     const int64_t R = (int64_t)a.B * a.Qs;
     if (R == 0 || a.N == 0) return hipSuccess;
-    const int eb = a.dtype == 0 ? a.K * 2 : a.dtype == 1 ? a.K : a.K / 2;  // key bytes per entry
-    const int cpl = eb / 128;
-    const bool fast = eb % 128 == 0 && (cpl == 1 || cpl == 2 || cpl == 4 || cpl == 8);
-    if (a.dtype == 0 && a.Qs >= 2 && !a.pool && a.fix_cnt && eb % 128 == 0 && (cpl == 2 || cpl == 4)) {
+    int cpl, QR;
+    const ScorePath path = plan_score(a, &cpl, &QR);
+    if (path == ScorePath::ROWS) {
         // several rows of a sequence share every key load
-        const int QR = a.Qs <= 5 ? a.Qs : 4;
-        a.n_eblk = (a.N + kRowsEntriesPerBlock - 1) / kRowsEntriesPerBlock;
-        a.blocks = a.n_eblk * a.B * ((a.Qs + QR - 1) / QR);
-        a.per_xcd = (a.blocks + 7) / 8;
         const dim3 grid((unsigned)(8 * a.per_xcd));
 #define CSA2_ROWS_LAUNCH(CPLV, QRV)                                                                      \
     if (cpl == CPLV && QR == QRV)                                                                        \
@@ -896,10 +953,7 @@ hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
         CSA2_ROWS_LAUNCH(4, 5)
 #undef CSA2_ROWS_LAUNCH
         hipLaunchKernelGGL(score_fixup_kernel, dim3(256), dim3(kScoreThreads), 0, stream, a);
-    } else if (fast) {
-        a.n_eblk = (a.N + kScoreEntriesPerBlock - 1) / kScoreEntriesPerBlock;
-        a.blocks = a.n_eblk * R;
-        a.per_xcd = (a.blocks + 7) / 8;
+    } else if (path == ScorePath::STREAM) {
         const dim3 grid((unsigned)(8 * a.per_xcd));
         const bool pool = a.pool != nullptr;
 #define CSA2_SCORE_LAUNCH(DTV, CPLV)                                                                   \

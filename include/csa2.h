@@ -154,12 +154,22 @@ csa2_status csa2_fp4_pack(const float* x, int64_t rows, int32_t dim, uint8_t* co
  * LLMs", section 5).  iq: [B][Qs][H][d], ik: [B][N][H][d] in `dtype`
  * (FP4_E2M1: iq bf16, ik the codes [B][N][H*d/2] and ik_scales [B][N][H*d/32];
  * ik_scales is ignored for the other dtypes); scores: fp32 [B][Qs][N], each
- * the exact sum rounded once to fp32 (see the top of this file).  H*d must be
- * a multiple of 64 (bf16), 128 (fp8) or 256 (FP4) for the streaming kernel,
- * and at most 4096.  N == 0 is a no-op. */
+ * the exact sum rounded once to fp32 (see the top of this file).
+ * causal_offset: -1 scores every entry for every query row; c >= 0 makes row i
+ * of each sequence a causal query at position c + i ("Why Is DeepSeek V4.1
+ * Flash So Fast?", section 3: a query retrieves from the positions before it):
+ * it scores entries j <= c + i, and scores[.., i, j] = -inf for the others.
+ * exact: 1 asks for the exactly rounded scores; 0 allows a faster, inexact
+ * variant.  Both give the exact scores: for bf16 and fp8 keys the exact stream
+ * already runs at the memory bound, so no second, inexact kernel is kept.
+ * H*d must be a multiple of 64 (bf16), 128 (fp8) or 256 (FP4) for the
+ * streaming kernel, and at most 4096.  N == 0 is a no-op.  CSA2_ERR_UNSUPPORTED
+ * when B*Qs > 65535, N >= 2^31 or the launch would exceed 2^32 - 1 work-items
+ * (about B*Qs*N > 4.29e9), with nothing enqueued. */
 csa2_status csa2_index_score(const void* iq, const void* ik, const float* ik_scales,
                              csa2_idx_dtype dtype, int32_t B, int32_t Qs, int64_t N, int32_t H,
-                             int32_t d, float* scores, void* stream);
+                             int32_t d, int64_t causal_offset, int32_t exact, float* scores,
+                             void* stream);
 
 /* S3 - Top-k selection ("Why Is DeepSeek V4.1 Flash So Fast?", sections 3 and
  * 4: select the useful compressed positions).  scores: fp32 [R][ld], row r
@@ -178,7 +188,9 @@ csa2_status csa2_topk(const float* scores, int64_t R, int64_t N, int64_t ld,
  * other values must be < N); wk, wv: bf16 [B][Qs+W-1][D], query row i uses
  * window rows i..i+W-1 of which only the last wlen[b] rows of the buffer are
  * valid (wlen NULL = all); out fp32 [B][Qs][Hq][D]; lse fp32 [B][Qs][Hq] or
- * NULL.  A row with nothing to attend gets out = 0 and lse = -inf. */
+ * NULL.  A row with nothing to attend gets out = 0 and lse = -inf.  Window rows
+ * outside the valid tail and records no slot selects never reach the result,
+ * so they may hold any bits (NaN and Inf included). */
 size_t csa2_attend_workspace_bytes(int32_t B, int32_t Qs, int32_t Hq, int32_t D, int32_t k,
                                    int32_t W);
 csa2_status csa2_sparse_attend(const void* q, int32_t B, int32_t Qs, int32_t Hq, int32_t D,

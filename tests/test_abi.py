@@ -54,15 +54,21 @@ def test_fp4_pack_validation():
 
 def test_index_score_validation():
     L = csa2.lib()
-    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 1, 10, 64, 65, FAKE, None) == csa2.ERR_INVALID_ARG
-    assert L.csa2_index_score(FAKE, FAKE, None, 7, 1, 1, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
-    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 0, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
-    assert L.csa2_index_score(None, FAKE, None, 0, 1, 1, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
-    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 1, 1 << 31, 4, 64, FAKE, None) == csa2.ERR_UNSUPPORTED
-    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 1, 0, 4, 64, FAKE, None) == csa2.OK
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 1, 10, 64, 65, -1, 1, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, None, 7, 1, 1, 10, 4, 64, -1, 1, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 0, 10, 4, 64, -1, 1, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(None, FAKE, None, 0, 1, 1, 10, 4, 64, -1, 1, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 1, 1 << 31, 4, 64, -1, 1, FAKE, None) == csa2.ERR_UNSUPPORTED
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 1, 0, 4, 64, -1, 1, FAKE, None) == csa2.OK
     # FP4 keys need their scales, and whole 32-element blocks
-    assert L.csa2_index_score(FAKE, FAKE, None, 2, 1, 1, 10, 4, 64, FAKE, None) == csa2.ERR_INVALID_ARG
-    assert L.csa2_index_score(FAKE, FAKE, FAKE, 2, 1, 1, 10, 1, 48, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, None, 2, 1, 1, 10, 4, 64, -1, 1, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, FAKE, 2, 1, 1, 10, 1, 48, -1, 1, FAKE, None) == csa2.ERR_INVALID_ARG
+    # causal offsets below -1 are invalid; 0 and beyond are accepted for any N
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 1, 1, 10, 4, 64, -2, 1, FAKE, None) == csa2.ERR_INVALID_ARG
+    # a launch beyond 2^32 - 1 work-items (B*Qs*N about 4.3e9) is refused before anything is enqueued
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 4096, 1, 1 << 20, 4, 64, -1, 1, FAKE, None) == csa2.ERR_UNSUPPORTED
+    assert L.csa2_index_score(FAKE, FAKE, None, 0, 64, 64, 1 << 20, 4, 64, 5, 0, FAKE, None) == csa2.ERR_UNSUPPORTED
+    assert L.csa2_fp4_pack(FAKE, 1 << 33, 128, FAKE, FAKE, None) == csa2.ERR_UNSUPPORTED
 
 
 def test_topk_validation():
@@ -135,6 +141,13 @@ def test_layer_step_argument_errors():
     assert _step(0, _group(), _args(Hq=0)) == csa2.ERR_INVALID_ARG
     assert _step(0, _group(), _args(), ws_bytes=100) == csa2.ERR_WORKSPACE
     assert _step(0, _group(B=70000), _args()) == csa2.ERR_UNSUPPORTED
+    # launches beyond 2^32 - 1 work-items are refused before the Full layer writes anything:
+    # the decode score stream (B * N > 4.3e9) and the prefill score GEMM
+    big = dict(B=8192, N_cap=1 << 20, n_valid_max=1 << 20, sel_rows=8192)
+    assert _step(0, _group(**big), _args()) == csa2.ERR_UNSUPPORTED
+    assert _step(1, _group(**big), _args()) == csa2.ERR_UNSUPPORTED
+    pre = dict(B=1, N_cap=1 << 30, n_valid_max=1 << 30, idx_dtype=1, sel_rows=60000)
+    assert _step(0, _group(**pre), _args(Qs=60000)) == csa2.ERR_UNSUPPORTED
 
 
 def test_group_image_bytes_and_save_restore_validation():

@@ -70,6 +70,27 @@ def test_index_score_parity(dtype, H, d, Qs):
     assert bits_eq(host(got), ref)
 
 
+@pytest.mark.parametrize("dtype,H,d", [("bf16", 4, 64), ("e4m3", 4, 64), ("bf16", 3, 32), ("fp4", 4, 64)])
+@pytest.mark.parametrize("causal", [0, 1000, 2990, 5000])
+def test_index_score_causal_offset(dtype, H, d, causal):
+    # row i of a causal chunk scores entries j <= causal + i and reads -inf beyond
+    B, Qs, N = 2, 12, 2999
+    if dtype == "fp4":
+        rng = np.random.default_rng(causal + 1)
+        iq, ik, ks = _fp4_key_case(rng, B, N, H, d)
+        iq = np.concatenate([iq] * (Qs // 2), axis=1)
+        g_ks, o_ks = dev(ks), ks
+    else:
+        iq = synth.normal_idx(dtype, synth.seed(0, 912), B * Qs * H * d).reshape(B, Qs, H, d)
+        ik = synth.normal_idx(dtype, synth.seed(0, 913), B * N * H * d).reshape(B, N, H, d)
+        g_ks = o_ks = None
+    got = csa2.index_score(dev(iq), dev(ik), dtype, ik_scales=g_ks, causal_offset=causal, exact=False)
+    torch.cuda.synchronize()
+    nv = np.array([[causal + i + 1 for i in range(Qs)]] * B, np.int64).reshape(-1)
+    ref = oracle.index_score(dtype, iq, ik, n_valid_row=np.minimum(nv, N), ik_scales=o_ks)
+    assert bits_eq(host(got), ref)
+
+
 def test_index_score_fp8_every_code():
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
     n = codes.size
@@ -256,6 +277,36 @@ def test_attend_parity(B, Qs, Hq, D, W, k, wlen):
     assert np.all(host(out)[~fin] == 0)
 
 
+def test_attend_never_reads_invalid_window_rows_or_empty_slots():
+    # rows before the valid tail of the window hold NaN / Inf, and the record every
+    # empty (-1) slot is clamped to has a NaN scale: none of them may reach the result
+    B, Qs, Hq, D, W, k, N = 3, 3, 16, 128, 40, 70, 500
+    rng = np.random.default_rng(77)
+    x = synth.normal_f32(synth.seed(0, 930), B * N * D).reshape(B * N, D)
+    oc, os_ = oracle.fp4_pack(x)
+    oc, os_ = oc.reshape(B, N, D // 2), os_.reshape(B, N, D // 32)
+    os_[:, 0, :] = np.nan
+    wrows = Qs + W - 1
+    q = synth.normal_bf16(synth.seed(0, 931), B * Qs * Hq * D).reshape(B, Qs, Hq, D)
+    wk = synth.normal_bf16(synth.seed(0, 932), B * wrows * D).reshape(B, wrows, D)
+    wv = synth.normal_bf16(synth.seed(0, 933), B * wrows * D).reshape(B, wrows, D)
+    wl = np.array([5, 1, wrows - 2], np.int32)
+    for b in range(B):
+        wk[b, : wrows - wl[b]] = 0x7FC0  # NaN
+        wv[b, : wrows - wl[b]] = 0x7F80  # +Inf
+    idx = np.full((B * Qs, k), -1, np.int32)
+    for r in range(B * Qs):
+        m = int(rng.integers(1, k - 5))
+        idx[r, :m] = np.sort(rng.choice(np.arange(1, N), m, replace=False))
+    out, lse = csa2.sparse_attend(dev(q), dev(oc), dev(os_), dev(idx), dev(wk), dev(wv), W, 1 / np.sqrt(D),
+                                  wlen=dev(wl))
+    torch.cuda.synchronize()
+    ro, rl = oracle.attend(q, oc, os_, idx, wk, wv, W, np.float32(1 / np.sqrt(D)), wlen=wl)
+    assert np.all(np.isfinite(ro)) and np.all(np.isfinite(host(out)))
+    assert rel_err(host(out), ro) <= TOL
+    assert np.allclose(host(lse), rl, rtol=0, atol=TOL)
+
+
 # ---------------------------------------------------------------- S4 layer steps
 class Run:
     """One workload run through both sides, layer by layer."""
@@ -367,9 +418,12 @@ def test_group_save_restore_resumes_bitwise():
     for a, b in zip(before, after):
         assert bits_eq(a, b)
     for li in range(2, 4):
-        mode, _, _, _, go, gl = run.layer(li)
+        mode, gi, ro, rl, go, gl = run.layer(li)
         assert mode == "Ru"
         assert bits_eq(go, ref_out[li][0]) and bits_eq(gl, ref_out[li][1]), li
+        # and the resumed layers still match the oracle, which never left the host
+        assert np.array_equal(host(run.g_gpu[gi].sel), run.g_orc[gi].sel)
+        assert rel_err(go, ro) <= TOL and np.allclose(gl, rl, rtol=0, atol=TOL), li
 
 
 def test_hierarchical_group_save_restore_keeps_the_pool():
@@ -392,10 +446,14 @@ def test_hierarchical_group_save_restore_keeps_the_pool():
     g.restore(image)
     torch.cuda.synchronize()
     assert bits_eq(host(g.pool), pool_before)
-    mode, _, _, _, go, gl = run.layer(1)
+    mode, _, ro, rl, go, gl = run.layer(1)
     assert mode == "Ri"
     assert np.array_equal(host(g.sel), ref_sel)
     assert bits_eq(go, ref_res[1][4]) and bits_eq(gl, ref_res[1][5])
+    # the Reindex after the restore against the oracle's own pool and selection
+    assert np.array_equal(host(g.sel), run.g_orc[0].sel)
+    assert np.array_equal(host(g.pool)[:, :50], run.g_orc[0].pool[:, :50])
+    assert rel_err(go, ro) <= TOL and np.allclose(gl, rl, rtol=0, atol=TOL)
 
 
 def test_w7_scaled_fp4_index_keys():
