@@ -31,6 +31,7 @@ class CGroup(ctypes.Structure):
                 ("pool_qs", i32)]
 
 POOL_BLOCK = 8  # entries per block of a hierarchical group's pool
+STATIC_SCRATCH_BYTES = 128 << 20  # scratch of csa2_layer_step_noalloc, per GPU
 
 
 class CLayerArgs(ctypes.Structure):
@@ -73,6 +74,8 @@ def _load():
     lib.csa2_layer_workspace_bytes.restype = sz
     lib.csa2_layer_step.argtypes = [ctypes.c_int, ctypes.POINTER(CLayerArgs), ctypes.POINTER(CGroup),
                                     vp, sz, vp]
+    lib.csa2_layer_step_noalloc.argtypes = [ctypes.c_int, ctypes.POINTER(CLayerArgs), ctypes.POINTER(CGroup),
+                                            vp]
     lib.csa2_group_image_bytes.argtypes = [ctypes.POINTER(CGroup)]
     lib.csa2_group_image_bytes.restype = sz
     lib.csa2_group_save.argtypes = [ctypes.POINTER(CGroup), vp, sz, vp]
@@ -80,7 +83,7 @@ def _load():
     lib.csa2_cache_bytes.argtypes = [i64, i64, i64, i64]
     lib.csa2_cache_bytes.restype = i64
     for name in ("csa2_fp4_pack", "csa2_index_score", "csa2_topk", "csa2_sparse_attend",
-                 "csa2_layer_step", "csa2_group_save", "csa2_group_restore"):
+                 "csa2_layer_step", "csa2_layer_step_noalloc", "csa2_group_save", "csa2_group_restore"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -267,6 +270,21 @@ class Group:
         st = _load().csa2_layer_step(MODE[mode], ctypes.byref(a), ctypes.byref(self.c), ws.data_ptr(),
                                      ws.numel(), _stream(stream))
         _check(st, f"csa2_layer_step({mode})")
+        return out, lse
+
+    def layer_step_noalloc(self, mode: str, q, wk, wv, W: int, sm_scale: float, iq=None, new_entry=None,
+                           new_ikey=None, wlen=None, out=None, lse=None, stream=None):
+        """layer_step through csa2_layer_step_noalloc: the library's own per-GPU scratch replaces
+        the workspace.  out and lse must be given to allocate nothing here either."""
+        B, Qs, Hq, D = q.shape
+        if out is None:
+            out = torch.empty(B, Qs, Hq, D, dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty(B, Qs, Hq, dtype=torch.float32, device=q.device)
+        a = CLayerArgs(Qs, Hq, q.data_ptr(), _ptr(iq), _ptr(wk), _ptr(wv), W, _ptr(wlen),
+                       _ptr(new_entry), _ptr(new_ikey), float(sm_scale), out.data_ptr(), _ptr(lse))
+        st = _load().csa2_layer_step_noalloc(MODE[mode], ctypes.byref(a), ctypes.byref(self.c), _stream(stream))
+        _check(st, f"csa2_layer_step_noalloc({mode})")
         return out, lse
 
     def image_bytes(self) -> int:

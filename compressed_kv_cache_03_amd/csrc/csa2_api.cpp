@@ -2,8 +2,8 @@
 //
 // Host side only: argument validation (before anything is launched), the
 // workspace layout, the Full / Reindex / Reuse plumbing of a sharing group, and
-// the kernel launches.  No entry point allocates, synchronises or keeps global
-// state.
+// the kernel launches.  No entry point allocates or synchronises; the only
+// global state is the per-device scratch of csa2_layer_step_noalloc.
 #include "../../include/csa2.h"
 
 #include <hip/hip_runtime.h>
@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "launch.h"
 
@@ -280,6 +281,36 @@ csa2_status check_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_gro
         if (score_grid_threads(sa) > kMaxGridThreads) return CSA2_ERR_UNSUPPORTED;
     }
     return CSA2_OK;
+}
+
+}  // namespace
+
+// Scratch of csa2_layer_step_noalloc: one copy per GPU, held until the process
+// ends.  Host code never names it: its device address comes from
+// hipGetSymbolAddress, resolved once per device (see static_scratch below).
+static __device__ __align__(256) unsigned char scratch[CSA2_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up on the first
+// call on that device (with it current) and kept for later calls.
+hipError_t static_scratch(void** ptr) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    *ptr = g_scratch_ptr[dev];
+    return g_scratch_err[dev];
 }
 
 }  // namespace
@@ -664,6 +695,16 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         g->pool_qs = Qs;
     }
     return CSA2_OK;
+}
+
+csa2_status csa2_layer_step_noalloc(csa2_mode mode, const csa2_layer_args* a, csa2_group* g,
+                                    void* stream) {
+    const csa2_status st = check_layer(mode, a, g);
+    if (st != CSA2_OK) return st;
+    if (layer_layout(g, a->Qs, a->Hq, a->W).total > CSA2_STATIC_SCRATCH_BYTES) return CSA2_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (static_scratch(&ws) != hipSuccess || !ws) return CSA2_ERR_HIP;
+    return csa2_layer_step(mode, a, g, ws, CSA2_STATIC_SCRATCH_BYTES, stream);
 }
 
 size_t csa2_group_image_bytes(const csa2_group* g) {

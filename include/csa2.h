@@ -30,9 +30,9 @@
  *     and contiguous, 16-byte aligned.  bf16 and fp8 tensors are passed as raw
  *     bytes (const void*).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
- *     asynchronously; no entry point synchronises, allocates device memory or
- *     keeps global mutable state, so calls on different streams with disjoint
- *     buffers may run concurrently.
+ *     asynchronously; no entry point synchronises or allocates device memory,
+ *     and none but csa2_layer_step_noalloc keeps global mutable state, so calls
+ *     on different streams with disjoint buffers may run concurrently.
  *   - Arguments are validated on the host before anything is launched; on an
  *     error nothing is enqueued and the status says why.  A launch failure
  *     returns CSA2_ERR_HIP.  No C++ exception crosses this interface.
@@ -217,6 +217,24 @@ csa2_status csa2_sparse_attend(const void* q, int32_t B, int32_t Qs, int32_t Hq,
 size_t csa2_layer_workspace_bytes(const csa2_group* g, int32_t Qs, int32_t Hq, int32_t W);
 csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group* g, void* ws,
                             size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer step as csa2_layer_step, with the workspace taken from a scratch array
+ * of CSA2_STATIC_SCRATCH_BYTES that the library keeps in device memory on each
+ * GPU it runs on, from the first call there until the process ends.  It
+ * allocates nothing.  Returns CSA2_ERR_WORKSPACE, with nothing enqueued, when
+ * the layer needs more (csa2_layer_workspace_bytes > CSA2_STATIC_SCRATCH_BYTES;
+ * a decode step needs about 12 bytes per (query row, entry slot) plus the
+ * attention partials, so up to about 10 million slots fit, B = 64 at N =
+ * 131,072 among them; prefill chunks do not); other errors as csa2_layer_step.  Every call on one GPU uses that GPU's one array,
+ * which keeps the last call's contents (each call sets what it needs before
+ * reading it): calls that overlap in time on one GPU (several streams or host
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe. */
+#define CSA2_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+csa2_status csa2_layer_step_noalloc(csa2_mode mode, const csa2_layer_args* a, csa2_group* g,
+                                    void* stream);
 
 /* S7 - Cache accounting ("DeepSeek-V4.1-Flash", "Several mechanisms in one
  * release": entries x numbers per entry x stored layer copies x bits per

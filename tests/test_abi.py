@@ -194,3 +194,17 @@ def test_hierarchical_pool_validation_and_image():
     assert L.csa2_group_image_bytes(ctypes.byref(g)) == 2 * 10 * per_entry + 2 * 64 * 4 + 2 * 8 * 4
     assert L.csa2_group_save(ctypes.byref(_group(has_pool=1, pool_qs=1, pool_blocks=8)), FAKE, 10 ** 9,
                              None) == csa2.ERR_INVALID_ARG  # image with a pool needs the buffer
+
+
+def test_layer_step_noalloc_validation():
+    # the same checks as csa2_layer_step, then the scratch limit; all before any HIP call
+    L = csa2.lib()
+    ab = lambda g, a, mode=0: L.csa2_layer_step_noalloc(mode, ctypes.byref(a), ctypes.byref(g), None)  # noqa: E731
+    assert ab(_group(), _args(), mode=2) == csa2.ERR_STATE
+    assert ab(_group(D=100), _args()) == csa2.ERR_INVALID_ARG
+    assert ab(_group(B=70000), _args()) == csa2.ERR_UNSUPPORTED
+    # a layer whose workspace exceeds the static scratch is refused
+    g = _group(B=64, N_cap=131072, n_valid_max=131072, sel_rows=64 * 5)
+    assert L.csa2_layer_workspace_bytes(ctypes.byref(g), 5, 16, 128) > csa2.STATIC_SCRATCH_BYTES
+    assert ab(g, _args(Qs=5)) == csa2.ERR_WORKSPACE
+    assert L.csa2_layer_workspace_bytes(ctypes.byref(g), 1, 16, 128) <= csa2.STATIC_SCRATCH_BYTES
