@@ -1,23 +1,36 @@
 """CSA2 decode benchmark on one MI355X.
 
-One step = one decode token for every sequence of the batch through every layer of
-the workload (default: batch 32, 65,536 FP4 entries per sequence, one sharing group in
-modes Full, Reindex, Reuse, Reuse, top-k 2048, 16 bf16 heads of dim 128, window 128).
-Inputs are seeded synthetic N(0,1) data already resident in HBM when timing starts.
+One step = one decode token for every sequence of the batch through every layer of the
+workload.  The headline workload is the largest single-GPU decode configuration: the
+16-layer stack, batch 64, 131,072 FP4 entries per sequence, four sharing groups in modes
+Full, Reindex, Reuse, Reuse, top-k 2048, 16 bf16 heads of dim 128, window 128, bf16 index
+keys 4 x 64.  Inputs are seeded synthetic N(0,1) data already resident in HBM when timing
+starts.
 
-Prints one JSON line with tokens/s, the roofline of the dominant kernel (the exact
-index-score stream) measured with HIP events, the HBM traffic of that kernel from the
-committed rocprofv3 counter summary (null when the kernel source has changed since),
-a prefill-chunk leg (4,096 queries against 131,072 causal entries, e4m3 index keys on
-MFMA), and the CPU oracle timed on a bounded sample of the same workload on this
-host's cores.
+Prints one JSON line with:
+  * tokens/s over exactly --steps timed steps (after --warmup), and the median, p10 and p90
+    of the per-step times (HIP events around every step);
+  * the roofline of the dominant kernel, the exact index-score stream, from its launches
+    inside the timed steps (HIP events that the library records around each Full/Reindex
+    layer's scoring on the same stream); its algorithmic bytes are the index keys plus the
+    index queries, and the score spill is reported beside them;
+  * the HBM traffic of that kernel from the committed rocprofv3 counter summary (null when
+    the kernel source has changed since);
+  * legs: the 4-layer batch-32 group, the long-context fp8 decode, the draft-block verify,
+    FP4 index keys, hierarchical search, the host tier, and the prefill chunk (4,096 queries
+    against 131,072 causal entries, e4m3 index keys on MFMA) with its index stage's MFMA
+    utilisation;
+  * the CPU oracle on a bounded sample of the headline workload: one host thread, and all
+    the host's threads.
 
-`--traffic-probe` runs only a 1 GiB device copy and five launches of the dominant
-kernel, for `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs.
+`--traffic-probe` runs only three 1 GiB device copies and two steps of the workload, for
+`rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs.
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
+import ctypes
 import hashlib
 import json
 import os
@@ -31,16 +44,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_exact_w2_hbm_traffic.md")
+HEADLINE = 5  # the 16-layer, batch-64 decode stack
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_exact_w5_hbm_traffic.md")
 SCORE_SOURCE = os.path.join(ROOT, "compressed_kv_cache_03_amd", "csrc", "score.hip")
 
 
-TRAFFIC_WORKLOAD = "decode_b32_n65536_group_F_Ri_Ru_Ru"  # the workload the summary's counters cover
-
-
 def measured_traffic():
-    """Bytes per launch of the dominant kernel from the committed counter summary, or None
-    when the summary is missing or was taken on another version of the kernel source."""
+    """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE, scaled by the copy
+    calibration) from the committed counter summary, or None when the summary is missing or was
+    taken on another version of the kernel source."""
     try:
         text = open(TRAFFIC_SUMMARY).read()
         src = hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()
@@ -66,21 +78,29 @@ def _dev(a, device):
     return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(device)
 
 
-def algorithmic_bytes(wl):
-    """Bytes the method must move per step: every layer reads its selection, the selected FP4
-    records, its window rows and query and writes its output; a selecting layer also streams every
-    index key, reads its index query, writes a score per entry and its selection; a Full layer
-    also packs and stores its new entry and index key.  Returns (total, bytes of one score launch)."""
-    B, N, D, K, k, W, Hq, Qs = wl.B, wl.N, wl.D, wl.H_I * wl.d_I, wl.k, wl.W, wl.Hq, wl.Qs
+def _key_bytes(wl):
+    """(bytes per stored index key, per index query row, per new key written by Full)."""
+    K = wl.H_I * wl.d_I
     if wl.idx_dtype == "fp4":
-        key_b, q_b, new_key_b = K // 2 + K // 32 * 4, K * 2, K * 4 + K // 2 + K // 32 * 4
-    else:
-        eb = 2 if wl.idx_dtype == "bf16" else 1
-        key_b, q_b, new_key_b = K * eb, K * eb, K * eb * 2
+        return K // 2 + K // 32 * 4, K * 2, K * 4 + K // 2 + K // 32 * 4
+    eb = 2 if wl.idx_dtype == "bf16" else 1
+    return K * eb, K * eb, K * eb * 2
+
+
+def algorithmic_bytes(wl):
+    """Bytes the method must move per step.  Every layer reads its selection, the selected FP4
+    records, its window rows and query and writes its output; a selecting layer also streams
+    every index key and reads its index query (the dominant kernel's bytes), and writes its
+    selection; a Full layer also packs and stores its new entry and index key.  The fp32
+    scores a selecting layer spills between its scan and its top-k are an intermediate,
+    counted separately."""
+    B, N, D, k, W, Hq, Qs = wl.B, wl.N, wl.D, wl.k, wl.W, wl.Hq, wl.Qs
+    key_b, q_b, new_key_b = _key_bytes(wl)
     per_layer_attend = B * Qs * (k * (D // 2 + D // 32 * 4) + 2 * (Qs + W - 1) * D * 2 // Qs
                                  + Hq * D * 2 + Hq * D * 4 + Hq * 4)
-    scan = B * (N * key_b + Qs * q_b + Qs * N * 4)  # keys + index query + score write
-    select = B * Qs * k * 4                         # selection written
+    scan = B * (N * key_b + Qs * q_b)  # index keys + index queries
+    spill = B * Qs * N * 4             # score write
+    select = B * Qs * k * 4            # selection written
     full_write = B * Qs * (D * 4 + D // 2 + D // 32 * 4 + new_key_b)
     total = 0
     for mode in wl.pattern * wl.groups:
@@ -89,10 +109,19 @@ def algorithmic_bytes(wl):
             total += scan + select
         if mode == "F":
             total += full_write
-    return total, scan
+    return {"step": total, "score_launch": scan, "score_spill": spill}
 
 
-def run_gpu(wl, steps, warmup, device, scan_loop=True):
+def _pct(xs, q):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def _summary(ms_list):
+    return {"median": round(_pct(ms_list, 50), 4), "p10": round(_pct(ms_list, 10), 4),
+            "p90": round(_pct(ms_list, 90), 4)}
+
+
+def setup_decode(wl, device):
     import torch
 
     import compressed_kv_cache_03_amd as csa2
@@ -100,7 +129,7 @@ def run_gpu(wl, steps, warmup, device, scan_loop=True):
 
     t0 = time.time()
     inp = make_inputs(wl)
-    B, N, D = wl.B, wl.N, wl.D
+    B, N = wl.B, wl.N
     groups = []
     for g in range(wl.groups):
         gc, gs = csa2.fp4_pack(_dev(inp.cache_x[g], device))
@@ -111,24 +140,49 @@ def run_gpu(wl, steps, warmup, device, scan_loop=True):
             keys, kscales = kc.reshape(B, N, wl.H_I, wl.d_I // 2), kscales.reshape(B, N, K // 32)
         groups.append(csa2.Group(gc, gs, keys, _dev(inp.n_valid, device), wl.idx_dtype, wl.k,
                                  sel_rows=B * wl.Qs, ikey_scales=kscales, pool_blocks=wl.pool_blocks))
+        torch.cuda.synchronize()
     layers = []
     for L in inp.layers:
         d = {k: (_dev(v, device) if isinstance(v, np.ndarray) else v) for k, v in L.items()}
-        d["out"] = torch.empty(B, wl.Qs, wl.Hq, D, dtype=torch.float32, device=device)
+        d["out"] = torch.empty(B, wl.Qs, wl.Hq, wl.D, dtype=torch.float32, device=device)
         d["lse"] = torch.empty(B, wl.Qs, wl.Hq, dtype=torch.float32, device=device)
         layers.append(d)
     for grp in groups:
         grp.workspace(wl.Qs, wl.Hq, wl.W)
     torch.cuda.synchronize()
-    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    print(f"# {wl.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    return inp, groups, layers
 
-    def step():
+
+def run_decode(wl, steps, warmup, device, state=None):
+    """Warm up, then time exactly `steps` decode steps.  Returns per-step times and the
+    durations of every index-score launch inside the timed steps."""
+    import torch
+
+    inp, groups, layers = state if state is not None else setup_decode(wl, device)
+    stream = torch.cuda.current_stream()
+    selecting = [li for li, d in enumerate(layers) if d["mode"] in ("F", "Ri")]
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)  # creates the event, so the library can record it by handle
+        return e
+
+    score_ev = [[(new_event(), new_event()) for _ in selecting] for _ in range(steps)]
+    step_ev = [new_event() for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+
+    def step(t=None):
+        j = 0
         for d in layers:
             grp = groups[d["group"]]
             kw = dict(q=d["q"], wk=d["wk"], wv=d["wv"], W=wl.W, sm_scale=wl.sm_scale,
                       out=d["out"], lse=d["lse"])
             if d["iq"] is not None:
                 kw["iq"] = d["iq"]
+                if t is not None:
+                    kw["index_events"] = score_ev[t][j]
+                    j += 1
             if d["new_entry"] is not None:
                 kw["new_entry"] = d["new_entry"]
                 kw["new_ikey"] = d["new_ikey"]
@@ -137,33 +191,31 @@ def run_gpu(wl, steps, warmup, device, scan_loop=True):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
+    step_ev[0].record(stream)
+    for t in range(steps):
+        step(t)
+        step_ev[t + 1].record(stream)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / steps
-    if not scan_loop:
-        return ms_step, None, inp, groups
+    per_step = [step_ev[t].elapsed_time(step_ev[t + 1]) for t in range(steps)]
+    total = step_ev[0].elapsed_time(step_ev[-1])
+    score_ms = [a.elapsed_time(b) for row in score_ev for a, b in row]
+    return {"ms_mean": total / steps, "per_step": per_step, "score_ms": score_ms,
+            "state": (inp, groups, layers)}
 
-    # dominant kernel: the exact index-score stream over one group's keys (same kernel the
-    # Full/Reindex layers launch), timed over its own loop on the same stream
-    first = next(d for d in layers if d["mode"] == "F")
-    grp = groups[first["group"]]
-    scores = torch.empty(B, wl.Qs, N, dtype=torch.float32, device=device)
-    reps = max(steps, 5)
-    for _ in range(2):
-        csa2.index_score(first["iq"], grp.ikeys, wl.idx_dtype, out=scores, ik_scales=grp.ikey_scales)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        csa2.index_score(first["iq"], grp.ikeys, wl.idx_dtype, out=scores, ik_scales=grp.ikey_scales)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_scan = e0.elapsed_time(e1) / reps
-    return ms_step, ms_scan, inp, groups
+
+def decode_leg(wl, steps, warmup, device, extra=None):
+    r = run_decode(wl, steps, warmup, device)
+    ab = algorithmic_bytes(wl)
+    res = {"workload": wl.name, "steps": steps, "ms_per_step": round(r["ms_mean"], 4),
+           "ms_per_step_pct": _summary(r["per_step"]),
+           "tokens_per_s": round(wl.B * wl.Qs / (r["ms_mean"] * 1e-3), 1),
+           "step_GBps": round(ab["step"] / (r["ms_mean"] * 1e-3) / 1e9, 1)}
+    if r["score_ms"]:
+        us = float(np.mean(r["score_ms"])) * 1e3
+        res["score_launch_us"] = round(us, 2)
+        res["score_GBps"] = round(ab["score_launch"] / (us * 1e-6) / 1e9, 1)
+    res.update(extra or {})
+    return res, r
 
 
 def host_tier(grp, reps=3):
@@ -186,8 +238,25 @@ def host_tier(grp, reps=3):
     ms_save, ms_restore = e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
     return {"image_bytes": n, "save_GBps": round(n / (ms_save * 1e-3) / 1e9, 1),
             "restore_GBps": round(n / (ms_restore * 1e-3) / 1e9, 1),
-            "note": "pinned host image of the workload's first sharing group (FP4 codes, scales, index "
-                    "keys, selection); device <-> host copies, restored bits checked by the GPU tests"}
+            "note": "pinned host image of the batch-32 group (FP4 codes, scales, index keys, "
+                    "selection); device <-> host copies, restored bits checked by the GPU tests"}
+
+
+def copy_bandwidth(device, reps=5):
+    """Device-to-device copy of 1 GiB: bytes read plus bytes written per second."""
+    import torch
+
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return round(2 * src.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
 
 
 def cache_accounting(wl):
@@ -213,32 +282,23 @@ def cache_accounting(wl):
 
 
 def traffic_probe(wl, device):
-    """A plain 1 GiB device copy (the counter calibration) and five launches of the
-    dominant kernel on one group of the workload, nothing else."""
+    """Three plain 1 GiB device copies (the counter calibration), then two decode steps of the
+    workload (every Full/Reindex layer launches the dominant kernel once), nothing else."""
     import torch
 
-    import compressed_kv_cache_03_amd as csa2
-    from synth.inputs import make_inputs
-
-    inp = make_inputs(wl)
     src = torch.ones(1 << 30, dtype=torch.uint8, device=device)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    first = next(L for L in inp.layers if L["mode"] == "F")
-    iq = _dev(first["iq"], device)
-    keys = _dev(inp.ikeys[first["group"]], device)
-    scores = torch.empty(wl.B, wl.Qs, wl.N, dtype=torch.float32, device=device)
-    for _ in range(5):
-        csa2.index_score(iq, keys, wl.idx_dtype, out=scores)
-    torch.cuda.synchronize()
-    print("traffic probe: 3 copies of 1073741824 B, 5 index-score launches", flush=True)
+    run_decode(wl, 2, 0, device)
+    print(f"traffic probe: 3 copies of 1073741824 B, 2 steps of {wl.name}", flush=True)
 
 
 def run_prefill(wl, steps, warmup, device):
-    """One Full layer over a prefill chunk; returns ms per chunk."""
+    """One Full layer over a prefill chunk; returns ms per chunk and the index stage's (threshold
+    sample GEMM through the MFMA filter GEMM) ms per chunk, both from HIP events."""
     import torch
 
     import compressed_kv_cache_03_amd as csa2
@@ -255,15 +315,25 @@ def run_prefill(wl, steps, warmup, device):
     grp.workspace(wl.Qs, wl.Hq, wl.W)
     for _ in range(warmup):
         grp.layer_step("F", **kw)
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        grp.layer_step("F", **kw)
-    e1.record(stream)
+    ev = []
+    for _ in range(steps + 1):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.append(e)
+    idx_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in idx_ev:
+        a.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    ev[0].record(stream)
+    for t in range(steps):
+        grp.layer_step("F", index_events=idx_ev[t], **kw)
+        ev[t + 1].record(stream)
+    torch.cuda.synchronize()
+    chunk = [ev[t].elapsed_time(ev[t + 1]) for t in range(steps)]
+    index = [a.elapsed_time(b) for a, b in idx_ev]
+    return chunk, index
 
 
 def prefill_index_flops(wl):
@@ -273,59 +343,100 @@ def prefill_index_flops(wl):
     return 2 * K * visible
 
 
-def cpu_baseline(wl, inp, target_seconds=12.0, max_reps=50):
-    """The oracle, as it stands, on a bounded sample of the same workload: whole decode steps
-    over (up to) 32 sequences, repeated until about target_seconds of host time have run."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host_threads():
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    return max(1, min(avail, int(omp))) if omp and omp.isdigit() else avail
+
+
+def cpu_baseline(wl, inp, one_seqs=2, all_seqs=16, target_seconds=8.0, max_reps=20):
+    """The oracle, as it stands, on a bounded sample of the workload: whole decode steps through
+    every layer, first for `one_seqs` sequences on one host thread, then for `all_seqs`
+    sequences on every host thread (OpenMP over query rows).  Cache packing is untimed setup
+    (spread over host threads; the oracle's own packing routine)."""
     import oracle
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    threads = max(1, min(threads, os.cpu_count() or 1))
-    bs = min(wl.B, 32)
+    gomp = ctypes.CDLL("libgomp.so.1")  # the OpenMP runtime the oracle is linked against
+    threads = _host_threads()
+    bs = min(wl.B, max(all_seqs, one_seqs))
     B, N, D = wl.B, wl.N, wl.D
     t0 = time.time()
-    groups = []
-    for g in range(wl.groups):
-        x = inp.cache_x[g][:bs]
-        oc, os_ = oracle.fp4_pack(x.reshape(bs * N, D))
-        groups.append(oracle.Group(oc.reshape(bs, N, D // 2), os_.reshape(bs, N, D // 32),
-                                   inp.ikeys[g][:bs].copy(), inp.n_valid[:bs].astype(np.int64),
-                                   wl.idx_dtype, wl.k, max_rows=bs * wl.Qs))
+
+    def pack(g, b):
+        return oracle.fp4_pack(inp.cache_x[g][b].reshape(N, D))
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        packed = {(g, b): ex.submit(pack, g, b) for g in range(wl.groups) for b in range(bs)}
+        packed = {key: f.result() for key, f in packed.items()}
     t_setup = time.time() - t0
-    reps = 0
-    t0 = time.time()
-    while True:
-        for L in inp.layers:
-            kw = dict(q=L["q"][:bs], wk=L["wk"][:bs], wv=L["wv"][:bs], W=wl.W,
-                      sm_scale=np.float32(wl.sm_scale))
-            if L["iq"] is not None:
-                kw["iq"] = L["iq"][:bs]
-            if L["new_entry"] is not None:
-                kw["new_entry"] = L["new_entry"][:bs]
-                kw["new_ikey"] = L["new_ikey"][:bs]
-            rc, _, _ = groups[L["group"]].layer_step(L["mode"], **kw)
-            assert rc == 0
-        reps += 1
-        if time.time() - t0 >= target_seconds or reps >= max_reps:
-            break
-    t_step = time.time() - t0
-    return {"value": round(reps * bs * wl.Qs / t_step, 4), "unit": "tokens/s",
-            "cores": min(threads, bs), "kind": "oracle",
-            "sample": f"{reps} decode step(s) of {bs} of {B} sequences through all "
-                      f"{len(inp.layers)} layers, {t_step:.1f}s on {min(threads, bs)} host threads "
-                      f"(OpenMP over sequences; cache packing untimed, {t_setup:.1f}s)"}
+
+    def make_groups(n):
+        groups = []
+        for g in range(wl.groups):
+            oc = np.stack([packed[(g, b)][0] for b in range(n)])
+            os_ = np.stack([packed[(g, b)][1] for b in range(n)])
+            groups.append(oracle.Group(oc, os_, inp.ikeys[g][:n].copy(), inp.n_valid[:n].astype(np.int64),
+                                       wl.idx_dtype, wl.k, max_rows=n * wl.Qs))
+        return groups
+
+    def timed(n, nthreads):
+        gomp.omp_set_num_threads(nthreads)
+        groups = make_groups(n)
+        reps = 0
+        t0 = time.time()
+        while True:
+            for L in inp.layers:
+                kw = dict(q=L["q"][:n], wk=L["wk"][:n], wv=L["wv"][:n], W=wl.W,
+                          sm_scale=np.float32(wl.sm_scale))
+                if L["iq"] is not None:
+                    kw["iq"] = L["iq"][:n]
+                if L["new_entry"] is not None:
+                    kw["new_entry"] = L["new_entry"][:n]
+                    kw["new_ikey"] = L["new_ikey"][:n]
+                rc, _, _ = groups[L["group"]].layer_step(L["mode"], **kw)
+                assert rc == 0
+            reps += 1
+            if time.time() - t0 >= target_seconds or reps >= max_reps:
+                break
+        return reps, time.time() - t0
+
+    r1, t1 = timed(min(one_seqs, bs), 1)
+    ra, ta = timed(bs, threads)
+    gomp.omp_set_num_threads(threads)
+    n1 = min(one_seqs, bs)
+    return {"value": round(ra * bs * wl.Qs / ta, 4), "unit": "tokens/s", "cores": min(threads, bs),
+            "kind": "oracle",
+            "single_thread_tokens_per_s": round(r1 * n1 * wl.Qs / t1, 4),
+            "single_thread_s": round(t1, 2), "all_core_s": round(ta, 2),
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "threads_available": threads,
+            "sample": f"{wl.name}: whole decode steps through all {len(inp.layers)} layers; "
+                      f"{r1} step(s) of {n1} of {B} sequences on 1 thread ({t1:.1f}s), then {ra} "
+                      f"step(s) of {bs} sequences on {min(threads, bs)} threads ({ta:.1f}s); cache "
+                      f"packing untimed ({t_setup:.1f}s)"}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 5])
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=HEADLINE, choices=[1, 2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-legs", action="store_true", help="headline workload only")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-verify", action="store_true")
-    ap.add_argument("--no-fp4-index", action="store_true")
-    ap.add_argument("--no-hier", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -344,18 +455,21 @@ def main():
     if args.traffic_probe:
         traffic_probe(wl, device)
         return
-    ms_step, ms_scan, inp, groups = run_gpu(wl, args.steps, args.warmup, device)
-    total_bytes, scan_bytes = algorithmic_bytes(wl)
-    achieved = scan_bytes / (ms_scan * 1e-3) / 1e9
-    tokens = wl.B * wl.Qs
+    r = run_decode(wl, args.steps, args.warmup, device)
+    inp = r["state"][0]
+    ab = algorithmic_bytes(wl)
+    ms = r["ms_mean"]
+    score_us = float(np.mean(r["score_ms"])) * 1e3
+    achieved = ab["score_launch"] / (score_us * 1e-6) / 1e9
     res = {
         "metric": "CSA2 decode tokens/s + achieved HBM GB/s (frac. of peak) at 1 MI355X",
-        "value": round(tokens / (ms_step * 1e-3), 2),
+        "value": round(wl.B * wl.Qs / (ms * 1e-3), 2),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(ms, 4),
+        "ms_per_step_pct": _summary(r["per_step"]),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -363,60 +477,57 @@ def main():
         "dtype_detail": "exact index scores accumulated in f64 from bf16/e4m3 keys; attention in "
                         "f32 over FP4 e2m1 entries and bf16 window rows",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.B, "entries": wl.N, "layers": list(wl.pattern) * wl.groups,
-                   "index": f"{wl.H_I}x{wl.d_I} {wl.idx_dtype}", "k": wl.k, "heads": wl.Hq,
-                   "head_dim": wl.D, "window": wl.W},
-        "step_hbm": {"algorithmic_bytes": total_bytes,
-                     "GBps": round(total_bytes / (ms_step * 1e-3) / 1e9, 1),
-                     "frac": round(total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "roofline": {"kernel": "score_exact_kernel (exact index-score stream)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "config": {"workload": wl.name, "batch": wl.B, "entries": wl.N,
+                   "layers": list(wl.pattern) * wl.groups, "index": f"{wl.H_I}x{wl.d_I} {wl.idx_dtype}",
+                   "k": wl.k, "heads": wl.Hq, "head_dim": wl.D, "window": wl.W},
+        "step_hbm": {"algorithmic_bytes": ab["step"],
+                     "GBps": round(ab["step"] / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(ab["step"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "roofline": {"kernel": "score_exact_kernel (exact index-score stream, inside the timed steps)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic() if wl.name == TRAFFIC_WORKLOAD else None,
-                     "bytes_per_launch": scan_bytes, "avg_launch_us": round(ms_scan * 1e3, 2)},
+                     "traffic": measured_traffic() if wl.wid == HEADLINE else None,
+                     "bytes_per_launch": ab["score_launch"], "score_spill_bytes_per_launch": ab["score_spill"],
+                     "launches": len(r["score_ms"]), "avg_launch_us": round(score_us, 2),
+                     "launch_us_pct": _summary([x * 1e3 for x in r["score_ms"]])},
+        "hbm_copy_GBps": copy_bandwidth(device),
+        "cache": cache_accounting(wl),
     }
-    res["cache"] = cache_accounting(wl)
-    res["host_tier"] = host_tier(groups[0])
-    del groups
-    if not args.no_verify:
-        vw = ALL[6]
-        ms_v, _, _, _ = run_gpu(vw, max(args.steps // 2, 3), 2, device, scan_loop=False)
-        res["verify5"] = {
-            "workload": vw.name, "ms_per_step": round(ms_v, 4),
-            "tokens_per_s": round(vw.B * vw.Qs / (ms_v * 1e-3), 1),
-            "note": "draft block of 5 queries per sequence through the same 4-layer group; tokens/s "
-                    "counts the 5 verified positions of each of the 32 sequences per step"}
-    if not args.no_fp4_index:
-        fw = ALL[7]
-        ms_f, ms_fscan, _, _ = run_gpu(fw, max(args.steps // 2, 3), 2, device)
-        _, f_scan_bytes = algorithmic_bytes(fw)
-        res["fp4_index"] = {
-            "workload": fw.name, "ms_per_step": round(ms_f, 4),
-            "tokens_per_s": round(fw.B * fw.Qs / (ms_f * 1e-3), 1),
-            "score_us": round(ms_fscan * 1e3, 2),
-            "score_GBps": round(f_scan_bytes / (ms_fscan * 1e-3) / 1e9, 1),
-            "note": "the w2 step with FP4 e2m1 index keys (fp32 block-32 scales, bf16 index queries); "
-                    "scores still exact"}
-    if not args.no_hier:
-        hw = ALL[8]
-        ms_h, _, _, _ = run_gpu(hw, max(args.steps // 2, 3), 2, device, scan_loop=False)
-        res["hierarchical"] = {
-            "workload": hw.name, "ms_per_step": round(ms_h, 4),
-            "tokens_per_s": round(hw.B * hw.Qs / (ms_h * 1e-3), 1),
-            "pool": f"{hw.pool_blocks} blocks x 8 = {hw.pool_blocks * 8} candidates per row",
-            "note": "the w2 step with hierarchical search: Full scores all entries and keeps the pool, "
-                    "Reindex scores and ranks only the pool's entries"}
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_legs:
+        legs = {}
+        for wid, extra in ((2, None), (3, None),
+                           (6, {"note": "draft block of 5 queries per sequence; tokens/s counts the 5 "
+                                        "verified positions of each sequence"}),
+                           (7, {"note": "FP4 e2m1 index keys (fp32 block-32 scales, bf16 index queries); "
+                                        "scores still exact"}),
+                           (8, {"pool": "2048 blocks x 8 = 16384 candidates per row",
+                                "note": "Full scores all entries and keeps the pool; Reindex scores and "
+                                        "ranks only the pool's entries"})):
+            lw = ALL[wid]
+            leg, lr = decode_leg(lw, max(args.steps // 2, 10), 3, device, extra)
+            if wid == 2:
+                res["host_tier"] = host_tier(lr["state"][1][0])
+            legs[lw.name] = leg
+            del lr
+            torch.cuda.empty_cache()
+        res["legs"] = legs
     if not args.no_prefill:
         pw = ALL[4]
-        ms_chunk = run_prefill(pw, 5, 2, device)
+        chunk, index = run_prefill(pw, 10, 2, device)
         flops = prefill_index_flops(pw)
+        idx_ms = float(np.mean(index))
         res["prefill"] = {
-            "workload": pw.name, "ms_per_chunk": round(ms_chunk, 4),
-            "tokens_per_s": round(pw.Qs / (ms_chunk * 1e-3), 1),
+            "workload": pw.name, "ms_per_chunk": round(float(np.mean(chunk)), 4),
+            "ms_per_chunk_pct": _summary(chunk),
+            "tokens_per_s": round(pw.Qs / (float(np.mean(chunk)) * 1e-3), 1),
             "index_flops": flops,
-            "index_tflops_over_whole_chunk": round(flops / (ms_chunk * 1e-3) / 1e12, 1),
-            "note": "whole Full layer (sampled threshold, MFMA score filter, exact band selection, "
-                    "attention); per-kernel MFMA figures are in profiles/"}
+            "index_stage_us": round(idx_ms * 1e3, 2),
+            "index_stage_mfma_util": round(flops / (idx_ms * 1e-3) / (FP8_PEAK_TFLOPS * 1e12), 4),
+            "note": "index stage = sampled-threshold GEMM, key norms, threshold selection and the "
+                    "MFMA filter GEMM (HIP events around them inside the chunk); mfma_util = useful "
+                    "index flops / (index stage time x 5.0 PFLOP/s fp8)"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(res), flush=True)

@@ -37,7 +37,7 @@ STATIC_SCRATCH_BYTES = 128 << 20  # scratch of csa2_layer_step_noalloc, per GPU
 class CLayerArgs(ctypes.Structure):
     _fields_ = [("Qs", i32), ("Hq", i32), ("q", vp), ("iq", vp), ("wk", vp), ("wv", vp),
                 ("W", i32), ("wlen", vp), ("new_entry", vp), ("new_ikey", vp),
-                ("sm_scale", f32), ("out", vp), ("lse", vp)]
+                ("sm_scale", f32), ("out", vp), ("lse", vp), ("index_events", vp * 2)]
 
 
 class Csa2Error(RuntimeError):
@@ -163,6 +163,16 @@ def index_score(iq: torch.Tensor, ik: torch.Tensor, dtype: str, out: torch.Tenso
     return out
 
 
+def _events(pair):
+    """Raw hipEvent_t handles of a pair of created torch.cuda.Event, or (None, None)."""
+    if pair is None:
+        return (vp * 2)(None, None)
+    handles = [int(e.cuda_event) for e in pair]
+    if not all(handles):
+        raise ValueError("index_events must be created (record them once) before use")
+    return (vp * 2)(*handles)
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -256,8 +266,10 @@ class Group:
         return self._ws
 
     def layer_step(self, mode: str, q, wk, wv, W: int, sm_scale: float, iq=None, new_entry=None,
-                   new_ikey=None, wlen=None, out=None, lse=None, ws=None, stream=None):
-        """One CSA2 layer in mode 'F' (Full), 'Ri' (Reindex) or 'Ru' (Reuse); returns (out, lse)."""
+                   new_ikey=None, wlen=None, out=None, lse=None, ws=None, stream=None, index_events=None):
+        """One CSA2 layer in mode 'F' (Full), 'Ri' (Reindex) or 'Ru' (Reuse); returns (out, lse).
+        index_events: optional pair of created torch.cuda.Event (enable_timing) that the library
+        records around the layer's index-scoring kernels."""
         B, Qs, Hq, D = q.shape
         if out is None:
             out = torch.empty(B, Qs, Hq, D, dtype=torch.float32, device=q.device)
@@ -266,7 +278,8 @@ class Group:
         if ws is None:
             ws = self.workspace(Qs, Hq, W)
         a = CLayerArgs(Qs, Hq, q.data_ptr(), _ptr(iq), _ptr(wk), _ptr(wv), W, _ptr(wlen),
-                       _ptr(new_entry), _ptr(new_ikey), float(sm_scale), out.data_ptr(), _ptr(lse))
+                       _ptr(new_entry), _ptr(new_ikey), float(sm_scale), out.data_ptr(), _ptr(lse),
+                       _events(index_events))
         st = _load().csa2_layer_step(MODE[mode], ctypes.byref(a), ctypes.byref(self.c), ws.data_ptr(),
                                      ws.numel(), _stream(stream))
         _check(st, f"csa2_layer_step({mode})")

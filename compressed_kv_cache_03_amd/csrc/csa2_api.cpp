@@ -158,6 +158,11 @@ T* at(void* ws, size_t off) {
 
 csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 
+// Records a caller's timing event on the stream (no event: nothing).
+hipError_t mark(void* event, hipStream_t s) {
+    return event ? hipEventRecord(static_cast<hipEvent_t>(event), s) : hipSuccess;
+}
+
 bool valid_dim(int32_t D) { return D >= 32 && D <= 256 && D % 32 == 0; }
 
 bool valid_index_width(csa2_idx_dtype dt, int32_t H, int32_t d) {
@@ -568,7 +573,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         ba.flag_count = at<uint32_t>(ws, L.flag_count);
         ba.scores = at<float>(ws, L.scores);
         ba.ld = g->N_cap;
-        e = launch_gemm_fp8(ga, 0, s);
+        e = mark(a->index_events[0], s);
+        if (e == hipSuccess) e = launch_gemm_fp8(ga, 0, s);
         if (e == hipSuccess) e = launch_key_norm(ga.ik, K, g->B, N, g->N_cap, ba.nblk, ba.knorm, s);
         if (e == hipSuccess) e = launch_sample_select(ba, s);
         if (e == hipSuccess) {
@@ -584,6 +590,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
             fa.cap = ba.cap;
             e = launch_gemm_fp8(fa, 1, s);
         }
+        if (e == hipSuccess) e = mark(a->index_events[1], s);
         if (e == hipSuccess) e = launch_band_final(ba, s);
     } else if (e == hipSuccess && selects) {
         // S2 + S3: exact scores of the valid entries (or, for Reindex in a
@@ -637,7 +644,9 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         }
         t.slices = (int)((t.N + t.slice_len - 1) / t.slice_len);
         if (e == hipSuccess && mode != CSA2_MODE_FULL) e = launch_zero(t.hist, R * kHistBinsHost + 1, s);
+        if (e == hipSuccess) e = mark(a->index_events[0], s);
         if (e == hipSuccess) e = launch_score_exact(sa, s);
+        if (e == hipSuccess) e = mark(a->index_events[1], s);
         if (e == hipSuccess) e = launch_topk_select(t, s);
         // the selection holds pool slots: turn them into entries
         if (e == hipSuccess && in_pool) e = launch_pool_map(g->sel, R, g->k, g->pool, g->pool_blocks, s);

@@ -134,6 +134,12 @@ typedef struct csa2_layer_args {
     float sm_scale;        /* softmax scale, e.g. 1/sqrt(D)                           */
     float* out;            /* fp32 [B][Qs][Hq][D]                                     */
     float* lse;            /* fp32 [B][Qs][Hq] natural-log sum-exp, or NULL           */
+    void* index_events[2]; /* optional hipEvent_t pair for timing (NULL = none): a Full
+                              or Reindex layer records [0] on the stream right before its
+                              first index-scoring kernel (S2; for a prefill chunk on the
+                              MFMA path, the threshold-sample GEMM) and [1] right after
+                              its last (the score stream, or the filter GEMM); Reuse
+                              records neither                                         */
 } csa2_layer_args;
 
 /* Human-readable name of a status code (static storage). */

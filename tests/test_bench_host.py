@@ -24,16 +24,25 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def test_decode_step_bytes_w2():
     B, N, K, k, D, W, Hq = 32, 65536, 256, 2048, 128, 128, 16
-    total, scan = bench.algorithmic_bytes(W2)
-    # one scoring launch: bf16 keys of every entry, the index query, an fp32 score per entry
-    assert scan == B * (N * K * 2 + K * 2 + N * 4)
-    assert scan == 1_082_146_816
+    ab = bench.algorithmic_bytes(W2)
+    # one scoring launch: bf16 keys of every entry and the index query; the fp32 score per
+    # entry is an intermediate, reported beside it
+    assert ab["score_launch"] == B * (N * K * 2 + K * 2) == 1_073_758_208
+    assert ab["score_spill"] == B * N * 4
     # the four layers add their attention reads/writes, two selections and Full's new row on top
     record = D // 2 + D // 32 * 4
     attend = B * (k * record + 2 * W * D * 2 + Hq * D * 2 + Hq * D * 4 + Hq * 4)
     select = B * k * 4
     full = B * (D * 4 + record + K * 2 * 2)
-    assert total == 2 * scan + 4 * (attend + select) + 2 * select + full
+    assert ab["step"] == 2 * ab["score_launch"] + 4 * (attend + select) + 2 * select + full
+
+
+def test_decode_step_bytes_w5_headline():
+    B, N, K = 64, 131072, 256
+    ab = bench.algorithmic_bytes(W5)
+    assert ab["score_launch"] == B * (N * K * 2 + K * 2)
+    # 8 selecting layers of the 16 stream every key once each: 99 % of the step's bytes
+    assert 0.99 < 8 * ab["score_launch"] / ab["step"] < 1.0
 
 
 @pytest.mark.parametrize("wl,shared_fp4,shared_keys,ratio", [
