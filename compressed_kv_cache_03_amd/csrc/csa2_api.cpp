@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <mutex>
 
 #include "launch.h"
@@ -165,6 +166,25 @@ hipError_t mark(void* event, hipStream_t s) {
 
 bool valid_dim(int32_t D) { return D >= 32 && D <= 256 && D % 32 == 0; }
 
+// A C caller may pass any integer where the header declares an enum; reading
+// such a value through the enum type is undefined in C++, so the bits are read
+// as an integer and checked before the enum is used.
+template <typename E>
+int32_t enum_bits(const E& e) {
+    static_assert(sizeof(E) == sizeof(int32_t), "enums of the ABI are int-sized");
+    int32_t v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+bool valid_mode(const csa2_mode& m) {
+    const int32_t v = enum_bits(m);
+    return v == CSA2_MODE_FULL || v == CSA2_MODE_REINDEX || v == CSA2_MODE_REUSE;
+}
+bool valid_dtype(const csa2_idx_dtype& d) {
+    const int32_t v = enum_bits(d);
+    return v == CSA2_IDX_BF16 || v == CSA2_IDX_FP8_E4M3 || v == CSA2_IDX_FP4_E2M1;
+}
+
 bool valid_index_width(csa2_idx_dtype dt, int32_t H, int32_t d) {
     if (H < 1 || d < 1) return false;
     const int64_t K = (int64_t)H * d;
@@ -185,7 +205,7 @@ struct ImageParts {
 };
 
 bool image_parts(const csa2_group* g, ImageParts* p) {
-    if (!g || g->B < 1 || g->N_cap < 1 || !valid_dim(g->D) || g->k < 1 ||
+    if (!g || !valid_dtype(g->idx_dtype) || g->B < 1 || g->N_cap < 1 || !valid_dim(g->D) || g->k < 1 ||
         !valid_index_width(g->idx_dtype, g->H_I, g->d_I) || g->n_valid_max < 0 || g->n_valid_max > g->N_cap)
         return false;
     if (g->has_selection && (g->sel_qs < 1 || (int64_t)g->B * g->sel_qs > g->sel_rows)) return false;
@@ -215,10 +235,9 @@ hipError_t copy_rows(void* dst, size_t dpitch, const void* src, size_t spitch, s
 
 // Every check of csa2_layer_step except the workspace: arguments, group
 // geometry and state, and the launch sizes.  Touches no device.
-csa2_status check_layer(csa2_mode mode, const csa2_layer_args* a, const csa2_group* g) {
+csa2_status check_layer(const csa2_mode& mode, const csa2_layer_args* a, const csa2_group* g) {
     if (!a || !g) return CSA2_ERR_INVALID_ARG;
-    if (mode != CSA2_MODE_FULL && mode != CSA2_MODE_REINDEX && mode != CSA2_MODE_REUSE)
-        return CSA2_ERR_INVALID_ARG;
+    if (!valid_mode(mode) || !valid_dtype(g->idx_dtype)) return CSA2_ERR_INVALID_ARG;
     // group geometry
     if (g->B < 1 || g->N_cap < 1 || !valid_dim(g->D) || g->k < 1 || g->k > g->N_cap ||
         !valid_index_width(g->idx_dtype, g->H_I, g->d_I))
@@ -363,7 +382,7 @@ csa2_status csa2_index_score(const void* iq, const void* ik, const float* ik_sca
                              void* stream) {
     (void)exact;  // every score is exact (see the header)
     if (B < 0 || Qs < 1 || N < 0 || causal_offset < -1) return CSA2_ERR_INVALID_ARG;
-    if (!valid_index_width(dtype, H, d)) return CSA2_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype) || !valid_index_width(dtype, H, d)) return CSA2_ERR_INVALID_ARG;
     if (N >= (int64_t)1 << 31) return CSA2_ERR_UNSUPPORTED;
     if (B == 0 || N == 0) return CSA2_OK;
     if (!iq || !ik || !scores || (dtype == CSA2_IDX_FP4_E2M1 && !ik_scales)) return CSA2_ERR_INVALID_ARG;
@@ -486,7 +505,7 @@ csa2_status csa2_sparse_attend(const void* q, int32_t B, int32_t Qs, int32_t Hq,
 }
 
 size_t csa2_layer_workspace_bytes(const csa2_group* g, int32_t Qs, int32_t Hq, int32_t W) {
-    if (!g || g->B <= 0 || g->N_cap <= 0 || Qs <= 0 || Hq <= 0 || W < 0 || !valid_dim(g->D))
+    if (!g || !valid_dtype(g->idx_dtype) || g->B <= 0 || g->N_cap <= 0 || Qs <= 0 || Hq <= 0 || W < 0 || !valid_dim(g->D))
         return 0;
     return layer_layout(g, Qs, Hq, W).total;
 }

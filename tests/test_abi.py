@@ -208,3 +208,15 @@ def test_layer_step_noalloc_validation():
     assert L.csa2_layer_workspace_bytes(ctypes.byref(g), 5, 16, 128) > csa2.STATIC_SCRATCH_BYTES
     assert ab(g, _args(Qs=5)) == csa2.ERR_WORKSPACE
     assert L.csa2_layer_workspace_bytes(ctypes.byref(g), 1, 16, 128) <= csa2.STATIC_SCRATCH_BYTES
+
+
+def test_out_of_range_enums_are_rejected():
+    # a C caller can pass any integer where an enum is declared: rejected, nothing launched
+    L = csa2.lib()
+    assert L.csa2_index_score(FAKE, FAKE, None, 3, 1, 1, 10, 4, 64, -1, 1, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_score(FAKE, FAKE, None, -1, 1, 1, 10, 4, 64, -1, 1, FAKE, None) == csa2.ERR_INVALID_ARG
+    assert _step(7, _group(), _args()) == csa2.ERR_INVALID_ARG
+    assert _step(-1, _group(), _args()) == csa2.ERR_INVALID_ARG
+    assert _step(0, _group(idx_dtype=9), _args()) == csa2.ERR_INVALID_ARG
+    assert L.csa2_layer_workspace_bytes(ctypes.byref(_group(idx_dtype=9)), 1, 16, 128) == 0
+    assert L.csa2_group_image_bytes(ctypes.byref(_group(idx_dtype=-3))) == 0
