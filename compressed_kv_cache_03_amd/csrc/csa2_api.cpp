@@ -42,6 +42,8 @@ struct Layout {
     size_t scores = 0;                   // [R][N] f32
     size_t cand_idx = 0, cand_key = 0;   // [R][N]
     size_t slice_cnt = 0;                // [R][slices]
+    size_t bits = 0;                     // [R][ceil(N/32)] bitmap words of the split top-k
+    int64_t bits_ld = 0;
     // prefill selection on MFMA (e4m3 index keys, Qs > 1)
     size_t samp = 0, theta = 0, cand = 0, cand_cnt = 0, flag = 0, flag_count = 0, knorm = 0;
     size_t blk = 0, blkcnt = 0;
@@ -88,6 +90,9 @@ void add_topk(Layout& L, size_t& off, const TopkShape& t) {
     off = align_up(off + (size_t)t.R * t.N * 4);
     L.slice_cnt = off;
     off = align_up(off + (size_t)t.R * t.slices * 4);
+    L.bits_ld = (t.N + 31) / 32;
+    L.bits = off;
+    off = align_up(off + (size_t)t.R * L.bits_ld * 4);
 }
 
 size_t attend_part_bytes(int64_t R, int Hq, int D, int k, int W) {
@@ -451,6 +456,8 @@ csa2_status csa2_topk(const float* scores, int64_t R, int64_t N, int64_t ld, con
     t.slice_cnt = at<uint32_t>(ws, L.slice_cnt);
     t.slices = (int)slices;
     t.slice_len = topk_slice_len(Nn);
+    t.bits = at<uint32_t>(ws, L.bits);
+    t.bits_ld = L.bits_ld;
     hipError_t e = launch_zero(t.hist, (int64_t)R * kHistBinsHost, s);
     if (e == hipSuccess) e = launch_topk_hist(t, s);
     if (e == hipSuccess) e = launch_topk_select(t, s);
@@ -626,6 +633,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         t.cand_idx = at<int32_t>(ws, L.cand_idx);
         t.cand_key = at<uint32_t>(ws, L.cand_key);
         t.slice_cnt = at<uint32_t>(ws, L.slice_cnt);
+        t.bits = at<uint32_t>(ws, L.bits);
+        t.bits_ld = L.bits_ld;
         ScoreArgs sa{};
         sa.iq = a->iq;
         sa.ik = g->ikeys;

@@ -116,6 +116,8 @@ struct TopkArgs {
     uint32_t* slice_cnt;  // [R][slices]
     int slices;           // slices per row
     int64_t slice_len;
+    uint32_t* bits = nullptr;  // [R][bits_ld] bitmap words of the split path (null: no split path)
+    int64_t bits_ld = 0;       // words per row, >= ceil(N / 32)
 };
 int64_t topk_slice_len(int64_t N);
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t stream);

@@ -433,6 +433,241 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     }
 }
 
+// Split path for rows of up to kRowMaxN entries when rows are too few to keep
+// the chip busy with one workgroup each: the pass over the scores is spread
+// over many workgroups per row, and one workgroup per row finishes.
+//   topk_slice_kernel, one workgroup per (slice, row): b1 from the row
+//     histogram, then for its slice the bitmap words of the entries whose
+//     digit is above b1 (thread pairs own 32 consecutive entries, so each word
+//     is stored once) and, in index order, the (index, key) of the entries in
+//     bin b1, written to the slice's own segment of the candidate buffer;
+//   topk_merge_kernel, one workgroup per row: the candidates of all slices
+//     (one list in index order) to LDS, digits 2 and 3 to the exact keff-th
+//     key T, the bitmap to LDS, candidates above T (and the first `quota`
+//     equal to T, in index order) into it, then the ordered output.
+constexpr int kSplitThreads = 256;
+constexpr int kSplitSub = 16 * kSplitThreads;  // entries per pass: 16 per thread
+constexpr int kSplitMaxSlices = kRowMaxN / kSplitSub;
+constexpr int64_t kSplitMinN = 8192;          // shorter rows: the row kernel alone
+constexpr int kSplitTargetBlocks = 512;
+
+// Slice length of the split path: whole passes, about kSplitTargetBlocks
+// workgroups in all.
+int64_t split_len(int64_t R, int64_t N) {
+    const int64_t subs = (N + kSplitSub - 1) / kSplitSub;
+    int64_t per = R * subs / kSplitTargetBlocks;
+    if (per < 1) per = 1;
+    if (per > subs) per = subs;
+    return per * kSplitSub;
+}
+
+__global__ __launch_bounds__(kSplitThreads) void topk_slice_kernel(TopkArgs a, int64_t len) {
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
+    __shared__ uint32_t scan_lds[kSplitThreads / 64 + 1];
+    __shared__ uint32_t dig[2];
+    const int64_t r = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int64_t nv = topk_row_valid(a, r);
+    const int64_t keff = nv < a.k ? nv : a.k;
+    const int64_t j0 = (int64_t)blockIdx.x * len;
+    uint32_t* cnt = a.slice_cnt + r * a.slices + blockIdx.x;
+    if (j0 >= nv || keff == 0) {
+        if (tid == 0) *cnt = 0;
+        return;
+    }
+    const float* s = a.scores + r * a.ld;
+    const bool aligned16 = (reinterpret_cast<uintptr_t>(s) & 15) == 0;
+    const int64_t j_end = j0 + len < nv ? j0 + len : nv;
+    // thread t takes entries jt .. jt + 15 of each pass (jt a multiple of 16, of 32
+    // for even t); the first pass's scores are requested before the histogram so
+    // that the two latencies overlap
+    float x[16];
+    auto load = [&](int64_t jt) __attribute__((always_inline)) {
+        if (aligned16 && jt + 16 <= j_end) {
+            const float4* s4 = reinterpret_cast<const float4*>(s + jt);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float4 v = s4[c];
+                x[4 * c] = v.x;
+                x[4 * c + 1] = v.y;
+                x[4 * c + 2] = v.z;
+                x[4 * c + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) x[u] = jt + u < j_end ? s[jt + u] : 0.0f;
+        }
+    };
+    load(j0 + 16 * (int64_t)tid);
+    {
+        const uint4* h4 = reinterpret_cast<const uint4*>(a.hist + r * kHistBins);
+        uint4* l4 = reinterpret_cast<uint4*>(s_hist);
+#pragma unroll
+        for (int i = tid; i < kHistBins / 4; i += kSplitThreads) l4[i] = h4[i];
+    }
+    __syncthreads();
+    find_digit<kSplitThreads>(s_hist, kHistBins, (uint32_t)keff, scan_lds, dig);
+    const uint32_t b1 = dig[0];
+    int32_t* ci = a.cand_idx + r * a.N + j0;
+    uint32_t* ck = a.cand_key + r * a.N + j0;
+    uint32_t* bits = a.bits + r * a.bits_ld;
+    uint32_t written = 0;
+    for (int64_t js = j0; js < j_end; js += kSplitSub) {
+        const int64_t jt = js + 16 * (int64_t)tid;
+        if (js > j0) load(jt);
+        uint32_t keys[16];
+        uint32_t above = 0, eq = 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            keys[u] = sort_key(x[u]);
+            const bool ok = jt + u < j_end;
+            const uint32_t d = keys[u] >> (32 - kHistBits);
+            above |= (uint32_t)(ok && d > b1) << u;
+            eq |= (uint32_t)(ok && d == b1) << u;
+        }
+        uint32_t word = above << (16 * (tid & 1));
+        word |= (uint32_t)__builtin_amdgcn_ds_swizzle((int)word, (1 << 10) | 0x1f);
+        if ((tid & 1) == 0 && jt < j_end) bits[jt >> 5] = word;
+        uint32_t total;
+        uint32_t off = written + block_exclusive_scan((uint32_t)__popc(eq), scan_lds, &total);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if ((eq >> u) & 1u) {
+                ci[off] = (int32_t)(jt + u);
+                ck[off] = keys[u];
+                ++off;
+            }
+        }
+        written += total;
+    }
+    if (tid == 0) *cnt = written;
+}
+
+__global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(TopkArgs a, int64_t len) {
+    __shared__ uint32_t s_hist[kHistBins];
+    __shared__ uint32_t s_ckey[kRowCand];
+    __shared__ int32_t s_cidx[kRowCand];
+    __shared__ uint32_t s_bits[kRowMaxN / 32];
+    __shared__ uint32_t s_off[kSplitMaxSlices + 1];
+    __shared__ uint32_t scan_lds[kRowThreads / 64 + 1];
+    __shared__ uint32_t dig[2];
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t nv = topk_row_valid(a, r);
+    const int64_t keff = nv < a.k ? nv : a.k;
+    int32_t* out = a.idx + r * a.k;
+    for (int64_t t = keff + tid; t < a.k; t += kRowThreads) out[t] = -1;
+    if (keff == 0) return;
+    const int nwords = (int)((nv + 31) / 32);
+    const int nslices = (int)((nv + len - 1) / len);
+
+    // 1. the histogram, the slice counts and the bitmap are requested together;
+    //    then b1, the count above it and the slices' candidate offsets
+    const uint32_t c = tid < nslices ? a.slice_cnt[r * a.slices + tid] : 0u;
+    for (int i = tid; i < kHistBins; i += kRowThreads) s_hist[i] = a.hist[r * kHistBins + i];
+    for (int w = tid; w < nwords; w += kRowThreads) s_bits[w] = a.bits[r * a.bits_ld + w];
+    __syncthreads();
+    find_digit<kRowThreads>(s_hist, kHistBins, (uint32_t)keff, scan_lds, dig);
+    const uint32_t b1 = dig[0];
+    const uint32_t need2 = (uint32_t)keff - dig[1];
+    {
+        uint32_t total;
+        const uint32_t run = block_exclusive_scan(c, scan_lds, &total);
+        if (tid < nslices) s_off[tid] = run;
+        if (tid == 0) s_off[nslices] = total;
+    }
+    __syncthreads();
+    const uint32_t C = s_off[nslices];
+    const bool in_lds = C <= (uint32_t)kRowCand;
+    const int32_t* ci = a.cand_idx + r * a.N;
+    const uint32_t* ck = a.cand_key + r * a.N;
+    // global position of flat candidate p (slice order = index order)
+    auto gpos = [&](uint32_t p) -> int64_t {
+        int lo = 0, hi = nslices;  // s_off[lo] <= p < s_off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_off[mid] <= p) lo = mid; else hi = mid;
+        }
+        return (int64_t)lo * len + (p - s_off[lo]);
+    };
+    if (in_lds) {
+        for (uint32_t p = tid; p < C; p += kRowThreads) {
+            const int64_t gp = gpos(p);
+            s_ckey[p] = ck[gp];
+            s_cidx[p] = ci[gp];
+        }
+    }
+    auto key_at = [&](uint32_t p) -> uint32_t { return in_lds ? s_ckey[p] : ck[gpos(p)]; };
+    auto idx_at = [&](uint32_t p) -> int32_t { return in_lds ? s_cidx[p] : ci[gpos(p)]; };
+    __syncthreads();
+
+    // 2. digits 2 (bits 19..8) and 3 (bits 7..0) among the candidates (all in bin b1)
+    uint32_t prefix = b1 << (32 - kHistBits), need = need2;
+    for (int i = tid; i < kHistBins; i += kRowThreads) s_hist[i] = 0;
+    __syncthreads();
+    for (uint32_t p = tid; p < C; p += kRowThreads) atomicAdd(&s_hist[(key_at(p) >> 8) & 0xfffu], 1u);
+    __syncthreads();
+    find_digit<kRowThreads>(s_hist, kHistBins, need, scan_lds, dig);
+    prefix |= dig[0] << 8;
+    need -= dig[1];
+    __syncthreads();
+    for (int i = tid; i < 256; i += kRowThreads) s_hist[i] = 0;
+    __syncthreads();
+    for (uint32_t p = tid; p < C; p += kRowThreads) {
+        const uint32_t key = key_at(p);
+        if ((key & 0xffffff00u) == prefix) atomicAdd(&s_hist[key & 0xffu], 1u);
+    }
+    __syncthreads();
+    find_digit<kRowThreads>(s_hist, 256, need, scan_lds, dig);
+    prefix |= dig[0];
+    need -= dig[1];
+    const uint32_t T = prefix, quota = need;  // take every key > T and `quota` keys == T
+    const uint32_t ties = s_hist[T & 0xffu];
+    __syncthreads();
+
+    // 3. candidates above T, and the first `quota` equal to T in index order
+    if (quota == ties) {
+        for (uint32_t p = tid; p < C; p += kRowThreads) {
+            const uint32_t key = key_at(p);
+            if (key >= T) {
+                const int32_t j = idx_at(p);
+                atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+            }
+        }
+    } else {
+        uint32_t before = 0;
+        for (uint32_t p0 = 0; p0 < C; p0 += kRowThreads) {
+            const uint32_t p = p0 + tid;
+            const uint32_t key = p < C ? key_at(p) : 0u;
+            const uint32_t tie = (p < C && key == T) ? 1u : 0u;
+            uint32_t n;
+            const uint32_t rank = before + block_exclusive_scan(tie, scan_lds, &n);
+            if (p < C && (key > T || (tie && rank < quota))) {
+                const int32_t j = idx_at(p);
+                atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+            }
+            before += n;
+        }
+    }
+    __syncthreads();
+
+    // 4. ascending output
+    const int per = (nwords + kRowThreads - 1) / kRowThreads;
+    uint32_t mine = 0;
+    for (int wi = tid * per; wi < min(nwords, (tid + 1) * per); ++wi) mine += __popc(s_bits[wi]);
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan(mine, scan_lds, &total);
+    for (int wi = tid * per; wi < min(nwords, (tid + 1) * per); ++wi) {
+        uint32_t word = s_bits[wi];
+        while (word) {
+            const int bit = __ffs(word) - 1;
+            word &= word - 1;
+            if (pos < (uint32_t)keff) out[pos] = wi * 32 + bit;
+            ++pos;
+        }
+    }
+}
+
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t stream) {
     if (a.R == 0 || a.N == 0) return hipSuccess;
     dim3 grid((unsigned)a.slices, (unsigned)a.R);
@@ -446,6 +681,15 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t stream) {
     // fill the chip: its single pass reads the row on one CU (about 23 GB/s,
     // 11 us at 2^16 entries).  Fewer, longer rows are compacted slice by slice
     // across the chip and then resolved per row.
+    // Few rows of moderate length: the pass is spread over many workgroups per
+    // row (split path), then one workgroup per row finishes.
+    if (a.N <= kRowMaxN && a.N > kSplitMinN && a.R < kRowFill && a.bits) {
+        const int64_t len = split_len(a.R, a.N);
+        const dim3 grid((unsigned)((a.N + len - 1) / len), (unsigned)a.R);
+        hipLaunchKernelGGL(topk_slice_kernel, grid, dim3(kSplitThreads), 0, stream, a, len);
+        hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)a.R), dim3(kRowThreads), 0, stream, a, len);
+        return hipGetLastError();
+    }
     if (a.N <= kRowMaxN && (a.N <= kRowPassN || a.R >= kRowFill)) {
         hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)a.R), dim3(kRowThreads), 0, stream, a);
         return hipGetLastError();
