@@ -53,11 +53,11 @@ static_assert(kFThreads == kFRows, "one thread per query row of the workgroup");
 static_assert(kFBlkCols / 16 <= 256 && kFQG * 64 <= 256, "tags fit 8 bits");
 constexpr int kBandThreads = 1024;
 constexpr int kBandCap = 8192;     // candidates the final kernel holds in LDS
-constexpr int kBandMaxValid = 1 << 18;  // rows up to this many entries (LDS bitmap)
+constexpr int kBandOutChunk = 1 << 18;  // entries per pass of the output bitmap (over s_key)
+constexpr int kBandRegBatch = 512;      // column-block regions gathered per batch
 constexpr int kBandList = 1024;    // band entries resolved in LDS
 constexpr int kBandBits = 11;      // radix digit of the final selection
 constexpr int kBandHist = 1 << kBandBits;
-constexpr int kBandMaxBlk = kBandMaxValid / kFBlkCols;
 
 CSA2_DEV f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
     // e4m3 x e4m3 with E8M0 scales 127 = 2^0
@@ -617,12 +617,12 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
     __shared__ uint32_t bkey[kBandList];   // exact sort keys of the band (also the bin gather)
     __shared__ uint32_t scan_lds[kBandThreads / 64 + 1];
     __shared__ uint32_t dig[2];
-    __shared__ uint32_t s_off[kBandMaxBlk];  // first candidate of each column-block region
-    __shared__ uint32_t s_cnt[kBandMaxBlk];  // and its count
+    __shared__ uint32_t s_oc[kBandRegBatch];  // per region of a batch: first candidate | count << 16
     __shared__ uint32_t red_u[kBandThreads / 64];
     __shared__ double red_q[kBandThreads / 64];
     __shared__ float red_k[kBandThreads / 64];
-    static_assert(kBandCap * 4 >= kBandMaxValid / 8, "the output bitmap overlays s_key");
+    static_assert(kBandCap * 4 >= kBandOutChunk / 8, "the output bitmap overlays s_key");
+    static_assert(kBandCap < (1 << 16) && kFBlkCap < (1 << 16), "offset and count share a word");
 
     const int64_t r = blockIdx.x;
     const int b = (int)(r / a.Qs);
@@ -643,9 +643,10 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
     // every independent load first: overflow count, region counts, ||q||^2
     // (exact in fp64) and the sequence's bound on max ||k||^2
     const int64_t R = (int64_t)a.B * a.Qs;
-    const int nreg = (int)((min(nv, (int64_t)kBandMaxValid) + kFBlkCols - 1) / kFBlkCols);
+    const int nreg = (int)((nv + kFBlkCols - 1) / kFBlkCols);
     const uint32_t novf = a.cand_cnt[r];
-    const uint32_t mine_c = threadIdx.x < nreg ? min(a.blkcnt[threadIdx.x * R + r], (uint32_t)kFBlkCap) : 0u;
+    uint32_t mine_c = 0;
+    for (int i = threadIdx.x; i < nreg; i += kBandThreads) mine_c += min(a.blkcnt[(int64_t)i * R + r], (uint32_t)kFBlkCap);
     double q2 = 0.0;
     {
         const uint8_t* q = a.iq + r * RB;
@@ -656,25 +657,22 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
     }
     float k2 = 0.0f;
     for (int i = threadIdx.x; i < a.nblk; i += kBandThreads) k2 = fmaxf(k2, a.knorm[(int64_t)b * a.nblk + i]);
-    if (nv > kBandMaxValid || novf > (uint32_t)a.cap) {
+    if (novf > (uint32_t)a.cap) {
         flag_row();
         return;
     }
     // the candidates: the row's column-block regions in order, then its overflow list
     uint32_t nblkc;
-    const uint32_t my_off = block_exclusive_scan(mine_c, scan_lds, &nblkc);
+    block_exclusive_scan(mine_c, scan_lds, &nblkc);
     const uint32_t C = nblkc + novf;
     if (C < (uint32_t)keff || C > (uint32_t)kBandCap) {
         flag_row();
         return;
     }
-    if (threadIdx.x < nreg) {
-        s_off[threadIdx.x] = my_off;
-        s_cnt[threadIdx.x] = mine_c;
-    }
-    __syncthreads();
-    // keys relative to the smallest candidate key: they span few bits.  One
-    // wave per region (at most kFBlkCap = 64 entries), so the loads are independent.
+    // keys relative to the smallest candidate key: they span few bits.  Regions
+    // are taken kBandRegBatch at a time (offsets from a block scan of their
+    // counts); one wave per region (at most kFBlkCap = 64 entries), so the loads
+    // are independent.
     static_assert(kFBlkCap <= 64, "one lane per region entry");
     uint32_t kmin = 0xffffffffu, kmax = 0;
     const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
@@ -685,9 +683,22 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
         kmin = min(kmin, k);
         kmax = max(kmax, k);
     };
+    uint32_t base = 0;
+    for (int i0 = 0; i0 < nreg; i0 += kBandRegBatch) {
+        const int nb = min(kBandRegBatch, nreg - i0);
+        const uint32_t c = threadIdx.x < nb ? min(a.blkcnt[(int64_t)(i0 + threadIdx.x) * R + r], (uint32_t)kFBlkCap) : 0u;
+        uint32_t tot;
+        const uint32_t ex = base + block_exclusive_scan(c, scan_lds, &tot);
+        if (threadIdx.x < nb) s_oc[threadIdx.x] = ex | (c << 16);
+        __syncthreads();
 #pragma unroll 4
-    for (int i = wv; i < nreg; i += kBandThreads / 64)
-        if ((uint32_t)ln < s_cnt[i]) put(s_off[i] + ln, a.blk[((int64_t)i * R + r) * kFBlkCap + ln]);
+        for (int i = wv; i < nb; i += kBandThreads / 64) {
+            const uint32_t oc = s_oc[i];
+            if ((uint32_t)ln < (oc >> 16)) put((oc & 0xffffu) + ln, a.blk[((int64_t)(i0 + i) * R + r) * kFBlkCap + ln]);
+        }
+        base += tot;
+        __syncthreads();  // s_oc is rewritten by the next batch
+    }
     for (uint32_t p = threadIdx.x; p < novf; p += kBandThreads) put(nblkc + p, a.cand[r * a.cap + p]);
     for (int o = 32; o >= 1; o >>= 1) {
         q2 += __shfl_xor(q2, o);
@@ -836,35 +847,48 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
         }
     }
     __syncthreads();
-    // ascending output from a bitmap of the selected entries (over s_key)
+    {
+        uint32_t nsel_mine = 0, nsel;
+        for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) nsel_mine += s_idx[p] < 0 ? 1u : 0u;
+        block_exclusive_scan(nsel_mine, scan_lds, &nsel);
+        if (nsel != (uint32_t)keff) {  // cannot happen when the bound holds
+            flag_row();
+            return;
+        }
+    }
+    // ascending output from a bitmap of the selected entries (over s_key), one
+    // pass per kBandOutChunk entries of the row
     uint32_t* bitmap = s_key;
-    const int nwords = (int)((nv + 31) / 32);
-    for (int i = threadIdx.x; i < nwords; i += kBandThreads) bitmap[i] = 0;
-    __syncthreads();
-    for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
-        const int32_t v = s_idx[p];
-        if (v < 0) {
-            const int32_t j = v & 0x7fffffff;
-            atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+    uint32_t written = 0;
+    for (int64_t j0 = 0; j0 < nv; j0 += kBandOutChunk) {
+        const int64_t jn = min(nv - j0, (int64_t)kBandOutChunk);
+        const int nwords = (int)((jn + 31) / 32);
+        for (int i = threadIdx.x; i < nwords; i += kBandThreads) bitmap[i] = 0;
+        __syncthreads();
+        for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
+            const int32_t v = s_idx[p];
+            if (v < 0) {
+                const int64_t j = (int64_t)(v & 0x7fffffff) - j0;
+                if (j >= 0 && j < jn) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+            }
         }
-    }
-    __syncthreads();
-    const int per = (nwords + kBandThreads - 1) / kBandThreads;
-    uint32_t mine = 0;
-    for (int wi = threadIdx.x * per; wi < min(nwords, (int)(threadIdx.x + 1) * per); ++wi) mine += __popc(bitmap[wi]);
-    uint32_t total;
-    uint32_t pos = block_exclusive_scan(mine, scan_lds, &total);
-    if (total != (uint32_t)keff) {  // cannot happen when the bound holds
-        flag_row();
-        return;
-    }
-    for (int wi = threadIdx.x * per; wi < min(nwords, (int)(threadIdx.x + 1) * per); ++wi) {
-        uint32_t word = bitmap[wi];
-        while (word) {
-            const int bit = __ffs(word) - 1;
-            word &= word - 1;
-            out[pos++] = wi * 32 + bit;
+        __syncthreads();
+        const int per = (nwords + kBandThreads - 1) / kBandThreads;
+        uint32_t mine = 0;
+        for (int wi = threadIdx.x * per; wi < min(nwords, (int)(threadIdx.x + 1) * per); ++wi) mine += __popc(bitmap[wi]);
+        uint32_t total;
+        uint32_t pos = written + block_exclusive_scan(mine, scan_lds, &total);
+        for (int wi = threadIdx.x * per; wi < min(nwords, (int)(threadIdx.x + 1) * per); ++wi) {
+            uint32_t word = bitmap[wi];
+            while (word) {
+                const int bit = __ffs(word) - 1;
+                word &= word - 1;
+                if (pos < (uint32_t)keff) out[pos] = (int32_t)(j0 + wi * 32 + bit);
+                ++pos;
+            }
         }
+        written += total;
+        __syncthreads();  // the bitmap is cleared for the next pass
     }
 }
 

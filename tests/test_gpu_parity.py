@@ -564,6 +564,43 @@ def test_prefill_mfma_all_equal_scores_fall_back():
         ikeys=lambda g, k: np.full_like(k, 0x38)).check_all()
 
 
+def _time_layer(run, li, reps=3):
+    # GPU time of repeating layer li (a Full layer rewrites the same entries, so the
+    # repeat is idempotent), HIP events on the layer's stream
+    L = run.inp.layers[li]
+    kw = dict(q=dev(L["q"]), wk=dev(L["wk"]), wv=dev(L["wv"]), W=run.wl.W, sm_scale=run.wl.sm_scale,
+              iq=dev(L["iq"]), new_entry=dev(L["new_entry"]), new_ikey=dev(L["new_ikey"]))
+    g = run.g_gpu[L["group"]]
+    g.layer_step(L["mode"], **kw)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(reps):
+        g.layer_step(L["mode"], **kw)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def test_prefill_mfma_rows_beyond_2_18_visible_entries():
+    # a 1M-token context compressed 4x holds 2^18 entries; a chunk on top of it makes
+    # every row see more.  The band selection writes its output in passes of 2^18
+    # entries, so these rows stay on the MFMA path: bit-exact against the oracle, and
+    # fast (a row recomputed by the exact fallback alone would take > 10 ms)
+    run = Run(W4.scaled(N=(1 << 18) + 3000, Qs=48, k=512))
+    run.check_all()
+    ms = _time_layer(run, 0)
+    print(f"prefill chunk of 48 rows over {(1 << 18) + 3000} entries: {ms:.3f} ms")
+    assert ms < 8.0, ms
+
+
+def test_prefill_k_above_the_mfma_band_limit_takes_the_exact_path():
+    # k beyond what the band selection holds (3k + 2048 candidates in LDS): the chunk is
+    # scored and selected on the exact path instead, still bit-exact
+    Run(W4.scaled(N=12000, Qs=40, k=2100), n_valid=[12000]).check_all()
+
+
 def test_stack_w5_scaled():
     Run(W5.scaled(B=2, N=5000, groups=2), n_valid=[5000, 4321]).check_all()
 
