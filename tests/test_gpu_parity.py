@@ -601,6 +601,70 @@ def test_prefill_k_above_the_mfma_band_limit_takes_the_exact_path():
     Run(W4.scaled(N=12000, Qs=40, k=2100), n_valid=[12000]).check_all()
 
 
+def _e4m3_values(bits):
+    """Exact values of e4m3fn bit patterns (no NaN among the inputs here)."""
+    b = bits.astype(np.int64)
+    e, m = (b >> 3) & 15, b & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where(b & 0x80, -mag, mag)
+
+
+def test_mfma_score_error_within_the_band_bound():
+    # The prefill selection trusts |s^ - s| <= E = 2 gamma_(K-1) ||q|| ||k|| for the fp32
+    # MFMA scores s^ (u = 2^-23, any summation order, doubled).  With N <= 2048 the
+    # threshold-sample GEMM runs at stride 1, so the workspace holds s^ for every (row,
+    # entry); they are read back and checked against the exact sums on adversarial e4m3
+    # inputs: all-subnormal rows, +-448 cancellation with small terms, random bit patterns.
+    rng = np.random.default_rng(448)
+    B, N, Qs, H, d, Hq, D, W, k = 1, 2048, 64, 4, 64, 16, 128, 8, 64
+    K = H * d
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+
+    def kind(n, t):
+        if t == 0:  # N(0,1) rounded to e4m3
+            return synth.to_e4m3_bits(rng.normal(size=(n, K)).astype(np.float32))
+        if t == 1:  # subnormals only
+            return (rng.integers(1, 8, (n, K)) | (rng.integers(0, 2, (n, K)) << 7)).astype(np.uint8)
+        if t == 2:  # +-448 with small terms mixed in: large partial sums that cancel
+            x = np.where(rng.random((n, K)) < 0.5, 0x7E, 0xFE).astype(np.uint8)
+            small = rng.random((n, K)) < 0.25
+            x[small] = rng.integers(1, 0x30, int(small.sum())).astype(np.uint8)
+            return x
+        return codes[rng.integers(0, codes.size, (n, K))]  # any bit pattern
+
+    iq = np.concatenate([kind(Qs // 4, t) for t in range(4)]).reshape(B, Qs, H, d)
+    ik = np.concatenate([kind(N // 4, t) for t in range(4)])[rng.permutation(N)].reshape(B, N, H, d)
+    new_ikey = kind(Qs, 3).reshape(B, Qs, H, d)
+    x = synth.normal_f32(synth.seed(0, 940), B * N * D).reshape(B, N, D)
+    gc, gs = csa2.fp4_pack(dev(x))
+    grp = csa2.Group(gc, gs, dev(ik), dev(np.array([N], np.int32)), "e4m3", k, sel_rows=Qs)
+    q = synth.normal_bf16(synth.seed(0, 941), B * Qs * Hq * D).reshape(B, Qs, Hq, D)
+    wk = synth.normal_bf16(synth.seed(0, 942), B * (Qs + W - 1) * D).reshape(B, Qs + W - 1, D)
+    ne = synth.normal_f32(synth.seed(0, 943), B * Qs * D).reshape(B, Qs, D)
+    ws = grp.workspace(Qs, Hq, W)
+    grp.layer_step("F", q=dev(q), iq=dev(iq), wk=dev(wk), wv=dev(wk), W=W, sm_scale=0.125,
+                   new_entry=dev(ne), new_ikey=dev(new_ikey), ws=ws)
+    torch.cuda.synchronize()
+    # the workspace starts with the exact-score rows [Qs][N] (fp32, 256-byte aligned), then
+    # the sample scores [Qs][ncols] (ncols = N at stride 1)
+    off = (Qs * N * 4 + 255) // 256 * 256
+    samp = host(ws[off:off + Qs * N * 4].view(torch.float32)).reshape(Qs, N).astype(np.float64)
+    keys = ik[0].reshape(N, K).copy()
+    keys[N - Qs:] = new_ikey[0].reshape(Qs, K)
+    qv, kv = _e4m3_values(iq[0].reshape(Qs, K)), _e4m3_values(keys)
+    exact = qv @ kv.T  # e4m3 products and their partial sums are exact in fp64
+    gam = (K - 1) * 2.0 ** -23 / (1 - (K - 1) * 2.0 ** -23)
+    E = 2 * gam * np.sqrt((qv * qv).sum(1))[:, None] * np.sqrt((kv * kv).sum(1))[None, :]
+    visible = np.arange(N)[None, :] <= (N - Qs + np.arange(Qs))[:, None]
+    assert np.all(np.isneginf(samp[~visible]))
+    err = np.abs(samp - exact)[visible]
+    bound = E[visible]
+    assert np.all(err <= bound), float((err - bound).max())
+    ratio = float((err / np.where(bound > 0, bound, 1.0)).max())
+    print(f"MFMA fp32 score error: worst |s^ - s| / E = {ratio:.3e} over {int(visible.sum())} scores")
+    assert np.all(err[bound == 0] == 0)
+
+
 def test_stack_w5_scaled():
     Run(W5.scaled(B=2, N=5000, groups=2), n_valid=[5000, 4321]).check_all()
 
