@@ -46,6 +46,7 @@ struct Layout {
     int64_t bits_ld = 0;
     // prefill selection on MFMA (e4m3 index keys, Qs > 1)
     size_t samp = 0, theta = 0, cand = 0, cand_cnt = 0, flag = 0, flag_count = 0, knorm = 0;
+    size_t kexp = 0, kseq_norm = 0, kseq_exp = 0;  // MFMA error-bound inputs
     size_t blk = 0, blkcnt = 0;
     int cap = 0, nblk = 0;
     size_t part = 0;                     // attention partials
@@ -133,6 +134,13 @@ Layout layer_layout(const csa2_group* g, int Qs, int Hq, int W) {
         off = align_up(off + 4);
         L.knorm = off;
         off = align_up(off + (size_t)g->B * L.nblk * 4);
+        L.kexp = off;
+        const size_t G = (size_t)(g->H_I * g->d_I / 8);  // groups of 8 index elements
+        off = align_up(off + (size_t)g->B * L.nblk * G);
+        L.kseq_norm = off;
+        off = align_up(off + (size_t)g->B * 4);
+        L.kseq_exp = off;
+        off = align_up(off + (size_t)g->B * G);
         L.cand = off;
         off = align_up(off + (size_t)R * L.cap * 8);
         L.blkcnt = off;
@@ -593,6 +601,9 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         ba.cand_cnt = at<uint32_t>(ws, L.cand_cnt);
         ba.cap = L.cap;
         ba.knorm = at<float>(ws, L.knorm);
+        ba.kexp = at<uint8_t>(ws, L.kexp);
+        ba.kseq_norm = at<float>(ws, L.kseq_norm);
+        ba.kseq_exp = at<uint8_t>(ws, L.kseq_exp);
         ba.nblk = (int)((N + 255) / 256);
         ba.idx = g->sel;
         ba.flag = at<int32_t>(ws, L.flag);
@@ -601,7 +612,8 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         ba.ld = g->N_cap;
         e = mark(a->index_events[0], s);
         if (e == hipSuccess) e = launch_gemm_fp8(ga, 0, s);
-        if (e == hipSuccess) e = launch_key_norm(ga.ik, K, g->B, N, g->N_cap, ba.nblk, ba.knorm, s);
+        if (e == hipSuccess) e = launch_key_norm(ga.ik, K, g->B, N, g->N_cap, ba.nblk, ba.knorm, ba.kexp, ba.kseq_norm,
+                                                       ba.kseq_exp, s);
         if (e == hipSuccess) e = launch_sample_select(ba, s);
         if (e == hipSuccess) {
             GemmArgs fa = ga;

@@ -188,6 +188,9 @@ struct BandArgs {
     uint32_t* cand_cnt;
     int cap;
     float* knorm;          // [B][nblk] bounds on max ||k||^2 per 256 entries
+    uint8_t* kexp;         // [B][nblk][K/8] largest key exponent field per block and group of 8
+    float* kseq_norm;      // [B] largest knorm of the sequence
+    uint8_t* kseq_exp;     // [B][K/8] largest kexp of the sequence per group
     int nblk;
     int32_t* idx;          // [B*Qs][k] selection
     int32_t* flag;         // [B*Qs] rows recomputed exactly
@@ -196,8 +199,8 @@ struct BandArgs {
     int64_t ld;
 };
 hipError_t launch_sample_select(const BandArgs& a, hipStream_t stream);
-hipError_t launch_key_norm(const uint8_t* ik, int K, int B, int64_t N, int64_t N_cap, int nblk, float* out,
-                           hipStream_t stream);
+hipError_t launch_key_norm(const uint8_t* ik, int K, int B, int64_t N, int64_t N_cap, int nblk, float* knorm,
+                           uint8_t* kexp, float* kseq_norm, uint8_t* kseq_exp, hipStream_t stream);
 hipError_t launch_band_final(const BandArgs& a, hipStream_t stream);
 int band_cap(int k);    // candidate list length per row
 int band_max_k();       // largest k the candidate path handles
