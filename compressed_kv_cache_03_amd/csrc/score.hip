@@ -795,15 +795,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_fixup_kernel(ScoreArgs a)
     }
 }
 
-// Fallback for index widths the streaming kernel does not tile: one thread per
-// entry, same arithmetic and the same certification.
-__global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
-    const int64_t r = blockIdx.y;
+// Score of (row r, position pe) computed by one thread with the arithmetic and
+// certification of the streaming kernel: false when the certificate cannot
+// decide (then *out is not the score).
+CSA2_DEV bool generic_entry_certified(const ScoreArgs& a, int64_t r, int64_t pe, float* out) {
     const int64_t b = r / a.Qs;
-    const int64_t nv = row_valid(a, r);
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= nv) return;
-    const int64_t pe = slot_entry(a, r, e);
     const int K = a.K;
     double acc = 0.0, aacc = 0.0;
     float qmin = INFINITY, kmin = INFINITY;
@@ -862,21 +858,446 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
     } else {
         res = (float)acc;
     }
-    if (!ok)
-        res = a.dtype == 2
-                  ? exact_fp4_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * K,
-                                  reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + pe) * (K / 2),
-                                  a.ik_scales + (b * a.N_cap + pe) * (K / 32), K)
-                  : exact_bf16_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * K,
-                                   reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + pe) * K, K);
+    *out = res;
+    return ok;
+}
+
+// Exact score of (row r, position pe) computed by one thread: the certified
+// fp64 value, else the integer accumulator.
+CSA2_DEV float generic_entry_score(const ScoreArgs& a, int64_t r, int64_t pe) {
+    float res;
+    if (generic_entry_certified(a, r, pe, &res)) return res;
+    const int64_t b = r / a.Qs;
+    const int K = a.K;
+    return a.dtype == 2
+               ? exact_fp4_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * K,
+                               reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + pe) * (K / 2),
+                               a.ik_scales + (b * a.N_cap + pe) * (K / 32), K)
+               : exact_bf16_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * K,
+                                reinterpret_cast<const uint16_t*>(a.ik) + (b * a.N_cap + pe) * K, K);
+}
+
+// ---------------------------------------------------------------------------
+// FP4 keys (K = 256) on the matrix cores.  The block sums T_c = sum_e q_e * c_e
+// (bf16 query, e2m1 codes, one sum per 32-element key block c) come exactly out
+// of v_mfma_scale_f32_16x16x128_f8f6f4 with e4m3 query parts against the raw FP4
+// codes; fp64 then forms sum_c scale_c * T_c with an error bound, certified as
+// in the streaming kernel.
+//
+// The MFMA is not an exact dot product: it cuts each product in a group of 8
+// consecutive k toward zero to a multiple of 2^(ea + eb - 13), ea + eb the
+// group's largest operand exponent pair (measured on gfx950; e2m1 0.5 counts as
+// exponent 0), sums the group exactly and adds group sums in fp32.  The query
+// side is therefore split so that nothing is ever cut:
+//   * a block's query values fall into bands of 7 binades below its largest
+//     exponent field emax: band b holds fe in (emax - 7(b+1), emax - 7b];
+//   * each value is split into its top 4 significant bits (hi) and its low 4
+//     mantissa bits (lo), both exact e4m3 numbers once scaled by 2^-S_b, S_b the
+//     band's E8M0 scale (hi exponents 1..7, lo exponents -6..3);
+//   * a group's products are then multiples of 2^-3 (hi) or 2^-7 (lo) of 2^S_b,
+//     while its cut step is at most 2^(7+2-13) = 2^-4 or 2^(3+2-13) = 2^-8 of it;
+//     32 products stay below 2^16 (hi) or 2^12 (lo), so every group sum, every
+//     fp32 addition and hi + lo of one band are exact in fp32;
+//   * bands 0-1 (14 binades) cover common rows with one MFMA per 128 codes,
+//     bands 0-3 (28) with two; rows beyond that, with subnormal values, or
+//     with exponents far from 1 take a per-thread fp64 path.
+//
+// MFMA layout (gfx950, probed): B = FP4 codes, lane (n, g) holds column n's
+// codes k = 32g .. 32g+31 in nibble order; A = e4m3, lane (m, g2) holds row m's
+// k = 16g2 .. 16g2+15 (bytes 0-15) and 64+16g2 .. 64+16g2+15 (bytes 16-31);
+// C lane (n, g) holds rows 4g .. 4g+3 of column n.  A tile is 16 entries: lane
+// (n, g) loads entry n's key blocks 2g and 2g+1 (32 contiguous bytes, one MFMA
+// "slice" each) and their two scales; A row 4g + p carries part p (band 2j hi,
+// band 2j lo, band 2j+1 hi, band 2j+1 lo) of key block 2g + slice, so C lane
+// (n, g) receives exactly the parts of its own two blocks.  Four tiles (64
+// entries) are reduced across g with permlane swaps so that lane l ends with
+// entry l of the round.
+constexpr int kF4Threads = 256;                                   // 4 waves
+constexpr int kF4Rounds = 1;                                      // rounds of 64 entries per wave
+constexpr int kF4Ahead = 1;                                       // rounds of keys loaded ahead
+constexpr int kF4MinWaves = 4;                                    // waves per SIMD (launch bound)
+constexpr int kF4EntriesPerBlock = (kF4Threads / 64) * 64 * kF4Rounds;  // 256
+constexpr uint32_t kF4EmaxLo = 64, kF4EmaxHi = 220;  // block exponent fields kept on the MFMA path
+// NaN bit patterns never produced for finite inputs, left in the scores by
+// score_fp4_mfma_kernel for score_fp4_fixup_kernel, which always overwrites them:
+// an entry the certificate could not decide, and an entry of a row outside the
+// bands.  The fixup's rarely taken paths need many registers; kept out of the
+// streaming kernel they leave it room for more waves in flight.
+constexpr uint32_t kF4Undecided = 0x7fc5a2fdu, kF4Outside = 0x7fc5a2feu;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The scaled MFMA with e4m3 A (query parts, E8M0 scale sa) and e2m1 B (codes,
+// unit scale).  The empty asm keeps it at full EXEC: the compiler would
+// otherwise sink it into the branch that stores a result.
+CSA2_DEV f32x4 mfma_q8_k4(const i32x8& q, const u32x4& k, uint32_t sa) {
+    const i32x8 kb = {(int)k[0], (int)k[1], (int)k[2], (int)k[3], 0, 0, 0, 0};
+    f32x4 c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q, kb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0,
+                                                              (int)sa, 0, 127);
+    __asm__ volatile("" : "+v"(c));
+    return c;
+}
+
+// permlane32 (D = 32) or permlane16 (D = 16) swap of an fp64 pair, then their
+// sum: lanes with bit D clear get x(own) + x(lane + D), the others
+// y(lane - D) + y(own).
+template <int D>
+CSA2_DEV double swap_add(double x, double y) {
+    const uint2 xu = __builtin_bit_cast(uint2, x), yu = __builtin_bit_cast(uint2, y);
+    uint2 a, c;
+    if constexpr (D == 32) {
+        const auto lo = __builtin_amdgcn_permlane32_swap(xu.x, yu.x, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(xu.y, yu.y, false, false);
+        a = uint2{lo[0], hi[0]};
+        c = uint2{lo[1], hi[1]};
+    } else {
+        const auto lo = __builtin_amdgcn_permlane16_swap(xu.x, yu.x, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(xu.y, yu.y, false, false);
+        a = uint2{lo[0], hi[0]};
+        c = uint2{lo[1], hi[1]};
+    }
+    return __builtin_bit_cast(double, a) + __builtin_bit_cast(double, c);
+}
+template <int D>
+CSA2_DEV float swap_add(float x, float y) {
+    const auto r = D == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false)
+                           : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One wave's rounds of 64 entries on the matrix cores, NB band pairs.
+struct F4Round {
+    u32x4 c[4][2];  // per tile: the lane's two key blocks (32 bytes)
+    f32x2 sc[4];    // and their scales
+};
+
+// Loads one round (4 tiles of 16 entries from e_round) of a wave: lane (n, g)
+// takes key blocks 2g, 2g+1 of entry e_round + 16t + n.  Entries past nv load
+// entry nv - 1 (in bounds; never stored).
+CSA2_DEV void f4_load_round(const ScoreArgs& a, int64_t b, int64_t nv, int64_t e_round, F4Round& d) {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.ik) + b * a.N_cap * 128 + 32 * g;
+    const float* sbase = a.ik_scales + b * a.N_cap * 8 + 2 * g;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        int64_t e = e_round + 16 * t + n;
+        e = e < nv ? e : nv - 1;
+        const u32x4* src = reinterpret_cast<const u32x4*>(kbase + e * 128);
+        d.c[t][0] = __builtin_nontemporal_load(src);
+        d.c[t][1] = __builtin_nontemporal_load(src + 1);
+        d.sc[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(sbase + e * 8));
+    }
+}
+
+// Where the scores of the lanes with `mine` set are left for the fixup: with a
+// queue (a.fix_list) their (row, entry | flag) items are appended, one atomic
+// per wave; without one the score gets the marker.
+CSA2_DEV void f4_defer(const ScoreArgs& a, bool mine, int64_t r, int64_t e, bool outside) {
+    const uint64_t m = __ballot(mine);
+    if (m == 0) return;
+    if (a.fix_list) {
+        const int lane = threadIdx.x & 63, first = __builtin_ctzll(m);
+        uint32_t base = 0;
+        if (lane == first) base = atomicAdd(a.fix_cnt, (uint32_t)__builtin_popcountll(m));
+        base = (uint32_t)__shfl((int)base, first);
+        if (mine) {
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            a.fix_list[base + rank] = uint2{(uint32_t)r, (uint32_t)e | (outside ? 0x80000000u : 0u)};
+        }
+    } else if (mine) {
+        a.scores[r * a.ld + e] = __uint_as_float(outside ? kF4Outside : kF4Undecided);
+    }
+}
+
+// The wave's rounds: e_block + (NW i + wave) * 64 for i < kF4Rounds.  Keys are
+// loaded kF4Ahead rounds ahead into a ring of round buffers (the caller has
+// issued the first ones); the loop is unrolled so the ring index is static.
+// Entries the certificate cannot decide are deferred (f4_defer) with no histogram
+// count.
+template <int NB>
+CSA2_DEV void fp4_mfma_rows(const ScoreArgs& a, int64_t r, int64_t e_block, int64_t nv, const uint32_t (*s_afr)[2][64][8],
+                            const uint32_t (*s_scl)[2][64], uint32_t* lhist, F4Round (&ring)[kF4Ahead + 1]) {
+    constexpr int NW = kF4Threads / 64;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t b = r / a.Qs;
+    // the A fragments stay in LDS (read per MFMA) to leave registers for the key ring
+    uint32_t scl[NB][2];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) scl[j][s] = s_scl[j][s][lane];
+#pragma unroll
+    for (int i = 0; i < kF4Rounds; ++i) {
+        const int64_t e_round = e_block + (NW * i + wave) * 64;
+        if (e_round >= nv) break;  // wave-uniform
+        const int64_t e_ahead = e_round + kF4Ahead * NW * 64;
+        if (i + kF4Ahead < kF4Rounds && e_ahead < nv)
+            f4_load_round(a, b, nv, e_ahead, ring[(i + kF4Ahead) % (kF4Ahead + 1)]);
+        const F4Round& cur = ring[i % (kF4Ahead + 1)];
+        double P[4];
+        float A[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            double T[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                double ts = 0.0;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const f32x4 c =
+                        mfma_q8_k4(*reinterpret_cast<const i32x8*>(s_afr[j][s][lane]), cur.c[t][s], scl[j][s]);
+                    // hi + lo of one band is exact in fp32; the bands sum exactly in fp64
+                    ts += (double)(c[0] + c[1]) + (double)(c[2] + c[3]);
+                }
+                T[s] = ts;
+            }
+            const double p0 = T[0] * (double)cur.sc[t][0], p1 = T[1] * (double)cur.sc[t][1];
+            P[t] = p0 + p1;
+            A[t] = (float)(fabs(p0) + fabs(p1));
+        }
+        // lane l: entry e_round + l, summed over its 8 key blocks
+        const double acc = swap_add<16>(swap_add<32>(P[0], P[2]), swap_add<32>(P[1], P[3])) + 0.0;
+        const float sabs = swap_add<16>(swap_add<32>(A[0], A[2]), swap_add<32>(A[1], A[3]));
+        // every term saw one product and at most three additions in fp64 (4u), and
+        // sabs (fp32, three roundings) is within 2^-21 of its sum
+        const double eb = (4.001 * 0x1p-53 * (double)sabs * (1.0 + 0x1p-20) + fabs(acc) * 0x1p-52) * (1.0 + 0x1p-40);
+        const float lo = (float)(acc - eb), hi = (float)(acc + eb);
+        const int64_t e = e_round + lane;
+        const bool decided = __float_as_uint(lo) == __float_as_uint(hi);
+        if (e < nv && decided) {
+            a.scores[r * a.ld + e] = lo;
+            if (lhist) atomicAdd(&lhist[sort_key(lo) >> (32 - kHistBits)], 1u);
+        }
+        f4_defer(a, e < nv && !decided, r, e, false);
+    }
+}
+
+__global__ __launch_bounds__(kF4Threads, kF4MinWaves) void score_fp4_mfma_kernel(ScoreArgs a) {
+    constexpr int NW = kF4Threads / 64;
+    static_assert(kF4Threads >= 256, "one thread per query element");
+    int64_t r, e_block;
+    {
+        // tiles are counted in 32 bits (fewer than 2^31 by the launch checks)
+        const uint32_t w = blockIdx.x;
+        const uint32_t t = (w & 7) * (uint32_t)a.per_xcd + (w >> 3);
+        if (t >= (uint32_t)a.blocks) return;
+        const uint32_t Qs = (uint32_t)a.Qs, neb = (uint32_t)a.n_eblk;
+        const uint32_t rest = t / Qs;
+        r = (int64_t)(rest / neb) * Qs + t % Qs;
+        e_block = (int64_t)(rest % neb) * kF4EntriesPerBlock;
+    }
+    const int64_t nv = row_valid(a, r);
+    if (e_block >= nv) return;
+
+    __shared__ uint32_t lhist[kHistBins];
+    __shared__ __attribute__((aligned(32))) uint32_t s_afr[2][2][64][8];  // [band pair][slice][lane][word]: A fragments
+    __shared__ uint32_t s_scl[2][2][64];     // [band pair][slice][lane]: E8M0 scales
+    __shared__ uint32_t s_emax[8], s_band[NW], s_bad[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool with_hist = a.hist != nullptr;
+    // the first rounds' keys are in flight while the query is prepared
+    F4Round ring[kF4Ahead + 1];
+    {
+        const int64_t e0 = e_block + __builtin_amdgcn_readfirstlane(wave) * 64;
+#pragma unroll
+        for (int i = 0; i < kF4Ahead; ++i)
+            if (i < kF4Rounds && e0 + i * NW * 64 < nv) f4_load_round(a, r / a.Qs, nv, e0 + i * NW * 64, ring[i]);
+    }
+    if (with_hist)
+        for (int i = tid; i < kHistBins; i += kF4Threads) lhist[i] = 0;
+    for (int i = tid; i < 2 * 2 * 64 * 8 / 4; i += kF4Threads) reinterpret_cast<u32x4*>(s_afr)[i] = u32x4{0u, 0u, 0u, 0u};
+
+    // query element tid: its block's largest exponent field, its band and its two
+    // e4m3 parts (threads 256.. repeat element tid % 256, which changes no maximum)
+    const int el = tid & 255;
+    const uint32_t x = reinterpret_cast<const uint16_t*>(a.iq)[r * 256 + el];
+    const bool nz = (x & 0x7fffu) != 0;
+    const uint32_t fe = (x >> 7) & 0xffu;
+    uint32_t em = nz ? fe : 0u;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) em = max(em, (uint32_t)__shfl_xor((int)em, o));
+    const uint32_t band = nz ? (em - fe) / 7 : 0u;
+    uint32_t mb = band;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
+    const bool bad = nz && (fe == 0 || em < kF4EmaxLo || em > kF4EmaxHi);
+    const bool wbad = __ballot(bad) != 0;
+    if ((tid & 31) == 0 && tid < 256) s_emax[tid >> 5] = em;
+    if (lane == 0) {
+        s_band[wave] = mb;
+        s_bad[wave] = wbad ? 1u : 0u;
+    }
+    __syncthreads();  // also: the fragments are zeroed
+    uint32_t maxband = 0, rowbad = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        maxband = max(maxband, s_band[w]);
+        rowbad |= s_bad[w];
+    }
+    const int NB = rowbad || maxband >= 4 ? 0 : (maxband >= 2 ? 2 : 1);  // workgroup-uniform
+    uint32_t* const lh = with_hist ? lhist : nullptr;
+
+    if (NB == 0) {
+        // outside the bands: the fixup scores the block
+#pragma unroll 1
+        for (int i = 0; i < kF4Rounds; ++i) {
+            const int64_t e = e_block + i * kF4Threads + tid;
+            f4_defer(a, e < nv, r, e, true);
+        }
+    } else {
+        if (tid < 256) {
+            // element el's parts, as e4m3 bytes scaled by 2^-S (S + 127 = emax - 7 band
+            // - 7): hi = sign, exponent field tt + 14, its top 3 mantissa bits; lo =
+            // its low 4 mantissa bits l times 2^tt, normalised (exponent field tt +
+            // msb(l) + 7).  They go to rows 4g + 2(band & 1) and + 1 of band pair
+            // band / 2, slice blk & 1, at k = 32g + el % 32 (g = blk / 2)
+            if (nz) {
+                const uint32_t sign = (x >> 8) & 0x80u;
+                const int tt = (int)fe - ((int)em - 7 * (int)band);  // -6 .. 0
+                const uint32_t hib = sign | ((uint32_t)(tt + 14) << 3) | ((x >> 4) & 7u);
+                const uint32_t l = x & 15u;
+                const int msb = 31 - __builtin_clz(l | 1u);
+                const uint32_t lob = l == 0 ? 0u : sign | ((uint32_t)(tt + msb + 7) << 3) | ((l << (3 - msb)) & 7u);
+                const int blk = el >> 5, g = blk >> 1, sl = blk & 1;
+                const int k = 32 * g + (el & 31);
+                const int g2 = (k & 63) >> 4, jb = (k & 15) + (k >= 64 ? 16 : 0);
+                const int m = 4 * g + 2 * (int)(band & 1);
+                uint8_t* row = reinterpret_cast<uint8_t*>(&s_afr[band >> 1][sl][m + 16 * g2][0]);
+                row[jb] = (uint8_t)hib;
+                row[32 + jb] = (uint8_t)lob;  // lane m + 1 + 16 g2
+            }
+            // E8M0 scale of lane (j, slice, L): its row's band, of block 2g + slice
+            const int j = tid >> 7, sl = (tid >> 6) & 1, L = tid & 63;
+            if (j < NB) {
+                const int m = L & 15, g = m >> 2, bnd = 2 * j + ((m & 3) >> 1);
+                const uint32_t emx = s_emax[2 * g + sl];
+                s_scl[j][sl][L] = emx == 0 ? 127u : emx - 7u * (uint32_t)bnd - 7u;
+            }
+        }
+        __syncthreads();
+        if (NB == 1)
+            fp4_mfma_rows<1>(a, r, e_block, nv, s_afr, s_scl, lh, ring);
+        else
+            fp4_mfma_rows<2>(a, r, e_block, nv, s_afr, s_scl, lh, ring);
+    }
+    if (with_hist) {
+        __syncthreads();
+        uint32_t* ghist = a.hist + r * kHistBins;
+        for (int i = tid; i < kHistBins; i += kF4Threads) {
+            const uint32_t c = lhist[i];
+            if (c) atomicAdd(&ghist[i], c);
+        }
+    }
+}
+
+// Fallback for index widths the streaming kernel does not tile: one thread per
+// entry, same arithmetic and the same certification.
+__global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
+    const int64_t r = blockIdx.y;
+    const int64_t nv = row_valid(a, r);
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= nv) return;
+    const float res = generic_entry_score(a, r, slot_entry(a, r, e));
     a.scores[r * a.ld + e] = res;
     if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
 }
 
+// Score of (row r, entry e) for FP4 keys computed by a whole wave in fp64: lane l
+// takes elements l, l+64, l+128, l+192; every product q * e2m1 * scale is exact in
+// fp64 (8 + 2 + 24 significant bits) and their sum is within
+// gamma_(K-1) * sum|p| of the exact one in any order.  false when the rounding
+// to fp32 is not decided by that bound.
+CSA2_DEV bool wave_certified_fp4(const ScoreArgs& a, int64_t r, int64_t e, int lane, float* out) {
+    const int64_t b = r / a.Qs;
+    const int K = a.K;
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.iq) + r * K;
+    const uint8_t* k = reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * (K / 2);
+    const float* sc = a.ik_scales + (b * a.N_cap + e) * (K / 32);
+    double acc = 0.0, aacc = 0.0;
+    for (int i = lane; i < K; i += 64) {
+        const uint32_t nib = (k[i >> 1] >> (4 * (i & 1))) & 15u;
+        const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, 1.0f, 0);
+        const double p = (double)bf16_to_f32(q[i]) * (double)v[0] * (double)sc[i >> 5];
+        acc += p;
+        aacc += fabs(p);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        acc += __shfl_xor(acc, o);
+        aacc += __shfl_xor(aacc, o);
+    }
+    // aacc is itself an fp64 sum of K terms: low by at most a factor (1 - K 2^-53)
+    const double eb = ((double)K * 0x1p-53 * 1.001 * aacc * (1.0 + (double)K * 0x1p-52) + fabs(acc) * 0x1p-52);
+    const float lo = (float)(acc - eb), hi = (float)(acc + eb);
+    *out = lo;
+    return __float_as_uint(lo) == __float_as_uint(hi);
+}
+
+// Scores the items score_fp4_mfma_kernel queued (a.fix_list), one per wave:
+// entries of rows outside the bands (flag bit 31) first in fp64
+// (wave_certified_fp4), then, like the undecided entries, exactly with the
+// integer accumulator.
+__global__ __launch_bounds__(256) void score_fp4_list_kernel(ScoreArgs a) {
+    const uint32_t n = *a.fix_cnt;
+    const int lane = threadIdx.x & 63;
+    const uint32_t wid = blockIdx.x * 4 + (threadIdx.x >> 6), nw = gridDim.x * 4;
+#pragma unroll 1
+    for (uint32_t i = wid; i < n; i += nw) {
+        const uint2 it = a.fix_list[i];
+        const int64_t r = it.x, e = it.y & 0x7fffffffu, b = r / a.Qs;
+        float res = 0.0f;
+        const bool ok = (it.y >> 31) != 0 && wave_certified_fp4(a, r, e, lane, &res);
+        if (!ok)
+            res = wave_exact_fp4_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * a.K,
+                                     reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * (a.K / 2),
+                                     a.ik_scales + (b * a.N_cap + e) * (a.K / 32), a.K, lane);
+        if (lane == 0) {
+            a.scores[r * a.ld + e] = res;
+            if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
+        }
+    }
+}
+
+// Scores the entries score_fp4_mfma_kernel left marked.  kF4Outside: one thread
+// per entry with the streaming kernel's fp64 arithmetic and certificate;
+// kF4Undecided, and what that leaves undecided, are computed exactly by the
+// whole wave at once.  Each thread checks four entries of its row.
+__global__ __launch_bounds__(256) void score_fp4_fixup_kernel(ScoreArgs a) {
+    const int64_t r = blockIdx.y, b = r / a.Qs;
+    const int64_t nv = row_valid(a, r);
+    const int lane = threadIdx.x & 63;
+#pragma unroll 1
+    for (int j = 0; j < 4; ++j) {
+        const int64_t e = (int64_t)blockIdx.x * 1024 + j * 256 + threadIdx.x;
+        const uint32_t m = e < nv ? __float_as_uint(a.scores[r * a.ld + e]) : 0u;
+        const bool outside = m == kF4Outside, marked = outside || m == kF4Undecided;
+        if (__ballot(marked) == 0) continue;
+        float res = 0.0f;
+        const bool ok = outside && generic_entry_certified(a, r, e, &res);
+        uint64_t pend = __ballot(marked && !ok);
+        while (pend) {
+            const int L = __builtin_ctzll(pend);
+            pend &= pend - 1;
+            const int64_t eL = __builtin_amdgcn_readlane((int)e, L);
+            const float x = wave_exact_fp4_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * a.K,
+                                               reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + eL) * (a.K / 2),
+                                               a.ik_scales + (b * a.N_cap + eL) * (a.K / 32), a.K, lane);
+            if (lane == L) res = x;
+        }
+        if (marked) {
+            a.scores[r * a.ld + e] = res;
+            if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
+        }
+    }
+}
+
+
 // Which scoring kernel a call takes, with its tiling (n_eblk, blocks, per_xcd
-// filled in a).  ROWS: several rows share key loads; STREAM: one row per
-// workgroup tile; GENERIC: one thread per entry.
-enum class ScorePath { ROWS, STREAM, GENERIC };
+// filled in a).  ROWS: several rows share key loads; FP4: FP4 keys with K = 256
+// on the matrix cores; STREAM: one row per workgroup tile; GENERIC: one thread
+// per entry.
+enum class ScorePath { ROWS, FP4, STREAM, GENERIC };
 
 static ScorePath plan_score(ScoreArgs& a, int* cpl_out, int* qr_out) {
     const int64_t R = (int64_t)a.B * a.Qs;
@@ -893,6 +1314,12 @@ static ScorePath plan_score(ScoreArgs& a, int* cpl_out, int* qr_out) {
         a.per_xcd = (a.blocks + 7) / 8;
         return ScorePath::ROWS;
     }
+    if (a.dtype == 2 && a.K == 256 && !a.pool) {
+        a.n_eblk = (a.N + kF4EntriesPerBlock - 1) / kF4EntriesPerBlock;
+        a.blocks = a.n_eblk * R;
+        a.per_xcd = (a.blocks + 7) / 8;
+        return ScorePath::FP4;
+    }
     if (fast) {
         a.n_eblk = (a.N + kScoreEntriesPerBlock - 1) / kScoreEntriesPerBlock;
         a.blocks = a.n_eblk * R;
@@ -908,6 +1335,7 @@ int64_t score_grid_threads(const ScoreArgs& args) {
     int cpl, qr;
     switch (plan_score(a, &cpl, &qr)) {
         case ScorePath::ROWS: return 8 * a.per_xcd * kScoreThreads;
+        case ScorePath::FP4: return 8 * a.per_xcd * kF4Threads;
         case ScorePath::STREAM: return 8 * a.per_xcd * kStreamThreads;
         default: return (a.N + 255) / 256 * 256;
     }
@@ -953,6 +1381,14 @@ hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
         CSA2_ROWS_LAUNCH(4, 5)
 #undef CSA2_ROWS_LAUNCH
         hipLaunchKernelGGL(score_fixup_kernel, dim3(256), dim3(kScoreThreads), 0, stream, a);
+    } else if (path == ScorePath::FP4) {
+        hipLaunchKernelGGL(score_fp4_mfma_kernel, dim3((unsigned)(8 * a.per_xcd)), dim3(kF4Threads), 0, stream, a);
+        if (a.fix_list)
+            hipLaunchKernelGGL(score_fp4_list_kernel, dim3(256), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL(score_fp4_fixup_kernel, dim3((unsigned)((a.N + 1023) / 1024), (unsigned)R), dim3(256),
+                               0, stream, a);
+
     } else if (path == ScorePath::STREAM) {
         const dim3 grid((unsigned)(8 * a.per_xcd));
         const bool pool = a.pool != nullptr;

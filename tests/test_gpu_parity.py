@@ -175,6 +175,63 @@ def test_index_score_fp4_keys_rounding_ties_take_exact_path():
     assert bits_eq(host(got), oracle.index_score("fp4", iq, codes, ik_scales=scales))
 
 
+def _bf16_fields(rng, fields):
+    """bf16 bits with the given exponent fields, random sign and mantissa."""
+    fields = np.asarray(fields, np.int64)
+    return ((rng.integers(0, 2, fields.shape) << 15) | (fields << 7) |
+            rng.integers(0, 128, fields.shape)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("case", ["normal", "band1", "band3", "beyond", "subnormal", "zeros", "edges"])
+def test_index_score_fp4_mfma_bands(case):
+    # FP4 keys with K = 256 score on the matrix cores when every query block's values lie within
+    # 28 binades of the block's largest (bands of 7 binades, one or two band pairs) and the
+    # exponents are moderate; other rows take the per-thread fp64 path.  Each case mixes rows of
+    # both kinds with ragged N (3000 = 2048 + 952) and three rows per sequence.
+    rng = np.random.default_rng(["normal", "band1", "band3", "beyond", "subnormal", "zeros", "edges"].index(case))
+    B, Qs, N, H, d = 2, 3, 3000, 4, 64
+    K = H * d
+    R = B * Qs
+    emax = 127 + rng.integers(-3, 4, (R, K // 32, 1))
+    if case == "normal":
+        iq = synth.to_bf16_bits(rng.normal(size=(R, K)).astype(np.float32))
+    elif case in ("band1", "band3", "beyond"):
+        span = 14 if case == "band1" else 28
+        f = emax - rng.integers(0, span, (R, K // 32, 32))
+        f[:, :, 0] = emax[:, :, 0]
+        f[:, :, 1] = emax[:, :, 0] - (span - 1)  # the deepest band's lowest binade
+        if case == "beyond":
+            f[0, 3, 5] = emax[0, 3, 0] - 28
+        iq = _bf16_fields(rng, f).reshape(R, K)
+    elif case == "subnormal":
+        iq = synth.to_bf16_bits(rng.normal(size=(R, K)).astype(np.float32))
+        iq[1, 77] = 0x0005
+        iq[4, 3] = 0x8041
+    elif case == "zeros":
+        iq = synth.to_bf16_bits(rng.normal(size=(R, K)).astype(np.float32))
+        iq[rng.random((R, K)) < 0.3] = 0
+        iq[0, 64:96] = 0x8000  # a block of -0
+        iq[2, :] = 0
+    else:  # edges: block maxima at the ends of the MFMA range and just outside it
+        f = emax - rng.integers(0, 10, (R, K // 32, 32))
+        for row, top in enumerate([64 + 9, 63, 220, 221, 127, 64]):
+            f[row] += top - emax[row]
+            f[row, :, 0] = top
+        iq = _bf16_fields(rng, np.maximum(f, 1)).reshape(R, K)
+    iq = iq.reshape(B, Qs, H, d)
+    codes = rng.integers(0, 256, (B, N, H, d // 2)).astype(np.uint8)
+    sc = ((rng.random((B, N, K // 32)) + 0.5) * np.exp2(rng.integers(-20, 20, (B, N, K // 32))) *
+          np.where(rng.random((B, N, K // 32)) < 0.2, -1.0, 1.0))
+    sc[:, ::11, 3] = 0.0
+    scales = sc.astype(np.float32)
+    for causal in (-1, N - Qs - 100):
+        got = csa2.index_score(dev(iq), dev(codes), "fp4", ik_scales=dev(scales), causal_offset=causal)
+        torch.cuda.synchronize()
+        nv = None if causal < 0 else np.tile(causal + 1 + np.arange(Qs), B).astype(np.int64)
+        want = oracle.index_score("fp4", iq, codes, n_valid_row=nv, ik_scales=scales)
+        assert bits_eq(host(got), want), case
+
+
 # ---------------------------------------------------------------- S3 top-k
 def _topk_scores(R, N, seed):
     rng = np.random.default_rng(seed)
@@ -473,6 +530,26 @@ def test_w8_hierarchical_all_scores_equal():
     # equal keys: every block ties, the pool is the first blocks and Reindex the first entries
     Run(W8.scaled(B=2, N=2000, k=50, pool_blocks=20), n_valid=[2000, 1501],
         ikeys=lambda g, k: np.full_like(k, k.flat[0])).check_all()
+
+
+def _fp4_band_queries(iq):
+    # rows of every kind the FP4 matrix-core scorer meets, by row index mod 4: one band pair,
+    # two band pairs (a value 20 binades below its block's largest), and rows it leaves to the
+    # queue (a value 30 binades below, or a subnormal)
+    out = iq.copy()
+    flat = out.reshape(-1, out.shape[-2] * out.shape[-1])
+    for r in range(flat.shape[0]):
+        emax = int(((flat[r, :32] >> 7) & 0xFF).max())
+        kind = r % 4
+        if kind in (1, 2):
+            flat[r, 5] = ((emax - (20 if kind == 1 else 30)) << 7) | 0x35
+        elif kind == 3:
+            flat[r, 9] = 0x0003
+    return out
+
+
+def test_w7_fp4_keys_rows_outside_the_bands():
+    Run(W7.scaled(B=4, N=3000, k=300), n_valid=[3000, 2999, 1234, 3000], iq=_fp4_band_queries).check_all()
 
 
 def test_w8_hierarchical_fp4_keys_and_draft_rows():
