@@ -266,6 +266,26 @@ CSA2_DEV float wave_exact_fp4_dot(const uint16_t* q, const uint8_t* codes, const
     return fix_to_f32(d, -288);
 }
 
+// wave_exact_fp4_dot for K = 256 with every lane's loads issued before the
+// accumulation (lane l: elements l, l+64, l+128, l+192).
+CSA2_DEV float wave_exact_fp4_256(const uint16_t* q, const uint8_t* codes, const float* scales, int lane) {
+    uint32_t qx[4], nib[4], sb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = lane + 64 * u;
+        qx[u] = q[i];
+        nib[u] = codes[i >> 1];
+        sb[u] = __float_as_uint(scales[i >> 5]);
+    }
+    int64_t d[kFixDigits];
+#pragma unroll
+    for (int j = 0; j < kFixDigits; ++j) d[j] = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fp4_accum(d, qx[u], (nib[u] >> (4 * (lane & 1))) & 15u, sb[u]);
+    wave_sum_digits(d);
+    return fix_to_f32(d, -288);
+}
+
 // Bound on the error of a block sum of 32 products q * e2m1 accumulated with fp64
 // FMAs: zero when the sum is provably exact, else gamma_32 * 6 * sum|q|.  Every
 // product is a multiple of 2^(emin - 135) (bf16 lsb 2^(E-134), e2m1 lsb 2^-1), so
@@ -1203,18 +1223,19 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
     if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
 }
 
-// Score of (row r, entry e) for FP4 keys computed by a whole wave in fp64: lane l
+// Score of (row r, entry e) for FP4 keys (K = 256) computed by a whole wave in fp64: lane l
 // takes elements l, l+64, l+128, l+192; every product q * e2m1 * scale is exact in
 // fp64 (8 + 2 + 24 significant bits) and their sum is within
 // gamma_(K-1) * sum|p| of the exact one in any order.  false when the rounding
 // to fp32 is not decided by that bound.
 CSA2_DEV bool wave_certified_fp4(const ScoreArgs& a, int64_t r, int64_t e, int lane, float* out) {
     const int64_t b = r / a.Qs;
-    const int K = a.K;
+    constexpr int K = 256;
     const uint16_t* q = reinterpret_cast<const uint16_t*>(a.iq) + r * K;
     const uint8_t* k = reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * (K / 2);
     const float* sc = a.ik_scales + (b * a.N_cap + e) * (K / 32);
     double acc = 0.0, aacc = 0.0;
+#pragma unroll
     for (int i = lane; i < K; i += 64) {
         const uint32_t nib = (k[i >> 1] >> (4 * (i & 1))) & 15u;
         const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, 1.0f, 0);
@@ -1249,9 +1270,9 @@ __global__ __launch_bounds__(256) void score_fp4_list_kernel(ScoreArgs a) {
         float res = 0.0f;
         const bool ok = (it.y >> 31) != 0 && wave_certified_fp4(a, r, e, lane, &res);
         if (!ok)
-            res = wave_exact_fp4_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * a.K,
-                                     reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * (a.K / 2),
-                                     a.ik_scales + (b * a.N_cap + e) * (a.K / 32), a.K, lane);
+            res = wave_exact_fp4_256(reinterpret_cast<const uint16_t*>(a.iq) + r * 256,
+                                     reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * 128,
+                                     a.ik_scales + (b * a.N_cap + e) * 8, lane);
         if (lane == 0) {
             a.scores[r * a.ld + e] = res;
             if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
@@ -1280,9 +1301,9 @@ __global__ __launch_bounds__(256) void score_fp4_fixup_kernel(ScoreArgs a) {
             const int L = __builtin_ctzll(pend);
             pend &= pend - 1;
             const int64_t eL = __builtin_amdgcn_readlane((int)e, L);
-            const float x = wave_exact_fp4_dot(reinterpret_cast<const uint16_t*>(a.iq) + r * a.K,
-                                               reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + eL) * (a.K / 2),
-                                               a.ik_scales + (b * a.N_cap + eL) * (a.K / 32), a.K, lane);
+            const float x = wave_exact_fp4_256(reinterpret_cast<const uint16_t*>(a.iq) + r * 256,
+                                               reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + eL) * 128,
+                                               a.ik_scales + (b * a.N_cap + eL) * 8, lane);
             if (lane == L) res = x;
         }
         if (marked) {
