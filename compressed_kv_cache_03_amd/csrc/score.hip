@@ -986,6 +986,37 @@ CSA2_DEV float swap_add(float x, float y) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The two operands a permlane swap_add<D> would add, for checks on the sum.
+template <int D>
+CSA2_DEV void swap_pair(double x, double y, double& a, double& c) {
+    const uint2 xu = __builtin_bit_cast(uint2, x), yu = __builtin_bit_cast(uint2, y);
+    if constexpr (D == 32) {
+        const auto lo = __builtin_amdgcn_permlane32_swap(xu.x, yu.x, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(xu.y, yu.y, false, false);
+        a = __builtin_bit_cast(double, uint2{lo[0], hi[0]});
+        c = __builtin_bit_cast(double, uint2{lo[1], hi[1]});
+    } else {
+        const auto lo = __builtin_amdgcn_permlane16_swap(xu.x, yu.x, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(xu.y, yu.y, false, false);
+        a = __builtin_bit_cast(double, uint2{lo[0], hi[0]});
+        c = __builtin_bit_cast(double, uint2{lo[1], hi[1]});
+    }
+}
+template <int D>
+CSA2_DEV uint32_t swap_and(uint32_t x, uint32_t y) {
+    const auto r = D == 32 ? __builtin_amdgcn_permlane32_swap(x, y, false, false)
+                           : __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    return r[0] & r[1];
+}
+
+// s = a + c and whether that addition was exact (the TwoSum error is zero).
+CSA2_DEV double add_exact(double a, double c, uint32_t& exact) {
+    const double s = a + c, bv = s - a;
+    const double err = (a - (s - bv)) + (c - bv);
+    exact &= err == 0.0 ? 1u : 0u;
+    return s;
+}
+
 // One wave's rounds of 64 entries on the matrix cores, NB band pairs.
 struct F4Round {
     u32x4 c[4][2];  // per tile: the lane's two key blocks (32 bytes)
@@ -1084,10 +1115,50 @@ CSA2_DEV void fp4_mfma_rows(const ScoreArgs& a, int64_t r, int64_t e_block, int6
         const double eb = (4.001 * 0x1p-53 * (double)sabs * (1.0 + 0x1p-20) + fabs(acc) * 0x1p-52) * (1.0 + 0x1p-40);
         const float lo = (float)(acc - eb), hi = (float)(acc + eb);
         const int64_t e = e_round + lane;
-        const bool decided = __float_as_uint(lo) == __float_as_uint(hi);
+        bool decided = __float_as_uint(lo) == __float_as_uint(hi);
+        float res = lo;
+        if (__ballot(e < nv && !decided) != 0) {
+            // rare (exact fp32 ties, mostly): the same sum again with every
+            // product and addition checked; when none rounded, acc is the exact
+            // value and its fp32 rounding is the score
+            double Q[4];
+            uint32_t X[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                uint32_t ex = 1u;
+                double p[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    double ts = 0.0;
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        const f32x4 c =
+                            mfma_q8_k4(*reinterpret_cast<const i32x8*>(s_afr[j][s][lane]), cur.c[t][s], scl[j][s]);
+                        ts += (double)(c[0] + c[1]) + (double)(c[2] + c[3]);
+                    }
+                    const double sd = (double)cur.sc[t][s];
+                    p[s] = ts * sd;
+                    ex &= fma(ts, sd, -p[s]) == 0.0 ? 1u : 0u;
+                }
+                Q[t] = add_exact(p[0], p[1], ex);
+                X[t] = ex;
+            }
+            double u0, u1, v0, v1, w0, w1;
+            swap_pair<32>(Q[0], Q[2], u0, u1);
+            swap_pair<32>(Q[1], Q[3], v0, v1);
+            uint32_t xu = swap_and<32>(X[0], X[2]), xv = swap_and<32>(X[1], X[3]);
+            const double su = add_exact(u0, u1, xu), sv = add_exact(v0, v1, xv);
+            swap_pair<16>(su, sv, w0, w1);
+            uint32_t xw = swap_and<16>(xu, xv);
+            const double sw = add_exact(w0, w1, xw);
+            if (!decided && xw != 0u) {
+                decided = true;
+                res = (float)sw;
+            }
+        }
         if (e < nv && decided) {
-            a.scores[r * a.ld + e] = lo;
-            if (lhist) atomicAdd(&lhist[sort_key(lo) >> (32 - kHistBits)], 1u);
+            a.scores[r * a.ld + e] = res;
+            if (lhist) atomicAdd(&lhist[sort_key(res) >> (32 - kHistBits)], 1u);
         }
         f4_defer(a, e < nv && !decided, r, e, false);
     }
