@@ -926,17 +926,18 @@ CSA2_DEV float generic_entry_score(const ScoreArgs& a, int64_t r, int64_t pe) {
 // codes k = 32g .. 32g+31 in nibble order; A = e4m3, lane (m, g2) holds row m's
 // k = 16g2 .. 16g2+15 (bytes 0-15) and 64+16g2 .. 64+16g2+15 (bytes 16-31);
 // C lane (n, g) holds rows 4g .. 4g+3 of column n.  A tile is 16 entries: lane
-// (n, g) loads entry n's key blocks 2g and 2g+1 (32 contiguous bytes, one MFMA
-// "slice" each) and their two scales; A row 4g + p carries part p (band 2j hi,
+// (n, g) holds entry n's key blocks 2g and 2g+1 (32 contiguous bytes, one MFMA
+// "slice" each) and their two scales, rearranged through LDS from loads of whole
+// 128-byte lines; A row 4g + p carries part p (band 2j hi,
 // band 2j lo, band 2j+1 hi, band 2j+1 lo) of key block 2g + slice, so C lane
 // (n, g) receives exactly the parts of its own two blocks.  Four tiles (64
 // entries) are reduced across g with permlane swaps so that lane l ends with
 // entry l of the round.
-constexpr int kF4Threads = 256;                                   // 4 waves
+constexpr int kF4Threads = 512;                                   // 8 waves
 constexpr int kF4Rounds = 1;                                      // rounds of 64 entries per wave
 constexpr int kF4Ahead = 1;                                       // rounds of keys loaded ahead
 constexpr int kF4MinWaves = 4;                                    // waves per SIMD (launch bound)
-constexpr int kF4EntriesPerBlock = (kF4Threads / 64) * 64 * kF4Rounds;  // 256
+constexpr int kF4EntriesPerBlock = (kF4Threads / 64) * 64 * kF4Rounds;  // 512
 constexpr uint32_t kF4EmaxLo = 64, kF4EmaxHi = 220;  // block exponent fields kept on the MFMA path
 // NaN bit patterns never produced for finite inputs, left in the scores by
 // score_fp4_mfma_kernel for score_fp4_fixup_kernel, which always overwrites them:
@@ -1019,27 +1020,49 @@ CSA2_DEV double add_exact(double a, double c, uint32_t& exact) {
 
 // One wave's rounds of 64 entries on the matrix cores, NB band pairs.
 struct F4Round {
-    u32x4 c[4][2];  // per tile: the lane's two key blocks (32 bytes)
-    f32x2 sc[4];    // and their scales
+    u32x4 c[4][2];  // per tile: 16 bytes of each of two entries (as loaded)
+    f32x2 sc[4];    // and two scales of one entry
 };
 
-// Loads one round (4 tiles of 16 entries from e_round) of a wave: lane (n, g)
-// takes key blocks 2g, 2g+1 of entry e_round + 16t + n.  Entries past nv load
-// entry nv - 1 (in bounds; never stored).
+// Loads one round (4 tiles of 16 entries from e_round) of a wave in whole 128-byte
+// lines: per tile, lane L takes chunk L % 8 (16 bytes, one key block) of entries
+// e_round + 16t + L / 8 and + 8, and scales 2(L % 4), 2(L % 4) + 1 of entry
+// e_round + 16t + L / 4.  Entries past nv load entry nv - 1 (in bounds; never
+// stored).  f4_tile rearranges a tile for the matrix cores.
 CSA2_DEV void f4_load_round(const ScoreArgs& a, int64_t b, int64_t nv, int64_t e_round, F4Round& d) {
-    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.ik) + b * a.N_cap * 128 + 32 * g;
-    const float* sbase = a.ik_scales + b * a.N_cap * 8 + 2 * g;
+    const int lane = threadIdx.x & 63;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.ik) + b * a.N_cap * 128 + 16 * (lane & 7);
+    const float* sbase = a.ik_scales + b * a.N_cap * 8 + 2 * (lane & 3);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        int64_t e = e_round + 16 * t + n;
-        e = e < nv ? e : nv - 1;
-        const u32x4* src = reinterpret_cast<const u32x4*>(kbase + e * 128);
-        d.c[t][0] = __builtin_nontemporal_load(src);
-        d.c[t][1] = __builtin_nontemporal_load(src + 1);
-        d.sc[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(sbase + e * 8));
+        int64_t e0 = e_round + 16 * t + (lane >> 3), e1 = e0 + 8, es = e_round + 16 * t + (lane >> 2);
+        e0 = e0 < nv ? e0 : nv - 1;
+        e1 = e1 < nv ? e1 : nv - 1;
+        es = es < nv ? es : nv - 1;
+        d.c[t][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + e0 * 128));
+        d.c[t][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + e1 * 128));
+        d.sc[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(sbase + es * 8));
     }
 }
+
+constexpr int kF4TilePitch = 144;                   // bytes per entry row in LDS (128 + 16 against bank conflicts)
+constexpr int kF4TileBytes = 16 * kF4TilePitch + 16 * 32;  // codes and scales of one tile
+
+// Tile t of a loaded round in the matrix-core layout, through the wave's LDS
+// buffer wb: lane (n, g) gets entry n's key blocks 2g and 2g + 1 (kc[0], kc[1])
+// and their scales.
+CSA2_DEV void f4_tile(const F4Round& d, int t, uint8_t* wb, u32x4 (&kc)[2], f32x2& ks) {
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    *reinterpret_cast<u32x4*>(wb + (lane >> 3) * kF4TilePitch + 16 * (lane & 7)) = d.c[t][0];
+    *reinterpret_cast<u32x4*>(wb + ((lane >> 3) + 8) * kF4TilePitch + 16 * (lane & 7)) = d.c[t][1];
+    *reinterpret_cast<f32x2*>(wb + 16 * kF4TilePitch + 8 * lane) = d.sc[t];
+    __builtin_amdgcn_wave_barrier();
+    kc[0] = *reinterpret_cast<const u32x4*>(wb + n * kF4TilePitch + 32 * g);
+    kc[1] = *reinterpret_cast<const u32x4*>(wb + n * kF4TilePitch + 32 * g + 16);
+    ks = *reinterpret_cast<const f32x2*>(wb + 16 * kF4TilePitch + 32 * n + 8 * g);
+    __builtin_amdgcn_wave_barrier();
+}
+
 
 // Where the scores of the lanes with `mine` set are left for the fixup: with a
 // queue (a.fix_list) their (row, entry | flag) items are appended, one atomic
@@ -1068,7 +1091,8 @@ CSA2_DEV void f4_defer(const ScoreArgs& a, bool mine, int64_t r, int64_t e, bool
 // count.
 template <int NB>
 CSA2_DEV void fp4_mfma_rows(const ScoreArgs& a, int64_t r, int64_t e_block, int64_t nv, const uint32_t (*s_afr)[2][64][8],
-                            const uint32_t (*s_scl)[2][64], uint32_t* lhist, F4Round (&ring)[kF4Ahead + 1]) {
+                            const uint32_t (*s_scl)[2][64], uint32_t* lhist, F4Round (&ring)[kF4Ahead + 1],
+                            uint8_t* wb) {
     constexpr int NW = kF4Threads / 64;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t b = r / a.Qs;
@@ -1090,20 +1114,22 @@ CSA2_DEV void fp4_mfma_rows(const ScoreArgs& a, int64_t r, int64_t e_block, int6
         float A[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
+            u32x4 kc[2];
+            f32x2 ks;
+            f4_tile(cur, t, wb, kc, ks);
             double T[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 double ts = 0.0;
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    const f32x4 c =
-                        mfma_q8_k4(*reinterpret_cast<const i32x8*>(s_afr[j][s][lane]), cur.c[t][s], scl[j][s]);
+                    const f32x4 c = mfma_q8_k4(*reinterpret_cast<const i32x8*>(s_afr[j][s][lane]), kc[s], scl[j][s]);
                     // hi + lo of one band is exact in fp32; the bands sum exactly in fp64
                     ts += (double)(c[0] + c[1]) + (double)(c[2] + c[3]);
                 }
                 T[s] = ts;
             }
-            const double p0 = T[0] * (double)cur.sc[t][0], p1 = T[1] * (double)cur.sc[t][1];
+            const double p0 = T[0] * (double)ks[0], p1 = T[1] * (double)ks[1];
             P[t] = p0 + p1;
             A[t] = (float)(fabs(p0) + fabs(p1));
         }
@@ -1127,16 +1153,18 @@ CSA2_DEV void fp4_mfma_rows(const ScoreArgs& a, int64_t r, int64_t e_block, int6
             for (int t = 0; t < 4; ++t) {
                 uint32_t ex = 1u;
                 double p[2];
+                u32x4 kc[2];
+                f32x2 ks;
+                f4_tile(cur, t, wb, kc, ks);
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     double ts = 0.0;
 #pragma unroll
                     for (int j = 0; j < NB; ++j) {
-                        const f32x4 c =
-                            mfma_q8_k4(*reinterpret_cast<const i32x8*>(s_afr[j][s][lane]), cur.c[t][s], scl[j][s]);
+                        const f32x4 c = mfma_q8_k4(*reinterpret_cast<const i32x8*>(s_afr[j][s][lane]), kc[s], scl[j][s]);
                         ts += (double)(c[0] + c[1]) + (double)(c[2] + c[3]);
                     }
-                    const double sd = (double)cur.sc[t][s];
+                    const double sd = (double)ks[s];
                     p[s] = ts * sd;
                     ex &= fma(ts, sd, -p[s]) == 0.0 ? 1u : 0u;
                 }
@@ -1184,6 +1212,7 @@ __global__ __launch_bounds__(kF4Threads, kF4MinWaves) void score_fp4_mfma_kernel
     __shared__ uint32_t lhist[kHistBins];
     __shared__ __attribute__((aligned(32))) uint32_t s_afr[2][2][64][8];  // [band pair][slice][lane][word]: A fragments
     __shared__ uint32_t s_scl[2][2][64];     // [band pair][slice][lane]: E8M0 scales
+    __shared__ __attribute__((aligned(16))) uint8_t s_tile[NW][kF4TileBytes];  // per wave: a tile rearranged
     __shared__ uint32_t s_emax[8], s_band[NW], s_bad[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool with_hist = a.hist != nullptr;
@@ -1268,9 +1297,9 @@ __global__ __launch_bounds__(kF4Threads, kF4MinWaves) void score_fp4_mfma_kernel
         }
         __syncthreads();
         if (NB == 1)
-            fp4_mfma_rows<1>(a, r, e_block, nv, s_afr, s_scl, lh, ring);
+            fp4_mfma_rows<1>(a, r, e_block, nv, s_afr, s_scl, lh, ring, s_tile[wave]);
         else
-            fp4_mfma_rows<2>(a, r, e_block, nv, s_afr, s_scl, lh, ring);
+            fp4_mfma_rows<2>(a, r, e_block, nv, s_afr, s_scl, lh, ring, s_tile[wave]);
     }
     if (with_hist) {
         __syncthreads();
