@@ -624,29 +624,28 @@ __global__ __launch_bounds__(256) void key_norm_kernel(const uint8_t* __restrict
     }
 }
 
-// Per sequence: the largest block bound on ||k||^2 and, per group of 8 elements,
-// the largest key exponent field over all blocks.
+// Per sequence: the largest block bound on ||k||^2 (blockIdx.y == G) and, per group
+// g = blockIdx.y < G of 8 elements, the largest key exponent field over all blocks.
 __global__ __launch_bounds__(256) void key_bound_kernel(const float* __restrict__ knorm,
                                                          const uint8_t* __restrict__ kexp, int nblk, int G,
                                                          float* kseq_norm, uint8_t* kseq_exp) {
-    __shared__ uint32_t s_exp[32];
     __shared__ float red[4];
-    const int b = blockIdx.x;
-    if (threadIdx.x < 32) s_exp[threadIdx.x] = 0;
-    __syncthreads();
-    float k2 = 0.0f;
-    for (int i = threadIdx.x; i < nblk; i += 256) k2 = fmaxf(k2, knorm[(int64_t)b * nblk + i]);
-    // thread t takes group t % G of the blocks t / G, t / G + 256 / G, ...
-    const int g = threadIdx.x % G, step = 256 / G;
-    uint32_t m = 0;
-    for (int i = threadIdx.x / G; i < nblk; i += step) m = max(m, (uint32_t)kexp[((int64_t)b * nblk + i) * G + g]);
-    atomicMax(&s_exp[g], m);
+    const int b = blockIdx.x, g = blockIdx.y;
+    float m = 0.0f;
+    if (g == G) {
+        for (int i = threadIdx.x; i < nblk; i += 256) m = fmaxf(m, knorm[(int64_t)b * nblk + i]);
+    } else {
+        for (int i = threadIdx.x; i < nblk; i += 256) m = fmaxf(m, (float)kexp[((int64_t)b * nblk + i) * G + g]);
+    }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = k2;
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0) kseq_norm[b] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if (threadIdx.x < G) kseq_exp[(int64_t)b * G + threadIdx.x] = (uint8_t)s_exp[threadIdx.x];
+    if (threadIdx.x == 0) {
+        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        if (g == G) kseq_norm[b] = m;
+        else kseq_exp[(int64_t)b * G + g] = (uint8_t)m;
+    }
 }
 
 // Exact fp32 index score of (query row r, entry j): e4m3 products are exact in
@@ -683,14 +682,13 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
     constexpr int RB = KB * 128;
     __shared__ uint32_t s_key[kBandCap];   // sort keys minus the smallest; later the output bitmap
     __shared__ int32_t s_idx[kBandCap];    // entry index; bit 31 = selected
-    // the digit histogram is dead once T^ is known; the band list and its
-    // entries then reuse its words (80 KB in all: two workgroups per CU)
+    // the digit histogram is dead once T^ is known; the band list then reuses
+    // its words (80 KB in all: two workgroups per CU)
     __shared__ uint32_t s_hist[kBandHist];
-    static_assert(kBandHist >= 2 * kBandList, "band and bidx overlay the histogram");
+    static_assert(kBandHist >= kBandList, "the band list overlays the histogram");
     uint32_t* const hist = s_hist;
     uint32_t* const band = s_hist;                                        // positions of band entries
-    int32_t* const bidx = reinterpret_cast<int32_t*>(s_hist + kBandList);  // and their entries
-    __shared__ uint32_t bkey[kBandList];   // exact sort keys of the band (also the bin gather)
+    __shared__ uint32_t bkey[kBandList];   // keys of the bin that holds T^ (the bin gather)
     __shared__ uint32_t scan_lds[kBandThreads / 64 + 1];
     __shared__ uint32_t dig[2];
     __shared__ uint32_t s_oc[kBandRegBatch];  // per region of a batch: first candidate | count << 16
@@ -913,27 +911,61 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
     }
     const uint32_t need_b = (uint32_t)keff - nin;
     if (need_b > 0) {
-        // exact rescoring of the band, one wave per entry
-        const uint8_t* q = a.iq + r * RB;
-        for (uint32_t t = threadIdx.x >> 6; t < nband; t += kBandThreads / 64) {
-            const int32_t j = s_idx[band[t]];
-            const float sc = exact_score_fp8<KB>(q, a.ik + ((int64_t)b * a.N_cap + j) * RB);
-            if ((threadIdx.x & 63) == 0) {
-                bkey[t] = sort_key(sc);
-                bidx[t] = j;
+        uint64_t* const bcomp = reinterpret_cast<uint64_t*>(s_key);  // the band's exact keys
+        static_assert(kBandCap >= 2 * kBandList, "bcomp fits s_key");
+        // exact rescoring of the band, LPE lanes per entry: e4m3 products and all
+        // their partial sums are exact in fp64 (multiples of 2^-18 below 2^30), so
+        // the fp64 sum rounded once is the defined score
+        constexpr int LPE = 8, BPL = RB / LPE;
+        const int sub = threadIdx.x % LPE;
+        const uint8_t* qrow = a.iq + r * RB + sub * BPL;
+        for (uint32_t t0 = 0; t0 < nband; t0 += kBandThreads / LPE) {
+            const uint32_t t = t0 + threadIdx.x / LPE;
+            const bool live = t < nband;
+            const int32_t j = live ? s_idx[band[t]] : s_idx[band[0]];
+            const uint8_t* krow = a.ik + ((int64_t)b * a.N_cap + j) * RB + sub * BPL;
+            double acc = 0.0;
+#pragma unroll 1
+            for (int c = 0; c < BPL / 16; ++c) {
+                const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
+                const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + 16 * c);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const auto q0 = __builtin_amdgcn_cvt_pk_f32_fp8(qv[w], false), q1 = __builtin_amdgcn_cvt_pk_f32_fp8(qv[w], true);
+                    const auto k0 = __builtin_amdgcn_cvt_pk_f32_fp8(kv[w], false), k1 = __builtin_amdgcn_cvt_pk_f32_fp8(kv[w], true);
+                    acc = fma((double)q0[0], (double)k0[0], acc);
+                    acc = fma((double)q0[1], (double)k0[1], acc);
+                    acc = fma((double)q1[0], (double)k1[0], acc);
+                    acc = fma((double)q1[1], (double)k1[1], acc);
+                }
+            }
+#pragma unroll
+            for (int o = LPE / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+            if (live && sub == 0) {
+                // (exact score desc, index asc) as one 64-bit key, larger first; the
+                // candidate keys in s_key are no longer needed
+                const float sc = (float)acc;
+                bcomp[t] = ((uint64_t)sort_key(sc == 0.0f ? 0.0f : sc) << 32) | (uint32_t)~j;
             }
         }
         __syncthreads();
-        // rank in the band by (exact score desc, index asc); the first need_b are taken
-        for (uint32_t t = threadIdx.x; t < nband; t += kBandThreads) {
-            const uint32_t kt = bkey[t];
-            const int32_t jt = bidx[t];
+        // rank in the band: the entries ahead of t are those with a larger bcomp;
+        // the first need_b are taken.  Four lanes share each t (every fourth v),
+        // eight v per step so the LDS reads overlap.
+        const uint32_t part = threadIdx.x & 3;
+        for (uint32_t t0 = 0; t0 < nband; t0 += kBandThreads / 4) {
+            const uint32_t t = t0 + (threadIdx.x >> 2);
+            const uint64_t ct = t < nband ? bcomp[t] : ~0ull;
             uint32_t rank = 0;
-            for (uint32_t v = 0; v < nband; ++v) {
-                const uint32_t kv = bkey[v];
-                rank += (kv > kt || (kv == kt && bidx[v] < jt)) ? 1u : 0u;
+            uint32_t v = part;
+            for (; v + 28 < nband; v += 32) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) rank += bcomp[v + 4 * u] > ct ? 1u : 0u;
             }
-            if (rank < need_b) s_idx[band[t]] = jt | (int32_t)0x80000000;
+            for (; v < nband; v += 4) rank += bcomp[v] > ct ? 1u : 0u;
+            rank += __shfl_xor((int)rank, 1);
+            rank += __shfl_xor((int)rank, 2);
+            if (t < nband && part == 0 && rank < need_b) s_idx[band[t]] = (int32_t)~(uint32_t)ct | (int32_t)0x80000000;
         }
     }
     __syncthreads();
@@ -1045,8 +1077,8 @@ hipError_t launch_key_norm(const uint8_t* ik, int K, int B, int64_t N, int64_t N
         hipLaunchKernelGGL(key_norm_kernel<2>, grid, dim3(256), 0, stream, ik, N, N_cap, nblk, knorm, kexp);
     else
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(key_bound_kernel, dim3((unsigned)B), dim3(256), 0, stream, knorm, kexp, nblk, K / 8,
-                       kseq_norm, kseq_exp);
+    hipLaunchKernelGGL(key_bound_kernel, dim3((unsigned)B, (unsigned)(K / 8 + 1)), dim3(256), 0, stream, knorm, kexp,
+                       nblk, K / 8, kseq_norm, kseq_exp);
     return hipGetLastError();
 }
 
