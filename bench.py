@@ -428,16 +428,39 @@ def cpu_baseline(wl, inp, one_seqs=2, all_seqs=16, target_seconds=8.0, max_reps=
                       f"packing untimed ({t_setup:.1f}s)"}
 
 
+def prefill_section(device):
+    """The prefill chunk (one Full layer over 4,096 queries) timed with HIP events."""
+    from synth.workloads import ALL
+
+    pw = ALL[4]
+    chunk, index = run_prefill(pw, 10, 2, device)
+    flops = prefill_index_flops(pw)
+    idx_ms = float(np.mean(index))
+    return {
+        "workload": pw.name, "ms_per_chunk": round(float(np.mean(chunk)), 4),
+        "ms_per_chunk_pct": _summary(chunk),
+        "tokens_per_s": round(pw.Qs / (float(np.mean(chunk)) * 1e-3), 1),
+        "index_flops": flops,
+        "index_stage_us": round(idx_ms * 1e3, 2),
+        "index_stage_mfma_util": round(flops / (idx_ms * 1e-3) / (FP8_PEAK_TFLOPS * 1e12), 4),
+        "note": "index stage = sampled-threshold GEMM, key norms, threshold selection and the "
+                "MFMA filter GEMM (HIP events around them inside the chunk); mfma_util = useful "
+                "index flops / (index stage time x 5.0 PFLOP/s fp8)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=HEADLINE, choices=[1, 2, 3, 5])
+    ap.add_argument("--workload", type=int, default=HEADLINE, choices=[1, 2, 3, 5, 6, 7, 8],
+                    help="decode workload timed as the main line (the default is the headline stack)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-legs", action="store_true", help="headline workload only")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill chunk and print its section (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this implementation runs on one GPU; --gpus {args.gpus} is not supported "
@@ -454,6 +477,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.traffic_probe:
         traffic_probe(wl, device)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_section(device)}), flush=True)
         return
     r = run_decode(wl, args.steps, args.warmup, device)
     inp = r["state"][0]
@@ -483,7 +509,9 @@ def main():
         "step_hbm": {"algorithmic_bytes": ab["step"],
                      "GBps": round(ab["step"] / (ms * 1e-3) / 1e9, 1),
                      "frac": round(ab["step"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-        "roofline": {"kernel": "score_exact_kernel (exact index-score stream, inside the timed steps)",
+        "roofline": {"kernel": ("score_fp4_mfma_kernel (FP4-key index scores on the matrix cores, inside "
+                                "the timed steps)" if wl.idx_dtype == "fp4" else
+                                "score_exact_kernel (exact index-score stream, inside the timed steps)"),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic() if wl.wid == HEADLINE else None,
@@ -514,20 +542,7 @@ def main():
             torch.cuda.empty_cache()
         res["legs"] = legs
     if not args.no_prefill:
-        pw = ALL[4]
-        chunk, index = run_prefill(pw, 10, 2, device)
-        flops = prefill_index_flops(pw)
-        idx_ms = float(np.mean(index))
-        res["prefill"] = {
-            "workload": pw.name, "ms_per_chunk": round(float(np.mean(chunk)), 4),
-            "ms_per_chunk_pct": _summary(chunk),
-            "tokens_per_s": round(pw.Qs / (float(np.mean(chunk)) * 1e-3), 1),
-            "index_flops": flops,
-            "index_stage_us": round(idx_ms * 1e3, 2),
-            "index_stage_mfma_util": round(flops / (idx_ms * 1e-3) / (FP8_PEAK_TFLOPS * 1e12), 4),
-            "note": "index stage = sampled-threshold GEMM, key norms, threshold selection and the "
-                    "MFMA filter GEMM (HIP events around them inside the chunk); mfma_util = useful "
-                    "index flops / (index stage time x 5.0 PFLOP/s fp8)"}
+        res["prefill"] = prefill_section(device)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(res), flush=True)
