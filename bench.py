@@ -45,16 +45,19 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 HEADLINE = 5  # the 16-layer, batch-64 decode stack
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_exact_w5_hbm_traffic.md")
+TRAFFIC_SUMMARY = {5: os.path.join(ROOT, "profiles", "score_exact_w5_hbm_traffic.md"),
+                   7: os.path.join(ROOT, "profiles", "score_fp4_mfma_w7_hbm_traffic.md")}
 SCORE_SOURCE = os.path.join(ROOT, "compressed_kv_cache_03_amd", "csrc", "score.hip")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE, scaled by the copy
-    calibration) from the committed counter summary, or None when the summary is missing or was
+def measured_traffic(wid):
+    """HBM bytes per launch of the workload's dominant kernel (FETCH_SIZE + WRITE_SIZE, scaled by
+    the copy calibration) from the committed counter summary, or None when there is none or it was
     taken on another version of the kernel source."""
+    if wid not in TRAFFIC_SUMMARY:
+        return None
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(TRAFFIC_SUMMARY[wid]).read()
         src = hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()
     except OSError:
         return None
@@ -514,7 +517,7 @@ def main():
                                 "score_exact_kernel (exact index-score stream, inside the timed steps)"),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic() if wl.wid == HEADLINE else None,
+                     "traffic": measured_traffic(wl.wid),
                      "bytes_per_launch": ab["score_launch"], "score_spill_bytes_per_launch": ab["score_spill"],
                      "launches": len(r["score_ms"]), "avg_launch_us": round(score_us, 2),
                      "launch_us_pct": _summary([x * 1e3 for x in r["score_ms"]])},
