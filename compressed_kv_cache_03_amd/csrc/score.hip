@@ -9,9 +9,11 @@
 //
 //   * 8 lanes share one entry; each lane loads 16-byte chunks at byte offset
 //     c*128 + lane8*16, so one wave instruction reads eight 128-byte segments;
-//   * every lane keeps its slice of the index query in registers as fp64;
-//   * products of two bf16 (or two fp8) values are exact in fp64 and are summed
-//     with fp64 FMAs; a 3-step swizzle butterfly finishes each entry.
+//   * every lane keeps its slice of the index query in registers (fp64; bf16
+//     queries as fp32);
+//   * products of two fp8 values are exact in fp64 and are summed with fp64
+//     FMAs; products of two bf16 values (16 significant bits) are formed exactly
+//     in fp32 and summed in fp64; a 3-step swizzle butterfly finishes each entry.
 //
 // Exactness:
 //   * e4m3: every product is a multiple of 2^-18 of magnitude < 2^17.6, so any
@@ -22,16 +24,18 @@
 //     exact sum lands exactly on an fp32 rounding midpoint surprisingly often
 //     (about 2% of N(0,1) scores); correctness therefore rests on proving the
 //     fp64 sum exact rather than merely close.  Every product is a multiple of
-//     2^L with L = lsb(min|q|) + lsb(min|k|) (bf16 value = M * 2^(E-134)), so if
+//     2^L with L = lsb(min|q|) + lsb(min|k|) (bf16 value = M * 2^(E-134)); with
+//     L >= -149 and every |p| below 2^128 each fp32 product is exact.  If
 //     sum|p| < 2^(L+53) every partial sum, in any order, is representable and
 //     the fp64 result is the exact sum: rounding it once is the answer, ties
-//     included.  The kernel tracks sum|p| (one extra fp64 FMA per element) and
-//     the smallest exponent field of k (a packed 16-bit minimum per two
-//     elements) per entry.  When that proof fails it falls back to an interval
-//     certificate (error <= gamma_(K-1) sum|p| for any order; both ends of
-//     [s - bound, s + bound] must round to the same fp32), and when both fail
-//     (a tie together with a > 53-bit exponent spread) the entry is recomputed
-//     with an integer long accumulator.
+//     included.  sum|p| is bounded by sum|q| * max|k|: the kernel tracks the
+//     smallest and the largest exponent field of k (packed 16-bit minimum and
+//     maximum per two elements) per entry.  When that proof fails it falls
+//     back to an interval certificate (error <= gamma_(K-1) sum|p| for any
+//     order; both ends of [s - bound, s + bound] must round to the same fp32),
+//     and when both fail (a tie together with a > 53-bit exponent spread), or a
+//     product may leave fp32's range, the entry is recomputed with an integer
+//     long accumulator.
 //   * FP4 keys (e2m1 code times an fp32 scale per 32-element block, bf16
 //     queries): each lane sums its block's 32 products q * e2m1 in fp64, exact
 //     whenever the query block's exponent spread allows (a per-row property
@@ -61,6 +65,11 @@ constexpr int kScoreChunks = 1;                                   // passes per 
 constexpr int kScoreEntriesPerBlock = kScoreChunks * kScoreEntriesPerChunk;  // 512
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+CSA2_DEV uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
 
 // Per-half minimum of two packed 16-bit fields.
 CSA2_DEV uint32_t pk_min_u16(uint32_t a, uint32_t b) {
@@ -343,8 +352,9 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 3, sub = lane & 7;
 
-    // this lane's slice of the index query, as fp64
-    double qd[CPL * EPC];
+    // this lane's slice of the index query, as fp64 (bf16: as fp32, exact)
+    double qd[DT == 0 ? 1 : CPL * EPC];
+    float qf[DT == 0 ? CPL * EPC : 1];
     double berr[DT == 2 ? CPL : 1];  // FP4 keys: error bound of each chunk's block sum
     constexpr double kBlkRound = (CPL + 3) * 0x1p-53 * 1.001;
     if constexpr (DT == 2) {
@@ -374,9 +384,9 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
             const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + c * 128 + sub * 16);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                if (DT == 0) {
-                    qd[c * EPC + 2 * t] = bf16_lo(w[t]);
-                    qd[c * EPC + 2 * t + 1] = bf16_hi(w[t]);
+                if constexpr (DT == 0) {
+                    qf[c * EPC + 2 * t] = bf16_lo(w[t]);
+                    qf[c * EPC + 2 * t + 1] = bf16_hi(w[t]);
                 } else {
                     const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[t], false);
                     const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[t], true);
@@ -393,15 +403,28 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
     const double bound_scale = (double)a.K * 0x1p-53 * 1.001 * (1.0 + (double)a.K * 0x1p-52);
     // least significant bit exponent of the smallest |q| of the row (bf16 values are
     // M * 2^(E-134) with integer M; a zero or subnormal gives the floor E = 1)
-    int lq = 0;
-    if (DT == 0) {
-        float qmin = INFINITY;
+    int lq = 0, eqmax = 0;
+    double qabs = 0.0;  // sum |q| over the row, rounded up
+    if constexpr (DT == 0) {
+        float qmin = INFINITY, qmax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < CPL * EPC; ++i) qmin = fminf(qmin, fabsf((float)qd[i]));
+        for (int i = 0; i < CPL * EPC; ++i) {
+            qmin = fminf(qmin, fabsf(qf[i]));
+            qmax = fmaxf(qmax, fabsf(qf[i]));
+            qabs += (double)fabsf(qf[i]);
+        }
         qmin = fminf(qmin, swz_xor<1>(qmin));
         qmin = fminf(qmin, swz_xor<2>(qmin));
         qmin = fminf(qmin, swz_xor<4>(qmin));
+        qmax = fmaxf(qmax, swz_xor<1>(qmax));
+        qmax = fmaxf(qmax, swz_xor<2>(qmax));
+        qmax = fmaxf(qmax, swz_xor<4>(qmax));
+        qabs += swz_xor<1>(qabs);
+        qabs += swz_xor<2>(qabs);
+        qabs += swz_xor<4>(qabs);
+        qabs *= 1.0 + 0x1p-40;
         lq = bf16_lsb_exp(qmin);
+        eqmax = (int)(__float_as_uint(qmax) >> 23);
     }
 
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.ik) + b * a.N_cap * (int64_t)EB;
@@ -411,12 +434,13 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
         const int64_t e_wave = e_block + chunk * kScoreEntriesPerChunk + wave * kScoreEntriesPerWave;
         if (e_wave >= nv) break;  // wave-uniform
         double keep = 0.0, keep_abs = 0.0;
-        uint32_t keep_ex = 0;
+        uint32_t keep_ex = 0, keep_mx = 0;
         // one round: 8 entries, 8 lanes each; lane sub == t keeps entry e_wave + 8t + g
         auto round_body = [&](int t, const u32x4(&w)[CPL], const float(&ksc)[DT == 2 ? CPL : 1])
                               __attribute__((always_inline)) {
             double acc = 0.0, aacc = 0.0;  // FP4 keys: aacc is the error bound of acc
             uint32_t kex = 0x7fff7fffu;  // packed minimum of the two bf16 exponent fields
+            uint32_t kmx = 0u;           // and their packed maximum
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
                 if constexpr (DT == 2) {
@@ -449,14 +473,15 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    if (DT == 0) {
-                        const double lo = bf16_lo(w[c][u]), hi = bf16_hi(w[c][u]);
-                        const double q0 = qd[c * EPC + 2 * u], q1 = qd[c * EPC + 2 * u + 1];
-                        acc = fma(q0, lo, acc);
-                        aacc = fma(fabs(q0), fabs(lo), aacc);
-                        acc = fma(q1, hi, acc);
-                        aacc = fma(fabs(q1), fabs(hi), aacc);
+                    if constexpr (DT == 0) {
+                        // bf16 x bf16 products are exact in fp32 when no product
+                        // leaves fp32's range (checked per entry below)
+                        const float p0 = qf[c * EPC + 2 * u] * bf16_lo(w[c][u]);
+                        const float p1 = qf[c * EPC + 2 * u + 1] * bf16_hi(w[c][u]);
+                        acc += (double)p0;
+                        acc += (double)p1;
                         kex = pk_min_u16(kex, w[c][u] & 0x7f807f80u);
+                        kmx = pk_max_u16(kmx, w[c][u] & 0x7f807f80u);
                     } else {
                         const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[c][u], false);
                         const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[c][u], true);
@@ -470,7 +495,7 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
             acc += swz_xor<1>(acc);
             acc += swz_xor<2>(acc);
             acc += swz_xor<4>(acc);
-            if (DT != 1) {
+            if (DT == 2) {
                 aacc += swz_xor<1>(aacc);
                 aacc += swz_xor<2>(aacc);
                 aacc += swz_xor<4>(aacc);
@@ -479,31 +504,39 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
                 kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (1 << 10) | 0x1f));
                 kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (2 << 10) | 0x1f));
                 kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (4 << 10) | 0x1f));
+                kmx = pk_max_u16(kmx, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kmx, (1 << 10) | 0x1f));
+                kmx = pk_max_u16(kmx, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kmx, (2 << 10) | 0x1f));
+                kmx = pk_max_u16(kmx, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kmx, (4 << 10) | 0x1f));
             }
             if (sub == t) {
                 keep = acc;
                 keep_abs = aacc;
                 keep_ex = kex;
+                keep_mx = kmx;
             }
         };
-        if constexpr (DT == 2) {
-            // FP4 rows are short (128 bytes per 256 elements): keys are loaded kPD
-            // rounds ahead of their use from a ring of kPD + 1 round buffers, so
-            // enough bytes are in flight per wave.  Entries past nv load entry
+        {
+            // keys are loaded kPD rounds ahead of their use from a ring of kPD + 1
+            // round buffers, so enough bytes are in flight per wave (FP4 and e4m3
+            // rows are short: 128 and 256 bytes).  Entries past nv load entry
             // nv - 1 (in bounds) and are never stored.
-            constexpr int kPD = 2;
+            constexpr int kPD = DT == 1 ? 3 : (DT == 0 && CPL >= 8) ? 1 : 2;
             u32x4 wr[kPD + 1][CPL];
-            float kr[kPD + 1][CPL];
-            auto load_round = [&](int t, u32x4(&w)[CPL], float(&ks)[CPL]) __attribute__((always_inline)) {
+            float kr[kPD + 1][DT == 2 ? CPL : 1];
+            auto load_round = [&](int t, u32x4(&w)[CPL], float(&ks)[DT == 2 ? CPL : 1]) __attribute__((always_inline)) {
                 int64_t e = e_wave + t * 8 + g;
                 e = e < nv ? e : nv - 1;
                 const int64_t pe = POOL ? slot_entry(a, r, e) : e;
                 const uint8_t* src = kbase + pe * EB + sub * 16;
-                const float* sp = a.ik_scales + (b * a.N_cap + pe) * (int64_t)(a.K / 32) + sub;
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) {
+                for (int c = 0; c < CPL; ++c)
                     w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
-                    ks[c] = __builtin_nontemporal_load(sp + 8 * c);
+                if constexpr (DT == 2) {
+                    const float* sp = a.ik_scales + (b * a.N_cap + pe) * (int64_t)(a.K / 32) + sub;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) ks[c] = __builtin_nontemporal_load(sp + 8 * c);
+                } else {
+                    ks[0] = 0.0f;
                 }
             };
 #pragma unroll
@@ -512,23 +545,6 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
             for (int t = 0; t < kScoreRounds; ++t) {
                 if (t + kPD < kScoreRounds) load_round(t + kPD, wr[(t + kPD) % (kPD + 1)], kr[(t + kPD) % (kPD + 1)]);
                 round_body(t, wr[t % (kPD + 1)], kr[t % (kPD + 1)]);
-            }
-        } else {
-#pragma unroll 2
-            for (int t = 0; t < kScoreRounds; ++t) {
-                const int64_t e = e_wave + t * 8 + g;
-                u32x4 w[CPL];
-                const float ksc[1] = {0.0f};
-                if (e < nv) {
-                    const uint8_t* src = kbase + (POOL ? slot_entry(a, r, e) : e) * EB + sub * 16;
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c)
-                        w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
-                } else {
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) w[c] = u32x4{0u, 0u, 0u, 0u};
-                }
-                round_body(t, w, ksc);
             }
         }
 
@@ -539,11 +555,20 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
         if (e < nv) {
             if (DT == 0) {
                 res = (float)keep;
-                // smallest exponent field among the entry's elements (0 = zero or subnormal)
+                // smallest and largest exponent field among the entry's elements
+                // (0 = zero or subnormal)
                 const uint32_t ex = min(keep_ex & 0xffffu, keep_ex >> 16) >> 7;
+                const uint32_t emx = max(keep_mx & 0xffffu, keep_mx >> 16) >> 7;
                 const int lk = (int)(ex > 0 ? ex : 1u) - 134;
-                if (!sum_is_exact(keep_abs, lq + lk)) {
-                    const double eb = bound_scale * keep_abs + fabs(keep) * 0x1p-52;
+                // every product a multiple of 2^(lq+lk) >= 2^-149 and below
+                // 2^(eqmax+emx-252) <= 2^127: each fp32 product was exact
+                const bool prod_exact = lq + lk >= -149 && eqmax + (int)emx <= 379 && eqmax < 255 && emx < 255;
+                // sum |p| <= sum |q| * max |k| < qabs * 2^(emx - 126)
+                const double sabs = qabs * ldexp(1.0, (int)(emx > 0 ? emx : 1u) - 126);
+                if (!prod_exact) {
+                    ok = false;
+                } else if (!sum_is_exact(sabs, lq + lk)) {
+                    const double eb = bound_scale * sabs + fabs(keep) * 0x1p-52;
                     const float lo = (float)(keep - eb), hi = (float)(keep + eb);
                     ok = __float_as_uint(lo) == __float_as_uint(hi);
                     res = lo;
