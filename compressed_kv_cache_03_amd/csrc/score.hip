@@ -25,10 +25,11 @@
 //     (about 2% of N(0,1) scores); correctness therefore rests on proving the
 //     fp64 sum exact rather than merely close.  Every product is a multiple of
 //     2^L with L = lsb(min|q|) + lsb(min|k|) (bf16 value = M * 2^(E-134)); with
-//     L >= -149 and every |p| below 2^128 each fp32 product is exact.  If
-//     sum|p| < 2^(L+53) every partial sum, in any order, is representable and
-//     the fp64 result is the exact sum: rounding it once is the answer, ties
-//     included.  sum|p| is bounded by sum|q| * max|k|: the kernel tracks the
+//     L >= -149 and every |p| below 2^128 each fp32 product is exact (with
+//     L < -149 each is within 2^-150 of exact, which the interval below
+//     absorbs).  If sum|p| < 2^(L+53) every partial sum, in any order, is
+//     representable and the fp64 result is the exact sum: rounding it once is
+//     the answer, ties included.  sum|p| is bounded by sum|q| * max|k|: the kernel tracks the
 //     smallest and the largest exponent field of k (packed 16-bit minimum and
 //     maximum per two elements) per entry.  When that proof fails it falls
 //     back to an interval certificate (error <= gamma_(K-1) sum|p| for any
@@ -560,15 +561,19 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
                 const uint32_t ex = min(keep_ex & 0xffffu, keep_ex >> 16) >> 7;
                 const uint32_t emx = max(keep_mx & 0xffffu, keep_mx >> 16) >> 7;
                 const int lk = (int)(ex > 0 ? ex : 1u) - 134;
-                // every product a multiple of 2^(lq+lk) >= 2^-149 and below
-                // 2^(eqmax+emx-252) <= 2^127: each fp32 product was exact
-                const bool prod_exact = lq + lk >= -149 && eqmax + (int)emx <= 379 && eqmax < 255 && emx < 255;
+                // every |p| below 2^(eqmax+emx-252) <= 2^127: no fp32 product
+                // overflowed; every product a multiple of 2^(lq+lk) >= 2^-149 (zero
+                // elements count as the smallest): none was rounded either,
+                // otherwise each is within 2^-150 of its exact value
+                const bool in_range = eqmax + (int)emx <= 379 && eqmax < 255 && emx < 255;
+                const bool prod_exact = lq + lk >= -149;
                 // sum |p| <= sum |q| * max |k| < qabs * 2^(emx - 126)
                 const double sabs = qabs * ldexp(1.0, (int)(emx > 0 ? emx : 1u) - 126);
-                if (!prod_exact) {
+                if (!in_range) {
                     ok = false;
-                } else if (!sum_is_exact(sabs, lq + lk)) {
-                    const double eb = bound_scale * sabs + fabs(keep) * 0x1p-52;
+                } else if (!prod_exact || !sum_is_exact(sabs, lq + lk)) {
+                    const double eb = bound_scale * sabs + fabs(keep) * 0x1p-52 +
+                                      (prod_exact ? 0.0 : (double)a.K * 0x1p-149);
                     const float lo = (float)(keep - eb), hi = (float)(keep + eb);
                     ok = __float_as_uint(lo) == __float_as_uint(hi);
                     res = lo;

@@ -135,6 +135,27 @@ def test_index_score_bf16_rounding_ties_take_exact_path():
     assert bits_eq(host(got), oracle.index_score("bf16", iq, ik))
 
 
+@pytest.mark.parametrize("qexp,kexp,zeros", [(0, 0, False), (-70, -70, False), (-60, -62, True),
+                                             (60, 66, False), (-20, 40, True)])
+def test_index_score_bf16_products_at_the_fp32_range(qexp, kexp, zeros):
+    # bf16 x bf16 products are formed in fp32: scaled so that products underflow
+    # into fp32's subnormal range (-70, -70; -60, -62), overflow it (60, 66), or
+    # stay inside it; zero query and key elements widen the bound on the smallest
+    # product.  K = 256 (the decode shape), several workgroups and a ragged tail.
+    rng = np.random.default_rng(2024 + qexp)
+    B, N, H, d = 2, 1500, 4, 64
+    q = rng.standard_normal((B, 1, H, d)) * 2.0 ** qexp
+    k = rng.standard_normal((B, N, H, d)) * 2.0 ** kexp
+    if zeros:
+        q[:, :, 0, :5] = 0.0
+        k[:, ::3, 1, 7] = 0.0
+    iq = synth.to_bf16_bits(q.astype(np.float32))
+    ik = synth.to_bf16_bits(k.astype(np.float32))
+    got = csa2.index_score(dev(iq), dev(ik), "bf16")
+    torch.cuda.synchronize()
+    assert bits_eq(host(got), oracle.index_score("bf16", iq, ik))
+
+
 def _fp4_key_case(rng, B, N, H, d):
     # wide-exponent bf16 queries; every code byte; block scales over many binades
     K = H * d
