@@ -74,10 +74,6 @@ bool rows_scorer(const csa2_group* g, int Qs) {
     return Qs >= 2 && g->idx_dtype == CSA2_IDX_BF16 && (K == 128 || K == 256);
 }
 
-// FP4 keys with K = 256 score on the matrix cores, which queue the entries
-// their certificate leaves undecided (score.hip) for a second kernel.
-bool fp4_queue(const csa2_group* g) { return g->idx_dtype == CSA2_IDX_FP4_E2M1 && g->H_I * g->d_I == 256; }
-
 int64_t pool_slots(const csa2_group* g) { return (int64_t)g->pool_blocks * CSA2_POOL_BLOCK; }
 int64_t block_count(int64_t N) { return (N + CSA2_POOL_BLOCK - 1) / CSA2_POOL_BLOCK; }
 
@@ -158,7 +154,7 @@ Layout layer_layout(const csa2_group* g, int Qs, int Hq, int W) {
             if (n > 0) slices = std::max(slices, (n + topk_slice_len(n) - 1) / topk_slice_len(n));
         add_topk(L, off, TopkShape{R, L.ld_scores, slices});
         L.rows_scorer = rows_scorer(g, Qs);
-        if (L.rows_scorer || fp4_queue(g)) {
+        if (L.rows_scorer) {
             L.fix_list = off;
             off = align_up(off + (size_t)R * N * 8);
         }
@@ -664,7 +660,7 @@ csa2_status csa2_layer_step(csa2_mode mode, const csa2_layer_args* a, csa2_group
         sa.scores = scores;
         sa.ld = L.ld_scores;
         sa.hist = t.hist;
-        if (L.rows_scorer || (fp4_queue(g) && !in_pool)) {
+        if (L.rows_scorer) {
             sa.fix_cnt = t.hist + R * kHistBinsHost;
             sa.fix_list = at<uint2>(ws, L.fix_list);
         }

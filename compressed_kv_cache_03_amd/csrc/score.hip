@@ -848,9 +848,39 @@ __global__ __launch_bounds__(kScoreThreads) void score_fixup_kernel(ScoreArgs a)
 // Score of (row r, position pe) computed by one thread with the arithmetic and
 // certification of the streaming kernel: false when the certificate cannot
 // decide (then *out is not the score).
+// FP4 keys, one thread: per 32-element block an fp64 sum of q * e2m1 with its
+// error bound, then one fma with the block scale; the bound covers every
+// rounding.  false when it does not decide the fp32 rounding.
+CSA2_DEV bool fp4_entry_certified(const uint16_t* q, const uint8_t* k, const float* sc, int K, float* out) {
+    double acc = 0.0, aacc = 0.0;
+    for (int blk0 = 0; blk0 < K; blk0 += 32) {
+        double blk = 0.0, qn1 = 0.0;
+        int emin = 1 << 20;
+        for (int i = blk0; i < blk0 + 32; ++i) {
+            const uint32_t nib = (k[i >> 1] >> (4 * (i & 1))) & 15u;
+            const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, 1.0f, 0);
+            const double qv = (double)bf16_to_f32(q[i]);
+            blk = fma(qv, (double)v[0], blk);
+            qn1 += fabs(qv);
+            emin = min(emin, bf16_pair_emin(q[i]));
+        }
+        const double sd = (double)sc[blk0 >> 5];
+        acc = fma(blk, sd, acc);
+        aacc = fma(fma((double)(K / 32) * 0x1p-53 * 1.001, fabs(blk), fp4_block_err(qn1, emin)), fabs(sd), aacc);
+    }
+    const double eb = (aacc + fabs(acc) * 0x1p-52) * (1.0 + 0x1p-40);
+    const float lo = (float)(acc - eb), hi = (float)(acc + eb);
+    *out = lo;
+    return __float_as_uint(lo) == __float_as_uint(hi);
+}
+
 CSA2_DEV bool generic_entry_certified(const ScoreArgs& a, int64_t r, int64_t pe, float* out) {
     const int64_t b = r / a.Qs;
     const int K = a.K;
+    if (a.dtype == 2)
+        return fp4_entry_certified(reinterpret_cast<const uint16_t*>(a.iq) + r * K,
+                                   reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + pe) * (K / 2),
+                                   a.ik_scales + (b * a.N_cap + pe) * (K / 32), K, out);
     double acc = 0.0, aacc = 0.0;
     float qmin = INFINITY, kmin = INFINITY;
     if (a.dtype == 0) {
@@ -862,27 +892,6 @@ CSA2_DEV bool generic_entry_certified(const ScoreArgs& a, int64_t r, int64_t pe,
             aacc = fma(fabs((double)qf), fabs((double)kf), aacc);
             qmin = fminf(qmin, fabsf(qf));
             kmin = fminf(kmin, fabsf(kf));
-        }
-    } else if (a.dtype == 2) {
-        // FP4 keys: per 32-element block an fp64 sum of q * e2m1 with its error
-        // bound, then one fma with the block scale; aacc bounds every rounding
-        const uint16_t* q = reinterpret_cast<const uint16_t*>(a.iq) + r * K;
-        const uint8_t* k = reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + pe) * (K / 2);
-        const float* sc = a.ik_scales + (b * a.N_cap + pe) * (K / 32);
-        for (int blk0 = 0; blk0 < K; blk0 += 32) {
-            double blk = 0.0, qn1 = 0.0;
-            int emin = 1 << 20;
-            for (int i = blk0; i < blk0 + 32; ++i) {
-                const uint32_t nib = (k[i >> 1] >> (4 * (i & 1))) & 15u;
-                const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, 1.0f, 0);
-                const double qv = (double)bf16_to_f32(q[i]);
-                blk = fma(qv, (double)v[0], blk);
-                qn1 += fabs(qv);
-                emin = min(emin, bf16_pair_emin(q[i]));
-            }
-            const double sd = (double)sc[blk0 >> 5];
-            acc = fma(blk, sd, acc);
-            aacc = fma(fma((double)(K / 32) * 0x1p-53 * 1.001, fabs(blk), fp4_block_err(qn1, emin)), fabs(sd), aacc);
         }
     } else {
         const uint8_t* q = reinterpret_cast<const uint8_t*>(a.iq) + r * K;
@@ -900,11 +909,6 @@ CSA2_DEV bool generic_entry_certified(const ScoreArgs& a, int64_t r, int64_t pe,
             ok = __float_as_uint(lo) == __float_as_uint(hi);
             res = lo;
         }
-    } else if (a.dtype == 2) {
-        const double eb = (aacc + fabs(acc) * 0x1p-52) * (1.0 + 0x1p-40);
-        const float lo = (float)(acc - eb), hi = (float)(acc + eb);
-        ok = __float_as_uint(lo) == __float_as_uint(hi);
-        res = lo;
     } else {
         res = (float)acc;
     }
@@ -969,12 +973,6 @@ constexpr int kF4Ahead = 1;                                       // rounds of k
 constexpr int kF4MinWaves = 4;                                    // waves per SIMD (launch bound)
 constexpr int kF4EntriesPerBlock = (kF4Threads / 64) * 64 * kF4Rounds;  // 512
 constexpr uint32_t kF4EmaxLo = 64, kF4EmaxHi = 220;  // block exponent fields kept on the MFMA path
-// NaN bit patterns never produced for finite inputs, left in the scores by
-// score_fp4_mfma_kernel for score_fp4_fixup_kernel, which always overwrites them:
-// an entry the certificate could not decide, and an entry of a row outside the
-// bands.  The fixup's rarely taken paths need many registers; kept out of the
-// streaming kernel they leave it room for more waves in flight.
-constexpr uint32_t kF4Undecided = 0x7fc5a2fdu, kF4Outside = 0x7fc5a2feu;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -1093,32 +1091,39 @@ CSA2_DEV void f4_tile(const F4Round& d, int t, uint8_t* wb, u32x4 (&kc)[2], f32x
     __builtin_amdgcn_wave_barrier();
 }
 
-
-// Where the scores of the lanes with `mine` set are left for the fixup: with a
-// queue (a.fix_list) their (row, entry | flag) items are appended, one atomic
-// per wave; without one the score gets the marker.
-CSA2_DEV void f4_defer(const ScoreArgs& a, bool mine, int64_t r, int64_t e, bool outside) {
-    const uint64_t m = __ballot(mine);
-    if (m == 0) return;
-    if (a.fix_list) {
-        const int lane = threadIdx.x & 63, first = __builtin_ctzll(m);
-        uint32_t base = 0;
-        if (lane == first) base = atomicAdd(a.fix_cnt, (uint32_t)__builtin_popcountll(m));
-        base = (uint32_t)__shfl((int)base, first);
-        if (mine) {
-            const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            a.fix_list[base + rank] = uint2{(uint32_t)r, (uint32_t)e | (outside ? 0x80000000u : 0u)};
-        }
-    } else if (mine) {
-        a.scores[r * a.ld + e] = __uint_as_float(outside ? kF4Outside : kF4Undecided);
-    }
+// The rare paths of score_fp4_mfma_kernel, out of line so that the registers
+// they need are not reserved in the streaming code; arguments are plain
+// pointers (a struct passed by reference would be copied to scratch per lane).
+// Exact score of an entry by the whole wave (q: the row's 256 bf16 values, k and
+// sc: the entry's codes and scales).
+static __device__ __attribute__((noinline)) float f4_wave_exact_ool(const uint16_t* q, const uint8_t* k, const float* sc,
+                                                                int lane) {
+    return wave_exact_fp4_256(q, k, sc, lane);
+}
+// fp4_entry_certified for K = 256, one thread.
+static __device__ __attribute__((noinline)) bool f4_entry_certified_ool(const uint16_t* q, const uint8_t* k, const float* sc,
+                                                                    float* out) {
+    return fp4_entry_certified(q, k, sc, 256, out);
+}
+CSA2_DEV float f4_wave_exact(const ScoreArgs& a, int64_t r, int64_t e, int lane) {
+    const int64_t b = r / a.Qs;
+    return f4_wave_exact_ool(reinterpret_cast<const uint16_t*>(a.iq) + r * 256,
+                             reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * 128,
+                             a.ik_scales + (b * a.N_cap + e) * 8, lane);
+}
+CSA2_DEV bool f4_entry_certified(const ScoreArgs& a, int64_t r, int64_t e, float* out) {
+    const int64_t b = r / a.Qs;
+    return f4_entry_certified_ool(reinterpret_cast<const uint16_t*>(a.iq) + r * 256,
+                                  reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * 128,
+                                  a.ik_scales + (b * a.N_cap + e) * 8, out);
 }
 
 // The wave's rounds: e_block + (NW i + wave) * 64 for i < kF4Rounds.  Keys are
 // loaded kF4Ahead rounds ahead into a ring of round buffers (the caller has
 // issued the first ones); the loop is unrolled so the ring index is static.
-// Entries the certificate cannot decide are deferred (f4_defer) with no histogram
-// count.
+// Entries the certificate cannot decide get a checked recompute, and what that
+// leaves open the exact integer sum, both in place; every score is counted in
+// the LDS histogram.
 template <int NB>
 CSA2_DEV void fp4_mfma_rows(const ScoreArgs& a, int64_t r, int64_t e_block, int64_t nv, const uint32_t (*s_afr)[2][64][8],
                             const uint32_t (*s_scl)[2][64], uint32_t* lhist, F4Round (&ring)[kF4Ahead + 1],
@@ -1214,17 +1219,26 @@ CSA2_DEV void fp4_mfma_rows(const ScoreArgs& a, int64_t r, int64_t e_block, int6
                 res = (float)sw;
             }
         }
-        if (e < nv && decided) {
+        // rarer still: what the check leaves undecided is computed exactly by the
+        // whole wave, one entry at a time (one round per wave: no keys in flight)
+        uint64_t pend = __ballot(e < nv && !decided);
+        while (pend) {
+            const int L = __builtin_ctzll(pend);
+            pend &= pend - 1;
+            const float x = f4_wave_exact(a, r, e_round + L, lane);
+            if (lane == L) res = x;
+        }
+        if (e < nv) {
             a.scores[r * a.ld + e] = res;
             if (lhist) atomicAdd(&lhist[sort_key(res) >> (32 - kHistBits)], 1u);
         }
-        f4_defer(a, e < nv && !decided, r, e, false);
     }
 }
 
 __global__ __launch_bounds__(kF4Threads, kF4MinWaves) void score_fp4_mfma_kernel(ScoreArgs a) {
     constexpr int NW = kF4Threads / 64;
     static_assert(kF4Threads >= 256, "one thread per query element");
+    static_assert(kF4Rounds * kF4Threads == kF4EntriesPerBlock, "one entry per thread outside the bands");
     int64_t r, e_block;
     {
         // tiles are counted in 32 bits (fewer than 2^31 by the launch checks)
@@ -1289,11 +1303,22 @@ __global__ __launch_bounds__(kF4Threads, kF4MinWaves) void score_fp4_mfma_kernel
     uint32_t* const lh = with_hist ? lhist : nullptr;
 
     if (NB == 0) {
-        // outside the bands: the fixup scores the block
-#pragma unroll 1
-        for (int i = 0; i < kF4Rounds; ++i) {
-            const int64_t e = e_block + i * kF4Threads + tid;
-            f4_defer(a, e < nv, r, e, true);
+        // outside the bands: one entry per thread in fp64 with its error bound
+        // (generic_entry_certified), what that leaves undecided exactly by the
+        // whole wave
+        const int64_t e = e_block + tid;
+        float res = 0.0f;
+        const bool ok = e < nv && f4_entry_certified(a, r, e, &res);
+        uint64_t pend = __ballot(e < nv && !ok);
+        while (pend) {
+            const int L = __builtin_ctzll(pend);
+            pend &= pend - 1;
+            const float x = f4_wave_exact(a, r, e_block + 64 * wave + L, lane);
+            if (lane == L) res = x;
+        }
+        if (e < nv) {
+            a.scores[r * a.ld + e] = res;
+            if (lh) atomicAdd(&lh[sort_key(res) >> (32 - kHistBits)], 1u);
         }
     } else {
         if (tid < 256) {
@@ -1385,63 +1410,7 @@ CSA2_DEV bool wave_certified_fp4(const ScoreArgs& a, int64_t r, int64_t e, int l
     return __float_as_uint(lo) == __float_as_uint(hi);
 }
 
-// Scores the items score_fp4_mfma_kernel queued (a.fix_list), one per wave:
-// entries of rows outside the bands (flag bit 31) first in fp64
-// (wave_certified_fp4), then, like the undecided entries, exactly with the
-// integer accumulator.
-__global__ __launch_bounds__(256) void score_fp4_list_kernel(ScoreArgs a) {
-    const uint32_t n = *a.fix_cnt;
-    const int lane = threadIdx.x & 63;
-    const uint32_t wid = blockIdx.x * 4 + (threadIdx.x >> 6), nw = gridDim.x * 4;
-#pragma unroll 1
-    for (uint32_t i = wid; i < n; i += nw) {
-        const uint2 it = a.fix_list[i];
-        const int64_t r = it.x, e = it.y & 0x7fffffffu, b = r / a.Qs;
-        float res = 0.0f;
-        const bool ok = (it.y >> 31) != 0 && wave_certified_fp4(a, r, e, lane, &res);
-        if (!ok)
-            res = wave_exact_fp4_256(reinterpret_cast<const uint16_t*>(a.iq) + r * 256,
-                                     reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * 128,
-                                     a.ik_scales + (b * a.N_cap + e) * 8, lane);
-        if (lane == 0) {
-            a.scores[r * a.ld + e] = res;
-            if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
-        }
-    }
-}
 
-// Scores the entries score_fp4_mfma_kernel left marked.  kF4Outside: one thread
-// per entry with the streaming kernel's fp64 arithmetic and certificate;
-// kF4Undecided, and what that leaves undecided, are computed exactly by the
-// whole wave at once.  Each thread checks four entries of its row.
-__global__ __launch_bounds__(256) void score_fp4_fixup_kernel(ScoreArgs a) {
-    const int64_t r = blockIdx.y, b = r / a.Qs;
-    const int64_t nv = row_valid(a, r);
-    const int lane = threadIdx.x & 63;
-#pragma unroll 1
-    for (int j = 0; j < 4; ++j) {
-        const int64_t e = (int64_t)blockIdx.x * 1024 + j * 256 + threadIdx.x;
-        const uint32_t m = e < nv ? __float_as_uint(a.scores[r * a.ld + e]) : 0u;
-        const bool outside = m == kF4Outside, marked = outside || m == kF4Undecided;
-        if (__ballot(marked) == 0) continue;
-        float res = 0.0f;
-        const bool ok = outside && generic_entry_certified(a, r, e, &res);
-        uint64_t pend = __ballot(marked && !ok);
-        while (pend) {
-            const int L = __builtin_ctzll(pend);
-            pend &= pend - 1;
-            const int64_t eL = __builtin_amdgcn_readlane((int)e, L);
-            const float x = wave_exact_fp4_256(reinterpret_cast<const uint16_t*>(a.iq) + r * 256,
-                                               reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + eL) * 128,
-                                               a.ik_scales + (b * a.N_cap + eL) * 8, lane);
-            if (lane == L) res = x;
-        }
-        if (marked) {
-            a.scores[r * a.ld + e] = res;
-            if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
-        }
-    }
-}
 
 
 // Which scoring kernel a call takes, with its tiling (n_eblk, blocks, per_xcd
@@ -1534,11 +1503,6 @@ hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
         hipLaunchKernelGGL(score_fixup_kernel, dim3(256), dim3(kScoreThreads), 0, stream, a);
     } else if (path == ScorePath::FP4) {
         hipLaunchKernelGGL(score_fp4_mfma_kernel, dim3((unsigned)(8 * a.per_xcd)), dim3(kF4Threads), 0, stream, a);
-        if (a.fix_list)
-            hipLaunchKernelGGL(score_fp4_list_kernel, dim3(256), dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL(score_fp4_fixup_kernel, dim3((unsigned)((a.N + 1023) / 1024), (unsigned)R), dim3(256),
-                               0, stream, a);
 
     } else if (path == ScorePath::STREAM) {
         const dim3 grid((unsigned)(8 * a.per_xcd));
