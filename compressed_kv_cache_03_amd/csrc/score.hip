@@ -1378,41 +1378,6 @@ __global__ __launch_bounds__(256) void score_exact_generic_kernel(ScoreArgs a) {
     if (a.hist) atomicAdd(&a.hist[r * kHistBins + (sort_key(res) >> (32 - kHistBits))], 1u);
 }
 
-// Score of (row r, entry e) for FP4 keys (K = 256) computed by a whole wave in fp64: lane l
-// takes elements l, l+64, l+128, l+192; every product q * e2m1 * scale is exact in
-// fp64 (8 + 2 + 24 significant bits) and their sum is within
-// gamma_(K-1) * sum|p| of the exact one in any order.  false when the rounding
-// to fp32 is not decided by that bound.
-CSA2_DEV bool wave_certified_fp4(const ScoreArgs& a, int64_t r, int64_t e, int lane, float* out) {
-    const int64_t b = r / a.Qs;
-    constexpr int K = 256;
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.iq) + r * K;
-    const uint8_t* k = reinterpret_cast<const uint8_t*>(a.ik) + (b * a.N_cap + e) * (K / 2);
-    const float* sc = a.ik_scales + (b * a.N_cap + e) * (K / 32);
-    double acc = 0.0, aacc = 0.0;
-#pragma unroll
-    for (int i = lane; i < K; i += 64) {
-        const uint32_t nib = (k[i >> 1] >> (4 * (i & 1))) & 15u;
-        const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(nib, 1.0f, 0);
-        const double p = (double)bf16_to_f32(q[i]) * (double)v[0] * (double)sc[i >> 5];
-        acc += p;
-        aacc += fabs(p);
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        acc += __shfl_xor(acc, o);
-        aacc += __shfl_xor(aacc, o);
-    }
-    // aacc is itself an fp64 sum of K terms: low by at most a factor (1 - K 2^-53)
-    const double eb = ((double)K * 0x1p-53 * 1.001 * aacc * (1.0 + (double)K * 0x1p-52) + fabs(acc) * 0x1p-52);
-    const float lo = (float)(acc - eb), hi = (float)(acc + eb);
-    *out = lo;
-    return __float_as_uint(lo) == __float_as_uint(hi);
-}
-
-
-
-
 // Which scoring kernel a call takes, with its tiling (n_eblk, blocks, per_xcd
 // filled in a).  ROWS: several rows share key loads; FP4: FP4 keys with K = 256
 // on the matrix cores; STREAM: one row per workgroup tile; GENERIC: one thread
