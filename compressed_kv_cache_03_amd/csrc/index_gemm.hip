@@ -774,10 +774,23 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
         const uint32_t ex = base + block_exclusive_scan(c, scan_lds, &tot);
         if (threadIdx.x < nb) s_oc[threadIdx.x] = ex | (c << 16);
         __syncthreads();
-#pragma unroll 4
-        for (int i = wv; i < nb; i += kBandThreads / 64) {
-            const uint32_t oc = s_oc[i];
-            if ((uint32_t)ln < (oc >> 16)) put((oc & 0xffffu) + ln, a.blk[((int64_t)(i0 + i) * R + r) * kFBlkCap + ln]);
+        // a wave takes regions wv, wv + 16, ...: the loads of eight of them are
+        // issued before any is stored, so they share one memory round trip
+        constexpr int kGU = 8;
+        for (int i = wv; i < nb; i += kGU * (kBandThreads / 64)) {
+            uint32_t oc[kGU];
+            uint2 cv[kGU];
+#pragma unroll
+            for (int u = 0; u < kGU; ++u) {
+                const int iu = i + u * (kBandThreads / 64);
+                oc[u] = iu < nb ? s_oc[iu] : 0u;
+                // lanes past the region's count read its first slot (in bounds) and store nothing
+                const int lu = (uint32_t)ln < (oc[u] >> 16) ? ln : 0;
+                cv[u] = a.blk[((int64_t)(i0 + (iu < nb ? iu : i)) * R + r) * kFBlkCap + lu];
+            }
+#pragma unroll
+            for (int u = 0; u < kGU; ++u)
+                if ((uint32_t)ln < (oc[u] >> 16)) put((oc[u] & 0xffffu) + ln, cv[u]);
         }
         base += tot;
         __syncthreads();  // s_oc is rewritten by the next batch
@@ -925,10 +938,14 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
             const int32_t j = live ? s_idx[band[t]] : s_idx[band[0]];
             const uint8_t* krow = a.ik + ((int64_t)b * a.N_cap + j) * RB + sub * BPL;
             double acc = 0.0;
+            // the key chunks are requested together (the query chunks hit in cache)
+            u32x4 kvs[BPL / 16];
+#pragma unroll
+            for (int c = 0; c < BPL / 16; ++c) kvs[c] = *reinterpret_cast<const u32x4*>(krow + 16 * c);
 #pragma unroll 1
             for (int c = 0; c < BPL / 16; ++c) {
                 const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
-                const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + 16 * c);
+                const u32x4 kv = kvs[c];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const auto q0 = __builtin_amdgcn_cvt_pk_f32_fp8(qv[w], false), q1 = __builtin_amdgcn_cvt_pk_f32_fp8(qv[w], true);
