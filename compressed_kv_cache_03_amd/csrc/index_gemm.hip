@@ -680,7 +680,7 @@ CSA2_DEV float exact_score_fp8(const uint8_t* q, const uint8_t* k) {
 template <int KB>
 __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a) {
     constexpr int RB = KB * 128;
-    __shared__ uint32_t s_key[kBandCap];   // sort keys minus the smallest; later the output bitmap
+    __shared__ uint32_t s_key[kBandCap];   // sort keys; later the output bitmap
     __shared__ int32_t s_idx[kBandCap];    // entry index; bit 31 = selected
     // the digit histogram is dead once T^ is known; the band list then reuses
     // its words (80 KB in all: two workgroups per CU)
@@ -752,10 +752,10 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
         flag_row();
         return;
     }
-    // keys relative to the smallest candidate key: they span few bits.  Regions
-    // are taken kBandRegBatch at a time (offsets from a block scan of their
-    // counts); one wave per region (at most kFBlkCap = 64 entries), so the loads
-    // are independent.
+    // the radix select works on keys relative to the smallest candidate key,
+    // which span few bits.  Regions are taken kBandRegBatch at a time (offsets
+    // from a block scan of their counts); one wave per region (at most kFBlkCap =
+    // 64 entries), so the loads are independent.
     static_assert(kFBlkCap <= 64, "one lane per region entry");
     uint32_t kmin = 0xffffffffu, kmax = 0;
     const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
@@ -820,7 +820,6 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
         K1 = max(K1, scan_lds[wv]);
     }
     __syncthreads();
-    for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) s_key[p] -= K0;
 
     // T^: the keff-th largest key.  11-bit digits from the top of the used range;
     // once the digit's bin holds few keys, they are ranked directly.
@@ -831,7 +830,7 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
         for (int i = threadIdx.x; i < kBandHist; i += kBandThreads) hist[i] = 0;
         __syncthreads();
         for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
-            const uint32_t k = s_key[p];
+            const uint32_t k = s_key[p] - K0;
             if ((k & fixed) == prefix) atomicAdd(&hist[(k >> sh) & DM], 1u);
         }
         __syncthreads();
@@ -847,7 +846,7 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
             if (threadIdx.x == 0) dig[0] = 0;
             __syncthreads();
             for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) {
-                const uint32_t k = s_key[p];
+                const uint32_t k = s_key[p] - K0;
                 if ((k & fixed) == prefix) bkey[atomicAdd(&dig[0], 1u)] = k;
             }
             __syncthreads();
@@ -895,7 +894,7 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
         for (int u = 0; u < PER; ++u) {
             const uint32_t p = threadIdx.x * PER + u;  // contiguous per thread
             if (p < C) {
-                const double v = key_to_float(s_key[p] + K0);
+                const double v = key_to_float(s_key[p]);
                 if (v > hi) {
                     ++nin_mine;
                     s_idx[p] |= (int32_t)0x80000000;
@@ -905,19 +904,23 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
                 }
             }
         }
-        uint32_t nband_tot;
-        uint32_t pos = block_exclusive_scan(nb_mine, scan_lds, &nband_tot);
+        // both counts in one scan: band positions in the low 16 bits, selected
+        // entries above (each total is at most kBandCap < 2^16)
+        uint32_t tot2;
+        uint32_t pos = block_exclusive_scan(nb_mine | (nin_mine << 16), scan_lds, &tot2) & 0xffffu;
         while (inb) {
             const int u = __ffs(inb) - 1;
             inb &= inb - 1;
             if (pos < (uint32_t)kBandList) band[pos] = threadIdx.x * PER + u;
             ++pos;
         }
-        if (threadIdx.x == 0) dig[0] = nband_tot;
+        if (threadIdx.x == 0) {
+            dig[0] = tot2 & 0xffffu;
+            dig[1] = tot2 >> 16;
+        }
     }
-    uint32_t nin;
-    block_exclusive_scan(nin_mine, scan_lds, &nin);
-    const uint32_t nband = dig[0];
+    __syncthreads();
+    const uint32_t nband = dig[0], nin = dig[1];
     if (nband > (uint32_t)kBandList || nin > (uint32_t)keff || (uint32_t)keff - nin > nband) {
         flag_row();  // a very wide band, or the error bound did not hold
         return;
@@ -986,7 +989,15 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
         }
     }
     __syncthreads();
-    {
+    // ascending output from a bitmap of the selected entries (over s_key), one
+    // pass per kBandOutChunk entries of the row.  With one pass (rows of up to
+    // kBandOutChunk entries) the count of selected entries is checked against
+    // keff from the pass's own scan before anything is written; longer rows
+    // count them first.
+    uint32_t* bitmap = s_key;
+    uint32_t written = 0;
+    const bool one_pass = nv <= kBandOutChunk;
+    if (!one_pass) {
         uint32_t nsel_mine = 0, nsel;
         for (uint32_t p = threadIdx.x; p < C; p += kBandThreads) nsel_mine += s_idx[p] < 0 ? 1u : 0u;
         block_exclusive_scan(nsel_mine, scan_lds, &nsel);
@@ -995,10 +1006,6 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
             return;
         }
     }
-    // ascending output from a bitmap of the selected entries (over s_key), one
-    // pass per kBandOutChunk entries of the row
-    uint32_t* bitmap = s_key;
-    uint32_t written = 0;
     for (int64_t j0 = 0; j0 < nv; j0 += kBandOutChunk) {
         const int64_t jn = min(nv - j0, (int64_t)kBandOutChunk);
         const int nwords = (int)((jn + 31) / 32);
@@ -1017,6 +1024,10 @@ __global__ __launch_bounds__(kBandThreads, 8) void band_final_kernel(BandArgs a)
         for (int wi = threadIdx.x * per; wi < min(nwords, (int)(threadIdx.x + 1) * per); ++wi) mine += __popc(bitmap[wi]);
         uint32_t total;
         uint32_t pos = written + block_exclusive_scan(mine, scan_lds, &total);
+        if (one_pass && total != (uint32_t)keff) {  // cannot happen when the bound holds
+            flag_row();
+            return;
+        }
         for (int wi = threadIdx.x * per; wi < min(nwords, (int)(threadIdx.x + 1) * per); ++wi) {
             uint32_t word = bitmap[wi];
             while (word) {
