@@ -13,7 +13,7 @@
 //     queries as fp32);
 //   * products of two fp8 values are exact in fp64 and are summed with fp64
 //     FMAs; products of two bf16 values (16 significant bits) are formed exactly
-//     in fp32 and summed in fp64; a 3-step swizzle butterfly finishes each entry.
+//     in fp32 and summed in fp64; a 3-step DPP butterfly finishes each entry.
 //
 // Exactness:
 //   * e4m3: every product is a multiple of 2^-18 of magnitude < 2^17.6, so any
@@ -66,6 +66,24 @@ constexpr int kScoreChunks = 1;                                   // passes per 
 constexpr int kScoreEntriesPerBlock = kScoreChunks * kScoreEntriesPerChunk;  // 512
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Cross-lane partner reads on DPP (VALU, no LDS round trip).  Applied in the
+// order S = 1, 2, 4, 8 they all-reduce within groups of 8 (or 16) lanes: the two
+// quad permutes pair xor 1 and xor 2, then the mirror of each 8-lane half pairs
+// its two quads, and the mirror of the 16-lane row its two halves.
+template <int S>
+CSA2_DEV uint32_t dpp_u32(uint32_t v) {
+    constexpr int kCtrl = S == 1 ? 0xB1 : S == 2 ? 0x4E : S == 4 ? 0x141 : 0x140;
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8, "a pairing of the reduction");
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kCtrl, 0xf, 0xf, false);
+}
+template <int S>
+CSA2_DEV double dpp_f64(double v) {
+    uint2 p = __builtin_bit_cast(uint2, v);
+    p.x = dpp_u32<S>(p.x);
+    p.y = dpp_u32<S>(p.y);
+    return __builtin_bit_cast(double, p);
+}
 
 CSA2_DEV uint32_t pk_max_u16(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
@@ -493,21 +511,21 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
                     }
                 }
             }
-            acc += swz_xor<1>(acc);
-            acc += swz_xor<2>(acc);
-            acc += swz_xor<4>(acc);
+            acc += dpp_f64<1>(acc);
+            acc += dpp_f64<2>(acc);
+            acc += dpp_f64<4>(acc);
             if (DT == 2) {
-                aacc += swz_xor<1>(aacc);
-                aacc += swz_xor<2>(aacc);
-                aacc += swz_xor<4>(aacc);
+                aacc += dpp_f64<1>(aacc);
+                aacc += dpp_f64<2>(aacc);
+                aacc += dpp_f64<4>(aacc);
             }
             if (DT == 0) {
-                kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (1 << 10) | 0x1f));
-                kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (2 << 10) | 0x1f));
-                kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (4 << 10) | 0x1f));
-                kmx = pk_max_u16(kmx, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kmx, (1 << 10) | 0x1f));
-                kmx = pk_max_u16(kmx, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kmx, (2 << 10) | 0x1f));
-                kmx = pk_max_u16(kmx, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kmx, (4 << 10) | 0x1f));
+                kex = pk_min_u16(kex, dpp_u32<1>(kex));
+                kex = pk_min_u16(kex, dpp_u32<2>(kex));
+                kex = pk_min_u16(kex, dpp_u32<4>(kex));
+                kmx = pk_max_u16(kmx, dpp_u32<1>(kmx));
+                kmx = pk_max_u16(kmx, dpp_u32<2>(kmx));
+                kmx = pk_max_u16(kmx, dpp_u32<4>(kmx));
             }
             if (sub == t) {
                 keep = acc;
@@ -753,16 +771,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_rows_kernel(ScoreArgs a) 
                                                                                  __builtin_bit_cast(u16x2, ef)));
                 }
             }
-            // 16-lane butterfly with swizzles (xor 1, 2, 4, 8 stay inside the entry's lanes)
+            // 16-lane DPP butterfly (its pairings stay inside the entry's lanes)
             auto fold = [&](auto xr) __attribute__((always_inline)) {
                 constexpr int X = decltype(xr)::value;
 #pragma unroll
-                for (int j = 0; j < QR; ++j) acc[j] += swz_xor<X>(acc[j]);
-                kex = pk_min_u16(kex, (uint32_t)__builtin_amdgcn_ds_swizzle((int)kex, (X << 10) | 0x1f));
-                kmx = __builtin_bit_cast(
-                    uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, kmx),
-                                                        __builtin_bit_cast(u16x2, (uint32_t)__builtin_amdgcn_ds_swizzle(
-                                                                                      (int)kmx, (X << 10) | 0x1f))));
+                for (int j = 0; j < QR; ++j) acc[j] += dpp_f64<X>(acc[j]);
+                kex = pk_min_u16(kex, dpp_u32<X>(kex));
+                kmx = pk_max_u16(kmx, dpp_u32<X>(kmx));
             };
             fold(std::integral_constant<int, 1>{});
             fold(std::integral_constant<int, 2>{});
