@@ -106,3 +106,39 @@ def test_topk_sweep(seed):
     torch.cuda.synchronize()
     ref = oracle.topk(s, k, n_valid=nv.astype(np.int64))
     assert np.array_equal(host(got), ref), (seed, s.shape, k)
+
+
+# ---------------------------------------------------------------- whole layer steps
+def _layer_case(seed):
+    """A workload recipe at random sizes: index width, entry width, query heads, window,
+    rows per step, selection size, valid counts and (hierarchical recipes) pool size."""
+    from synth.workloads import W1, W2, W3, W4, W6, W7, W8
+    rng = np.random.default_rng(11000 + seed)
+    base = [W1, W2, W3, W6, W7, W8, W4][seed % 7]
+    dt = base.idx_dtype
+    if base is W4:  # prefill chunks on the matrix-core selection: K of 128 or 256
+        H, d = [(2, 64), (4, 64), (1, 128)][rng.integers(3)]
+        Qs = int(rng.choice([2, 33, 96]))
+    else:
+        H, d = WIDTHS[dt][rng.integers(len(WIDTHS[dt]))]
+        Qs = base.Qs if base.Qs > 1 else int(rng.choice([1, 1, 2, 5]))
+    B = int(rng.integers(1, 4))
+    N = int(rng.integers(max(Qs, 20), 6001))
+    k = int(rng.integers(1, min(N, 700) + 1))
+    kw = dict(B=B, N=N, H_I=H, d_I=d, Qs=Qs, k=k, Hq=int(rng.choice([1, 4, 16])),
+              D=int(rng.choice([64, 128, 256])), W=int(rng.choice([0, 1, 17, 128])))
+    if base.pool_blocks:
+        blocks = (N + 7) // 8
+        kw["pool_blocks"] = int(rng.integers(min((k + 7) // 8, blocks), blocks + 1))
+    nv = rng.integers(Qs, N + 1, B)
+    if rng.random() < 0.5:
+        nv[rng.integers(B)] = N
+    return base.scaled(**kw), [int(v) for v in nv]
+
+
+@pytest.mark.parametrize("seed", range(56))
+def test_layer_step_sweep(seed):
+    from test_gpu_parity import Run
+    wl, nv = _layer_case(seed)
+    print(seed, wl, nv, flush=True)
+    Run(wl, n_valid=nv).check_all()
