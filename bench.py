@@ -262,6 +262,25 @@ def copy_bandwidth(device, reps=5):
     return round(2 * src.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
 
 
+def read_bandwidth(device, reps=5):
+    """Bytes per second read by torch's own sum over 4 GiB of fp32 (one pass, nothing written but
+    the result): what a library reduction reads on this device, beside the score kernel's rate."""
+    import torch
+
+    x = torch.ones(1 << 30, dtype=torch.float32, device=device)
+    torch.sum(x)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        torch.sum(x)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbps = round(x.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del x
+    return gbps
+
+
 def cache_accounting(wl):
     """Stored cache bytes of the workload's layers with entries and index keys shared inside each
     group, against every layer keeping its own (entries x numbers x copies x bits / 8 per array,
@@ -522,6 +541,7 @@ def main():
                      "launches": len(r["score_ms"]), "avg_launch_us": round(score_us, 2),
                      "launch_us_pct": _summary([x * 1e3 for x in r["score_ms"]])},
         "hbm_copy_GBps": copy_bandwidth(device),
+        "hbm_read_GBps": read_bandwidth(device),
         "cache": cache_accounting(wl),
     }
     del r
