@@ -125,8 +125,10 @@ def _layer_case(seed):
     B = int(rng.integers(1, 4))
     N = int(rng.integers(max(Qs, 20), 6001))
     k = int(rng.integers(1, min(N, 700) + 1))
-    kw = dict(B=B, N=N, H_I=H, d_I=d, Qs=Qs, k=k, Hq=int(rng.choice([1, 4, 16])),
-              D=int(rng.choice([64, 128, 256])), W=int(rng.choice([0, 1, 17, 128])))
+    # head counts that leave the last group of 16 partly empty, entry widths of every
+    # kernel instance kind (odd and even numbers of 32-element blocks)
+    kw = dict(B=B, N=N, H_I=H, d_I=d, Qs=Qs, k=k, Hq=int(rng.choice([1, 3, 4, 16, 17, 32])),
+              D=int(rng.choice([32, 64, 96, 128, 160, 256])), W=int(rng.choice([0, 1, 17, 128, 200])))
     if base.pool_blocks:
         blocks = (N + 7) // 8
         kw["pool_blocks"] = int(rng.integers(min((k + 7) // 8, blocks), blocks + 1))
@@ -136,7 +138,7 @@ def _layer_case(seed):
     return base.scaled(**kw), [int(v) for v in nv]
 
 
-@pytest.mark.parametrize("seed", range(56))
+@pytest.mark.parametrize("seed", range(84))
 def test_layer_step_sweep(seed):
     from test_gpu_parity import Run
     wl, nv = _layer_case(seed)
