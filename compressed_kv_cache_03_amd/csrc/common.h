@@ -52,33 +52,41 @@ CSA2_DEV double swz_xor(double v) {
     return *reinterpret_cast<double*>(&p);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts by 1, 2, 4
+// and 8 (a lane with no source in its 16-lane row adds 0) give the sums inside
+// each row, then every row adds the totals of the rows below it, read from
+// lanes 15, 31 and 47.
+CSA2_DEV uint32_t wave_inclusive_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return x + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
+}
+
 // Block-wide exclusive prefix sum of one uint32 per thread (blockDim.x <= 1024,
 // a multiple of 64).  `lds` must hold blockDim.x/64 + 1 words.  Returns the
-// exclusive prefix; *total receives the block sum.  Contains barriers.
+// exclusive prefix; *total receives the block sum.  Every thread adds the wave
+// totals itself (broadcast LDS reads), so there is no serial step.  Contains
+// barriers.
 CSA2_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds, uint32_t* total) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan(v);
     if (lane == 63) lds[wid] = x;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t run = 0;
-        for (int w = 0; w < nw; ++w) {
-            uint32_t t = lds[w];
-            lds[w] = run;
-            run += t;
-        }
-        lds[nw] = run;
+    uint32_t before = 0, all = 0;
+    for (int w = 0; w < nw; ++w) {
+        const uint32_t t = lds[w];
+        before += w < wid ? t : 0u;
+        all += t;
     }
-    __syncthreads();
-    uint32_t excl = lds[wid] + x - v;
-    *total = lds[nw];
-    __syncthreads();
-    return excl;
+    *total = all;
+    __syncthreads();  // the words are read before a later call overwrites them
+    return before + x - v;
 }
 
 // Find, within a histogram of `nbins` bins (highest bin = largest keys), the
