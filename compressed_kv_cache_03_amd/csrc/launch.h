@@ -80,6 +80,7 @@ struct ScoreArgs {
     // filled by launch_score_exact: with several query rows per sequence the
     // blocks of one entry block and all its rows run together on one XCD
     int64_t n_eblk = 0, blocks = 0, per_xcd = 0;
+    int64_t persist = 0;  // single-row stream: resident workgroups per row (0: one per block)
 };
 hipError_t launch_score_exact(const ScoreArgs& a, hipStream_t stream);
 // Work-items along x of the launches launch_score_exact would make for a.

@@ -64,6 +64,10 @@ constexpr int kStreamThreads = 512;
 constexpr int kScoreEntriesPerChunk = (kStreamThreads / 64) * kScoreEntriesPerWave;  // 512 per pass of the workgroup
 constexpr int kScoreChunks = 1;                                   // passes per workgroup
 constexpr int kScoreEntriesPerBlock = kScoreChunks * kScoreEntriesPerChunk;  // 512
+// Persistent single-row stream (e4m3 keys, K = 256): one workgroup of 8 waves per
+// CU (its 152 VGPRs leave room for no second one), each streaming a run of its
+// row's 512-entry blocks with the key ring running on across them.
+constexpr int64_t kPersistResident = 256;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -342,12 +346,23 @@ CSA2_DEV int bf16_pair_emin(uint32_t w) {
 // FP4 keys with K = 256 are held to 128 registers (4 waves per SIMD); only the
 // rare exact-recompute path spills.
 // POOL: the slots are a hierarchical pool's positions (a.pool set).
-template <int DT, int CPL, bool POOL>
+template <int DT, int CPL, bool POOL, bool PERSIST>
 __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void score_exact_kernel(ScoreArgs a) {
     constexpr int EPC = DT == 0 ? 8 : DT == 1 ? 16 : 32;  // key elements per 16-byte chunk
     constexpr int EB = 128 * CPL;         // bytes per entry
-    int64_t r, e_block;
-    {
+    int64_t r, e_block, blk_end;
+    if constexpr (PERSIST) {
+        // a.persist workgroups per row, each a run of consecutive 512-entry blocks
+        // of its row, resident for the whole launch
+        const int64_t w = blockIdx.x, P = a.persist;
+        r = w / P;
+        const int64_t L = (a.n_eblk + P - 1) / P;
+        const int64_t blk0 = (w % P) * L;
+        const int64_t nblk_row = (row_valid(a, r) + kScoreEntriesPerBlock - 1) / kScoreEntriesPerBlock;
+        blk_end = blk0 + L < nblk_row ? blk0 + L : nblk_row;
+        if (blk0 >= blk_end) return;
+        e_block = blk0 * kScoreEntriesPerBlock;
+    } else {
         // block w takes t = (w % 8) * per_xcd + w / 8: each XCD gets a run of
         // consecutive t, so the Qs rows of a sequence for one entry block read
         // its keys through the same L2
@@ -357,6 +372,7 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
         const int64_t rest = t / a.Qs;
         r = (rest / a.n_eblk) * a.Qs + t % a.Qs;
         e_block = (rest % a.n_eblk) * kScoreEntriesPerBlock;
+        blk_end = e_block / kScoreEntriesPerBlock + 1;
     }
     const int64_t b = r / a.Qs;
     const int64_t nv = row_valid(a, r);
@@ -449,9 +465,42 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.ik) + b * a.N_cap * (int64_t)EB;
     if (with_hist) __syncthreads();  // histogram zeroed before any chunk adds to it
 
-    for (int chunk = 0; chunk < kScoreChunks; ++chunk) {
-        const int64_t e_wave = e_block + chunk * kScoreEntriesPerChunk + wave * kScoreEntriesPerWave;
-        if (e_wave >= nv) break;  // wave-uniform
+    // keys are loaded kPD rounds ahead of their use from a ring of round buffers, so
+    // enough bytes are in flight per wave (FP4 and e4m3 rows are short: 128 and
+    // 256 bytes); a persistent workgroup's ring runs on across its blocks, so its
+    // size divides the 8 rounds of a block and the slot of a round is static.
+    // Entries past nv load entry nv - 1 (in bounds) and are never stored.
+    static_assert(kScoreChunks == 1, "one pass of 512 entries per block");
+    constexpr int kPD = DT == 1 ? 3 : (DT == 0 && CPL >= 8) ? 1 : 2;
+    constexpr int kRing = kPD + 1;
+    static_assert(!PERSIST || kScoreRounds % kRing == 0, "ring slots static across blocks");
+    u32x4 wr[kRing][CPL];
+    float kr[kRing][DT == 2 ? CPL : 1];
+    auto load_round = [&](int64_t e_wave, int t, u32x4(&w)[CPL], float(&ks)[DT == 2 ? CPL : 1]) __attribute__((always_inline)) {
+        int64_t e = e_wave + t * 8 + g;
+        e = e < nv ? e : nv - 1;
+        const int64_t pe = POOL ? slot_entry(a, r, e) : e;
+        const uint8_t* src = kbase + pe * EB + sub * 16;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
+        if constexpr (DT == 2) {
+            const float* sp = a.ik_scales + (b * a.N_cap + pe) * (int64_t)(a.K / 32) + sub;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) ks[c] = __builtin_nontemporal_load(sp + 8 * c);
+        } else {
+            ks[0] = 0.0f;
+        }
+    };
+    const int64_t nblk = PERSIST ? blk_end - e_block / kScoreEntriesPerBlock : 1;
+    for (int64_t bi = 0; bi < nblk; ++bi) {
+        const int64_t blk = e_block / kScoreEntriesPerBlock + bi;
+        const int64_t e_wave = blk * kScoreEntriesPerBlock + wave * kScoreEntriesPerWave;
+        if (e_wave >= nv) break;  // wave-uniform; only the row's last block is partial
+        if (bi == 0) {
+#pragma unroll
+            for (int t = 0; t < kPD; ++t) load_round(e_wave, t, wr[t], kr[t]);
+        }
         double keep = 0.0, keep_abs = 0.0;
         uint32_t keep_ex = 0, keep_mx = 0;
         // one round: 8 entries, 8 lanes each; lane sub == t keeps entry e_wave + 8t + g
@@ -535,35 +584,16 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
             }
         };
         {
-            // keys are loaded kPD rounds ahead of their use from a ring of kPD + 1
-            // round buffers, so enough bytes are in flight per wave (FP4 and e4m3
-            // rows are short: 128 and 256 bytes).  Entries past nv load entry
-            // nv - 1 (in bounds) and are never stored.
-            constexpr int kPD = DT == 1 ? 3 : (DT == 0 && CPL >= 8) ? 1 : 2;
-            u32x4 wr[kPD + 1][CPL];
-            float kr[kPD + 1][DT == 2 ? CPL : 1];
-            auto load_round = [&](int t, u32x4(&w)[CPL], float(&ks)[DT == 2 ? CPL : 1]) __attribute__((always_inline)) {
-                int64_t e = e_wave + t * 8 + g;
-                e = e < nv ? e : nv - 1;
-                const int64_t pe = POOL ? slot_entry(a, r, e) : e;
-                const uint8_t* src = kbase + pe * EB + sub * 16;
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
-                    w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 128));
-                if constexpr (DT == 2) {
-                    const float* sp = a.ik_scales + (b * a.N_cap + pe) * (int64_t)(a.K / 32) + sub;
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) ks[c] = __builtin_nontemporal_load(sp + 8 * c);
-                } else {
-                    ks[0] = 0.0f;
-                }
-            };
-#pragma unroll
-            for (int t = 0; t < kPD; ++t) load_round(t, wr[t], kr[t]);
+            // the next block's first rounds are requested during this block's last
+            const int64_t e_next = e_wave + kScoreEntriesPerBlock;
+            const bool more = PERSIST && blk + 1 < blk_end && e_next < nv;  // wave-uniform
 #pragma unroll
             for (int t = 0; t < kScoreRounds; ++t) {
-                if (t + kPD < kScoreRounds) load_round(t + kPD, wr[(t + kPD) % (kPD + 1)], kr[(t + kPD) % (kPD + 1)]);
-                round_body(t, wr[t % (kPD + 1)], kr[t % (kPD + 1)]);
+                if (t + kPD < kScoreRounds)
+                    load_round(e_wave, t + kPD, wr[(t + kPD) % kRing], kr[(t + kPD) % kRing]);
+                else if (more)
+                    load_round(e_next, t + kPD - kScoreRounds, wr[(t + kPD) % kRing], kr[(t + kPD) % kRing]);
+                round_body(t, wr[t % kRing], kr[t % kRing]);
             }
         }
 
@@ -1424,6 +1454,16 @@ static ScorePath plan_score(ScoreArgs& a, int* cpl_out, int* qr_out) {
         a.n_eblk = (a.N + kScoreEntriesPerBlock - 1) / kScoreEntriesPerBlock;
         a.blocks = a.n_eblk * R;
         a.per_xcd = (a.blocks + 7) / 8;
+        // e4m3 keys with K = 256, one query row per sequence, no pool: a.persist
+        // resident workgroups per row, each streaming a run of the row's blocks (no
+        // workgroup turnover; one histogram flush per workgroup)
+        a.persist = 0;
+        if (a.dtype == 1 && cpl == 2 && a.Qs == 1 && !a.pool && a.blocks > kPersistResident) {
+            int64_t P = (kPersistResident + R / 2) / R;
+            if (P < 1) P = 1;
+            if (P > a.n_eblk) P = a.n_eblk;
+            a.persist = P;
+        }
         return ScorePath::STREAM;
     }
     return ScorePath::GENERIC;
@@ -1431,12 +1471,13 @@ static ScorePath plan_score(ScoreArgs& a, int* cpl_out, int* qr_out) {
 
 int64_t score_grid_threads(const ScoreArgs& args) {
     ScoreArgs a = args;
-    if ((int64_t)a.B * a.Qs == 0 || a.N == 0) return 0;
+    const int64_t R = (int64_t)a.B * a.Qs;
+    if (R == 0 || a.N == 0) return 0;
     int cpl, qr;
     switch (plan_score(a, &cpl, &qr)) {
         case ScorePath::ROWS: return 8 * a.per_xcd * kScoreThreads;
         case ScorePath::FP4: return 8 * a.per_xcd * kF4Threads;
-        case ScorePath::STREAM: return 8 * a.per_xcd * kStreamThreads;
+        case ScorePath::STREAM: return (a.persist > 0 ? R * a.persist : 8 * a.per_xcd) * kStreamThreads;
         default: return (a.N + 255) / 256 * 256;
     }
 }
@@ -1485,14 +1526,17 @@ hipError_t launch_score_exact(const ScoreArgs& args, hipStream_t stream) {
         hipLaunchKernelGGL(score_fp4_mfma_kernel, dim3((unsigned)(8 * a.per_xcd)), dim3(kF4Threads), 0, stream, a);
 
     } else if (path == ScorePath::STREAM) {
-        const dim3 grid((unsigned)(8 * a.per_xcd));
         const bool pool = a.pool != nullptr;
+        const dim3 grid((unsigned)(8 * a.per_xcd));
+        if (a.persist > 0)  // plan_score sets it for e4m3 keys with K = 256 only
+            hipLaunchKernelGGL((score_exact_kernel<1, 2, false, true>), dim3((unsigned)(R * a.persist)),
+                               dim3(kStreamThreads), 0, stream, a);
 #define CSA2_SCORE_LAUNCH(DTV, CPLV)                                                                   \
-    if (a.dtype == DTV && cpl == CPLV) {                                                             \
+    if (a.persist == 0 && a.dtype == DTV && cpl == CPLV) {                                           \
         if (pool)                                                                                    \
-            hipLaunchKernelGGL((score_exact_kernel<DTV, CPLV, true>), grid, dim3(kStreamThreads), 0, stream, a); \
+            hipLaunchKernelGGL((score_exact_kernel<DTV, CPLV, true, false>), grid, dim3(kStreamThreads), 0, stream, a); \
         else                                                                                         \
-            hipLaunchKernelGGL((score_exact_kernel<DTV, CPLV, false>), grid, dim3(kStreamThreads), 0, stream, a); \
+            hipLaunchKernelGGL((score_exact_kernel<DTV, CPLV, false, false>), grid, dim3(kStreamThreads), 0, stream, a); \
     }
         CSA2_SCORE_LAUNCH(0, 1)
         CSA2_SCORE_LAUNCH(0, 2)
