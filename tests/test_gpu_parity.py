@@ -469,6 +469,30 @@ def test_w3_scaled_fp8():
     Run(W3.scaled(B=2, N=9000), n_valid=[9000, 5000]).check_all()
 
 
+@pytest.mark.parametrize("B,N,causal", [(40, 5000, -1), (40, 5000, 2047), (33, 4097, 4096), (300, 1200, -1)])
+def test_index_score_e4m3_persistent_stream(B, N, causal):
+    # e4m3 keys with K = 256 and one query row per sequence: once rows x 512-entry blocks exceed
+    # 256 the stream runs as resident workgroups over runs of a row's blocks.  40 x 10 blocks
+    # gives 6 workgroups per row with 2 blocks each (one with none); 33 x 9 blocks ends every row
+    # on a 1-entry block; 300 rows take one workgroup each over 3 blocks
+    iq = synth.normal_idx("e4m3", synth.seed(0, 960), B * 4 * 64).reshape(B, 1, 4, 64)
+    ik = synth.normal_idx("e4m3", synth.seed(0, 961), B * N * 4 * 64).reshape(B, N, 4, 64)
+    got = csa2.index_score(dev(iq), dev(ik), "e4m3", causal_offset=causal)
+    torch.cuda.synchronize()
+    nv = None if causal < 0 else np.full(B, min(causal + 1, N), np.int64)
+    ref = oracle.index_score("e4m3", iq, ik, n_valid_row=nv)
+    assert bits_eq(host(got), ref)
+
+
+def test_w3_scaled_persistent_stream_ragged():
+    # the long-context recipe at batch 40: Full scores every sequence's valid entries through
+    # the persistent stream (rows from 1 to 5,000 valid entries, blocks cut mid-run)
+    rng = np.random.default_rng(77)
+    nv = rng.integers(1, 5001, 40)
+    nv[[0, 7, 19]] = [5000, 1, 513]
+    Run(W3.scaled(B=40, N=5000, k=300), n_valid=[int(v) for v in nv]).check_all()
+
+
 def test_group_save_restore_resumes_bitwise():
     # Full and Reindex, then the group goes to a pinned host image, its device
     # buffers are overwritten, the image comes back, and the two Reuse layers
