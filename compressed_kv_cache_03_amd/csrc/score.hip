@@ -13,7 +13,11 @@
 //     queries as fp32);
 //   * products of two fp8 values are exact in fp64 and are summed with fp64
 //     FMAs; products of two bf16 values (16 significant bits) are formed exactly
-//     in fp32 and summed in fp64; a 3-step DPP butterfly finishes each entry.
+//     in fp32 and summed in fp64; a 3-step DPP butterfly finishes each entry;
+//   * a workgroup of 8 waves takes one 512-entry block of one row; with e4m3
+//     keys (K = 256) and one query row per sequence the workgroups instead stay
+//     resident, one per CU, each streaming a run of its row's blocks with the
+//     key loads running ahead across block boundaries.
 //
 // Exactness:
 //   * e4m3: every product is a multiple of 2^-18 of magnitude < 2^17.6, so any
