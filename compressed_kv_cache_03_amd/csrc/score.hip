@@ -662,7 +662,9 @@ __global__ __launch_bounds__(kStreamThreads, DT == 2 && CPL == 1 ? 4 : 1) void s
             }
         }
         if (e < nv) {
-            a.scores[r * a.ld + e] = res;
+            // streamed past the caches: plain stores of the scores among the key reads
+            // made a launch over 64 rows x 131,072 bf16 entries about 2 % slower
+            __builtin_nontemporal_store(res, a.scores + r * a.ld + e);
             if (with_hist) atomicAdd(&lhist[sort_key(res) >> (32 - kHistBits)], 1u);
         }
     }
