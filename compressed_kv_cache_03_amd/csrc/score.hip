@@ -1311,22 +1311,28 @@ __global__ __launch_bounds__(kF4Threads, kF4MinWaves) void score_fp4_mfma_kernel
     __shared__ uint32_t s_emax[8], s_band[NW], s_bad[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool with_hist = a.hist != nullptr;
-    // the first rounds' keys are in flight while the query is prepared
+    // query element tid & 255, loaded ahead of the keys: loads complete in the
+    // order they are issued, so the query is prepared while the first round's
+    // keys are in flight
+    const int el = tid & 255;
+    const uint32_t x = reinterpret_cast<const uint16_t*>(a.iq)[r * 256 + el];
     F4Round ring[kF4Ahead + 1];
     {
         const int64_t e0 = e_block + __builtin_amdgcn_readfirstlane(wave) * 64;
+        // the first round unconditionally (past nv it loads entry nv - 1, in bounds),
+        // so that the wait for the query is counted past the keys and never waits
+        // for them
+        f4_load_round(a, r / a.Qs, nv, e0, ring[0]);
 #pragma unroll
-        for (int i = 0; i < kF4Ahead; ++i)
+        for (int i = 1; i < kF4Ahead; ++i)
             if (i < kF4Rounds && e0 + i * NW * 64 < nv) f4_load_round(a, r / a.Qs, nv, e0 + i * NW * 64, ring[i]);
     }
     if (with_hist)
         for (int i = tid; i < kHistBins; i += kF4Threads) lhist[i] = 0;
     for (int i = tid; i < 2 * 2 * 64 * 8 / 4; i += kF4Threads) reinterpret_cast<u32x4*>(s_afr)[i] = u32x4{0u, 0u, 0u, 0u};
 
-    // query element tid: its block's largest exponent field, its band and its two
+    // query element el: its block's largest exponent field, its band and its two
     // e4m3 parts (threads 256.. repeat element tid % 256, which changes no maximum)
-    const int el = tid & 255;
-    const uint32_t x = reinterpret_cast<const uint16_t*>(a.iq)[r * 256 + el];
     const bool nz = (x & 0x7fffu) != 0;
     const uint32_t fe = (x >> 7) & 0xffu;
     uint32_t em = nz ? fe : 0u;

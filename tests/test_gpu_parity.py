@@ -253,6 +253,54 @@ def test_index_score_fp4_mfma_bands(case):
         assert bits_eq(host(got), want), case
 
 
+def _fp4_row_queries(rng, R, K):
+    """bf16 index queries of three kinds by row: N(0,1) values (one band pair on the
+    matrix cores), values spread over 28 binades below each block's largest (two band
+    pairs), and one value 28 binades down (outside the bands: the per-thread path)."""
+    emax = 127 + rng.integers(-3, 4, (R, K // 32, 1))
+    f = emax - rng.integers(0, 28, (R, K // 32, 32))
+    f[:, :, 0] = emax[:, :, 0]
+    f[:, :, 1] = emax[:, :, 0] - 27
+    iq = _bf16_fields(rng, f).reshape(R, K)
+    iq[0::3] = synth.to_bf16_bits(rng.normal(size=(len(range(0, R, 3)), K)).astype(np.float32))
+    iq[2::3, 37] = ((iq[2::3, 37].astype(np.int64) & 0x807f) |
+                    ((emax[2::3, 1, 0] - 28) << 7)).astype(np.uint16)
+    return iq
+
+
+@pytest.mark.parametrize("B,N,causal", [(32, 65536, -1), (200, 3000, -1), (64, 8192, 5000), (40, 5000, -1),
+                                        (33, 4097, 4096)])
+def test_index_score_fp4_mfma_decode_shapes(B, N, causal):
+    # FP4 keys with K = 256 and one query row per sequence on the matrix-core scorer, bit for bit
+    # at the FP4-key decode shape (32 x 65,536: 4,096 workgroups of 512 entries) and at shapes
+    # whose rows end inside a block: 200 rows of 6 blocks (the last of 440 entries), 64 rows cut
+    # at 5,001 entries, 40 rows of 10 blocks (the last of 392) and 33 rows that end on a 1-entry
+    # block.  Rows cycle through one band pair, two band pairs and the per-thread path
+    rng = np.random.default_rng(B * 7 + N)
+    K = 256
+    iq = _fp4_row_queries(rng, B, K).reshape(B, 1, 4, 64)
+    codes = rng.integers(0, 256, (B, N, 4, 32)).astype(np.uint8)
+    sc = ((rng.random((B, N, K // 32)) + 0.5) * np.exp2(rng.integers(-20, 20, (B, N, K // 32))) *
+          np.where(rng.random((B, N, K // 32)) < 0.2, -1.0, 1.0))
+    sc[:, ::11, 3] = 0.0
+    scales = sc.astype(np.float32)
+    got = csa2.index_score(dev(iq), dev(codes), "fp4", ik_scales=dev(scales), causal_offset=causal)
+    torch.cuda.synchronize()
+    nv = None if causal < 0 else np.full(B, min(causal + 1, N), np.int64)
+    want = oracle.index_score("fp4", iq, codes, n_valid_row=nv, ik_scales=scales)
+    assert bits_eq(host(got), want)
+
+
+def test_w7_scaled_fp4_ragged_batch():
+    # the FP4-key recipe at batch 40: Full scores every sequence's valid entries on the
+    # matrix-core scorer with the digit histogram (rows from 1 to 5,000 valid entries, most
+    # ending inside a block, one with a single entry)
+    rng = np.random.default_rng(78)
+    nv = rng.integers(1, 5001, 40)
+    nv[[0, 7, 19]] = [5000, 1, 513]
+    Run(W7.scaled(B=40, N=5000, k=300), n_valid=[int(v) for v in nv]).check_all()
+
+
 # ---------------------------------------------------------------- S3 top-k
 def _topk_scores(R, N, seed):
     rng = np.random.default_rng(seed)
