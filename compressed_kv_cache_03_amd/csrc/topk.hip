@@ -480,30 +480,37 @@ __global__ __launch_bounds__(kSplitThreads) void topk_slice_kernel(TopkArgs a, i
     const int64_t j_end = j0 + len < nv ? j0 + len : nv;
     // thread t takes entries jt .. jt + 15 of each pass (jt a multiple of 16, of 32
     // for even t); the first pass's scores are requested before the histogram so
-    // that the two latencies overlap
-    float x[16];
-    auto load = [&](int64_t jt) __attribute__((always_inline)) {
+    // that the two latencies overlap, and each later pass's while the one before
+    // it is processed
+    float x[16], xn[16];
+    auto load = [&](float(&dst)[16], int64_t jt) __attribute__((always_inline)) {
         if (aligned16 && jt + 16 <= j_end) {
             const float4* s4 = reinterpret_cast<const float4*>(s + jt);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const float4 v = s4[c];
-                x[4 * c] = v.x;
-                x[4 * c + 1] = v.y;
-                x[4 * c + 2] = v.z;
-                x[4 * c + 3] = v.w;
+                dst[4 * c] = v.x;
+                dst[4 * c + 1] = v.y;
+                dst[4 * c + 2] = v.z;
+                dst[4 * c + 3] = v.w;
             }
         } else {
 #pragma unroll
-            for (int u = 0; u < 16; ++u) x[u] = jt + u < j_end ? s[jt + u] : 0.0f;
+            for (int u = 0; u < 16; ++u) dst[u] = jt + u < j_end ? s[jt + u] : 0.0f;
         }
     };
-    load(j0 + 16 * (int64_t)tid);
+    load(x, j0 + 16 * (int64_t)tid);
     {
+        // all of a thread's histogram loads before any LDS store, so that one
+        // memory round trip covers them
+        constexpr int kPer = kHistBins / 4 / kSplitThreads;
+        static_assert(kPer * 4 * kSplitThreads == kHistBins, "whole uint4 per thread");
         const uint4* h4 = reinterpret_cast<const uint4*>(a.hist + r * kHistBins);
-        uint4* l4 = reinterpret_cast<uint4*>(s_hist);
+        uint4 hv[kPer];
 #pragma unroll
-        for (int i = tid; i < kHistBins / 4; i += kSplitThreads) l4[i] = h4[i];
+        for (int i = 0; i < kPer; ++i) hv[i] = h4[tid + i * kSplitThreads];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) reinterpret_cast<uint4*>(s_hist)[tid + i * kSplitThreads] = hv[i];
     }
     __syncthreads();
     find_digit<kSplitThreads>(s_hist, kHistBins, (uint32_t)keff, scan_lds, dig);
@@ -514,7 +521,11 @@ __global__ __launch_bounds__(kSplitThreads) void topk_slice_kernel(TopkArgs a, i
     uint32_t written = 0;
     for (int64_t js = j0; js < j_end; js += kSplitSub) {
         const int64_t jt = js + 16 * (int64_t)tid;
-        if (js > j0) load(jt);
+        if (js > j0) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) x[u] = xn[u];
+        }
+        if (js + kSplitSub < j_end) load(xn, jt + kSplitSub);  // block-uniform
         uint32_t keys[16];
         uint32_t above = 0, eq = 0;
 #pragma unroll
@@ -544,7 +555,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_slice_kernel(TopkArgs a, i
 }
 
 __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(TopkArgs a, int64_t len) {
-    __shared__ uint32_t s_hist[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
     __shared__ uint32_t s_ckey[kRowCand];
     __shared__ int32_t s_cidx[kRowCand];
     __shared__ uint32_t s_bits[kRowMaxN / 32];
@@ -563,9 +574,34 @@ __global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(TopkArgs a, int
 
     // 1. the histogram, the slice counts and the bitmap are requested together;
     //    then b1, the count above it and the slices' candidate offsets
+    //    (loads batched ahead of their LDS stores: the first 4 bitmap words per
+    //    thread, the histogram and the count share one round trip, each further
+    //    batch of 4 words takes one)
+    static_assert(kHistBins / 4 == kRowThreads, "one uint4 of the histogram per thread");
+    auto load_bits = [&](int w0, uint32_t(&bv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int w = w0 + u * kRowThreads + tid;
+            bv[u] = w < nwords ? a.bits[r * a.bits_ld + w] : 0u;
+        }
+    };
+    auto store_bits = [&](int w0, const uint32_t(&bv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int w = w0 + u * kRowThreads + tid;
+            if (w < nwords) s_bits[w] = bv[u];
+        }
+    };
+    uint32_t bv[4];
+    load_bits(0, bv);
     const uint32_t c = tid < nslices ? a.slice_cnt[r * a.slices + tid] : 0u;
-    for (int i = tid; i < kHistBins; i += kRowThreads) s_hist[i] = a.hist[r * kHistBins + i];
-    for (int w = tid; w < nwords; w += kRowThreads) s_bits[w] = a.bits[r * a.bits_ld + w];
+    const uint4 hv = reinterpret_cast<const uint4*>(a.hist + r * kHistBins)[tid];
+    store_bits(0, bv);
+    reinterpret_cast<uint4*>(s_hist)[tid] = hv;
+    for (int w0 = 4 * kRowThreads; w0 < nwords; w0 += 4 * kRowThreads) {
+        load_bits(w0, bv);
+        store_bits(w0, bv);
+    }
     __syncthreads();
     find_digit<kRowThreads>(s_hist, kHistBins, (uint32_t)keff, scan_lds, dig);
     const uint32_t b1 = dig[0];
