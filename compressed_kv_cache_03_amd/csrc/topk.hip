@@ -249,7 +249,7 @@ constexpr int64_t kRowPassN = 1 << 17;  // longest row the row kernel takes when
 constexpr int64_t kRowFill = 256;       // rows that keep every CU busy with the row kernel
 
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
-    __shared__ uint32_t s_hist[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
     __shared__ uint32_t s_ckey[kRowCand];
     __shared__ int32_t s_cidx[kRowCand];
     __shared__ uint32_t s_bits[kRowMaxN / 32];
@@ -279,8 +279,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs a) {
     };
     if (nv4 > 0) load_batch(0);
 
-    // 1. digit 1
-    for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) s_hist[i] = a.hist[r * kHistBins + i];
+    // 1. digit 1 (one uint4 of the histogram per thread: a single round trip,
+    //    shared with the first batch of scores)
+    static_assert(kHistBins / 4 == kRowThreads, "one uint4 of the histogram per thread");
+    reinterpret_cast<uint4*>(s_hist)[threadIdx.x] = reinterpret_cast<const uint4*>(a.hist + r * kHistBins)[threadIdx.x];
     for (int i = threadIdx.x; i < nwords; i += kRowThreads) s_bits[i] = 0;
     if (threadIdx.x == 0) s_ncand = 0;
     __syncthreads();
