@@ -93,6 +93,14 @@ CSA2_DEV double dpp_f64(double v) {
     return __builtin_bit_cast(double, p);
 }
 
+// Maximum over each 16-lane row, in every lane of the row.
+CSA2_DEV uint32_t wave_row_max(uint32_t v) {
+    v = max(v, dpp_u32<1>(v));
+    v = max(v, dpp_u32<2>(v));
+    v = max(v, dpp_u32<4>(v));
+    return max(v, dpp_u32<8>(v));
+}
+
 CSA2_DEV uint32_t pk_max_u16(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
                                                                   __builtin_bit_cast(u16x2, b)));
@@ -1335,13 +1343,21 @@ __global__ __launch_bounds__(kF4Threads, kF4MinWaves) void score_fp4_mfma_kernel
     // e4m3 parts (threads 256.. repeat element tid % 256, which changes no maximum)
     const bool nz = (x & 0x7fffu) != 0;
     const uint32_t fe = (x >> 7) & 0xffu;
-    uint32_t em = nz ? fe : 0u;
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) em = max(em, (uint32_t)__shfl_xor((int)em, o));
+    // maxima across lanes on DPP and permlane swaps (VALU, no LDS round trips):
+    // em over the element's 32-lane block, mb over the wave
+    uint32_t em = wave_row_max(nz ? fe : 0u);
+    {
+        const auto p = __builtin_amdgcn_permlane16_swap(em, em, false, false);
+        em = max(p[0], p[1]);
+    }
     const uint32_t band = nz ? (em - fe) / 7 : 0u;
-    uint32_t mb = band;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
+    uint32_t mb = wave_row_max(band);
+    {
+        const auto p = __builtin_amdgcn_permlane16_swap(mb, mb, false, false);
+        mb = max(p[0], p[1]);
+        const auto q = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+        mb = max(q[0], q[1]);
+    }
     const bool bad = nz && (fe == 0 || em < kF4EmaxLo || em > kF4EmaxHi);
     const bool wbad = __ballot(bad) != 0;
     if ((tid & 31) == 0 && tid < 256) s_emax[tid >> 5] = em;
